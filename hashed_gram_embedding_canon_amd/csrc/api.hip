@@ -1,0 +1,578 @@
+// C ABI of libengram.so: argument validation (host only, before any GPU
+// work), workspace sizing and carving, launch orchestration on the caller's
+// stream, the host-side prefetch planner, and optional kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace engram;
+
+namespace {
+
+struct Shape {
+  int J, D, d, d_mem, taps, max_order, es;
+  int32_t dtype;
+  int key_bits;
+};
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+engram_status check_config(const engram_config* c, Shape* s) {
+  if (!c || !c->table_rows || !c->multipliers) return ENGRAM_E_INVALID;
+  if (c->num_orders < 1 || c->num_orders > ENGRAM_MAX_ORDERS) return ENGRAM_E_INVALID;
+  if (c->heads < 1) return ENGRAM_E_INVALID;
+  const int J = c->num_orders * c->heads;
+  if (J > ENGRAM_MAX_TABLES) return ENGRAM_E_UNSUPPORTED;
+  int max_order = 0;
+  for (int o = 0; o < c->num_orders; ++o) {
+    if (c->orders[o] < 1 || c->orders[o] > ENGRAM_MAX_ORDERS) return ENGRAM_E_INVALID;
+    if (o > 0 && c->orders[o] <= c->orders[o - 1]) return ENGRAM_E_INVALID;
+    max_order = std::max(max_order, c->orders[o]);
+  }
+  if (c->dtype != ENGRAM_F32 && c->dtype != ENGRAM_BF16) return ENGRAM_E_UNSUPPORTED;
+  if (c->vocab < 1 || c->canon_vocab < 1) return ENGRAM_E_INVALID;
+  if (c->pad_id < 0) return ENGRAM_E_INVALID;
+  if (c->dim < 1 || c->hidden < 1) return ENGRAM_E_INVALID;
+  if (c->conv_kernel < 1 || c->conv_kernel > 8) return ENGRAM_E_UNSUPPORTED;
+  if (!(c->rms_eps >= 0.f)) return ENGRAM_E_INVALID;
+  const int es = (int)dtype_size(c->dtype);
+  if ((c->dim * es) % 16 != 0) return ENGRAM_E_UNSUPPORTED;
+  const int d_mem = J * c->dim;
+  if (d_mem % kGemmBF != 0) return ENGRAM_E_UNSUPPORTED;
+  if (c->hidden % kGemmBF != 0) return ENGRAM_E_UNSUPPORTED;
+  if (c->hidden / (c->dtype == ENGRAM_BF16 ? 8 : 4) > 1024) return ENGRAM_E_UNSUPPORTED;
+  int64_t max_rows = 1;
+  for (int j = 0; j < J; ++j) {
+    if (c->table_rows[j] < 1 || c->table_rows[j] >= (int64_t(1) << 31)) return ENGRAM_E_INVALID;
+    max_rows = std::max(max_rows, (int64_t)c->table_rows[j]);
+  }
+  int bits = 1;
+  while (bits < 31 && (int64_t(1) << bits) < max_rows) ++bits;
+  s->J = J;
+  s->D = c->dim;
+  s->d = c->hidden;
+  s->d_mem = d_mem;
+  s->taps = c->conv_kernel;
+  s->max_order = max_order;
+  s->es = es;
+  s->dtype = c->dtype;
+  s->key_bits = bits;
+  return ENGRAM_OK;
+}
+
+HashArgs make_hash_args(const engram_config* c, const Shape& s) {
+  HashArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.J = s.J;
+  a.num_orders = c->num_orders;
+  a.heads = c->heads;
+  a.max_order = s.max_order;
+  a.pad_id = c->pad_id;
+  for (int o = 0; o < c->num_orders; ++o) a.orders[o] = c->orders[o];
+  for (int j = 0; j < s.J; ++j) {
+    a.prime[j] = (uint32_t)c->table_rows[j];
+    a.recip[j] = mod_recip(a.prime[j]);
+    for (int i = 0; i < s.max_order; ++i) a.mult[j * s.max_order + i] = c->multipliers[j * s.max_order + i];
+  }
+  return a;
+}
+
+inline engram_status hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_E_HIP; }
+
+// ---------------------------------------------------------------- timing
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::vector<ProfRec> g_prof;
+
+class Timed {
+ public:
+  Timed(const char* name, hipStream_t s) : name_(name), s_(s) {
+    {
+      std::lock_guard<std::mutex> l(g_prof_mu);
+      on_ = g_prof_on;
+    }
+    if (on_) {
+      on_ = hipEventCreate(&a_) == hipSuccess && hipEventCreate(&b_) == hipSuccess &&
+            hipEventRecord(a_, s_) == hipSuccess;
+    }
+  }
+  ~Timed() {
+    if (!on_) return;
+    if (hipEventRecord(b_, s_) != hipSuccess) return;
+    std::lock_guard<std::mutex> l(g_prof_mu);
+    g_prof.push_back({name_, a_, b_});
+  }
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t a_{}, b_{};
+  bool on_ = false;
+};
+
+// ---------------------------------------------------------------- workspace
+struct FwdWs {
+  int32_t* idx;
+  uint8_t* e;
+  uint8_t* v;
+  float* partials;
+};
+
+size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out, uint8_t* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> uint8_t* {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  FwdWs w{};
+  w.idx = (sv && sv->idx) ? sv->idx : (int32_t*)take((size_t)N * s.J * 4);
+  w.e = (sv && sv->e) ? (uint8_t*)sv->e : take((size_t)N * s.d_mem * s.es);
+  w.v = (sv && sv->v) ? (uint8_t*)sv->v : take((size_t)N * s.d * s.es);
+  w.partials = (float*)take((size_t)N * (s.d / kGemmBF) * 3 * 4);
+  if (out) *out = w;
+  return off;
+}
+
+struct BwdWs {
+  uint8_t* dkv;
+  uint8_t* wt;
+  float* de;
+  uint8_t* sort;
+};
+
+size_t backward_ws(const Shape& s, int64_t N, BwdWs* out, uint8_t* base) {
+  const int eg = s.dtype == ENGRAM_BF16 ? 2 : 4;  // fp16 or fp32 GEMM operands
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> uint8_t* {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  BwdWs w{};
+  w.dkv = take((size_t)N * 2 * s.d * eg);
+  w.wt = take((size_t)s.d_mem * 2 * s.d * eg);
+  w.de = (float*)take((size_t)N * s.d_mem * 4);
+  w.sort = take(sort_workspace_bytes(N, s.J));
+  if (out) *out = w;
+  return off;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t engram_workspace_size(const engram_config* cfg, int64_t B, int64_t T, int32_t op) {
+  Shape s;
+  if (check_config(cfg, &s) != ENGRAM_OK || B < 0 || T < 0) return 0;
+  const int64_t N = B * T;
+  if (op == ENGRAM_OP_FORWARD) return forward_ws(s, N, nullptr, nullptr, nullptr);
+  if (op == ENGRAM_OP_BACKWARD) return backward_ws(s, N, nullptr, nullptr);
+  return 0;
+}
+
+const char* engram_status_string(engram_status st) {
+  switch (st) {
+    case ENGRAM_OK:
+      return "ok";
+    case ENGRAM_E_INVALID:
+      return "invalid argument";
+    case ENGRAM_E_UNSUPPORTED:
+      return "unsupported shape or dtype";
+    case ENGRAM_E_WORKSPACE:
+      return "workspace missing or too small";
+    case ENGRAM_E_HIP:
+      return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+engram_status engram_hash_indices(const engram_config* cfg, const int32_t* canon_map,
+                                  const int32_t* tokens, int64_t B, int64_t T, int32_t* idx,
+                                  void* stream) {
+  Shape s;
+  engram_status st = check_config(cfg, &s);
+  if (st != ENGRAM_OK) return st;
+  if (B < 0 || T < 0 || T > INT32_MAX) return ENGRAM_E_INVALID;
+  if (B * T == 0) return ENGRAM_OK;
+  if (!canon_map || !tokens || !idx) return ENGRAM_E_INVALID;
+  hipStream_t hs = (hipStream_t)stream;
+  HashArgs ha = make_hash_args(cfg, s);
+  Timed tm("hash", hs);
+  return hip_status(launch_hash(tokens, canon_map, B * T, (int32_t)T, idx, ha, hs));
+}
+
+engram_status engram_forward(const engram_config* cfg, const engram_params* p,
+                             const int32_t* tokens, const void* hidden, int64_t B, int64_t T,
+                             void* y, const engram_saved* saved, const engram_compact* compact,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  Shape s;
+  engram_status st = check_config(cfg, &s);
+  if (st != ENGRAM_OK) return st;
+  if (!p || B < 0 || T < 0 || T > INT32_MAX || B > 65535) return ENGRAM_E_INVALID;
+  const int64_t N = B * T;
+  if (N == 0) return ENGRAM_OK;
+  if ((uint64_t)N * (uint64_t)s.J >= (uint64_t(1) << 31)) return ENGRAM_E_UNSUPPORTED;
+  if (!hidden || !y || !p->w_kv || !p->conv_w) return ENGRAM_E_INVALID;
+  if (!aligned16(hidden) || !aligned16(y) || !aligned16(p->w_kv) || !aligned16(p->conv_w))
+    return ENGRAM_E_INVALID;
+  if ((p->gamma_q && !aligned16(p->gamma_q)) || (p->gamma_k && !aligned16(p->gamma_k)))
+    return ENGRAM_E_INVALID;
+  if (compact) {
+    if (!compact->rows_dev || !compact->inverse_dev) return ENGRAM_E_INVALID;
+    if (!aligned16(compact->rows_dev)) return ENGRAM_E_INVALID;
+  } else {
+    if (!tokens || !p->canon_map) return ENGRAM_E_INVALID;
+    for (int j = 0; j < s.J; ++j)
+      if (!p->tables[j] || !aligned16(p->tables[j])) return ENGRAM_E_INVALID;
+  }
+  if (saved) {
+    if ((saved->k && !aligned16(saved->k)) || (saved->v && !aligned16(saved->v)) ||
+        (saved->e && !aligned16(saved->e)) || (saved->stats && !aligned16(saved->stats)) ||
+        (saved->idx && !aligned16(saved->idx)))
+      return ENGRAM_E_INVALID;
+  }
+  const size_t need = forward_ws(s, N, saved, nullptr, nullptr);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return ENGRAM_E_WORKSPACE;
+  FwdWs w;
+  forward_ws(s, N, saved, &w, (uint8_t*)workspace);
+  hipStream_t hs = (hipStream_t)stream;
+
+  GatherArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.J = s.J;
+  g.row_chunks = s.D * s.es / 16;
+  const int32_t* idx = w.idx;
+  if (compact) {
+    if (compact->ready_event) {
+      if (hipStreamWaitEvent(hs, (hipEvent_t)compact->ready_event, 0) != hipSuccess)
+        return ENGRAM_E_HIP;
+    }
+    idx = compact->inverse_dev;
+    for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)compact->rows_dev;
+    if (saved && saved->idx) {
+      if (hipMemcpyAsync(saved->idx, compact->inverse_dev, (size_t)N * s.J * 4,
+                         hipMemcpyDeviceToDevice, hs) != hipSuccess)
+        return ENGRAM_E_HIP;
+    }
+  } else {
+    HashArgs ha = make_hash_args(cfg, s);
+    Timed tm("hash", hs);
+    if (launch_hash(tokens, p->canon_map, N, (int32_t)T, w.idx, ha, hs) != hipSuccess)
+      return ENGRAM_E_HIP;
+    for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
+  }
+  {
+    Timed tm("gather", hs);
+    if (launch_gather(idx, w.e, N, g, hs) != hipSuccess) return ENGRAM_E_HIP;
+  }
+  {
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.A = (const uint8_t*)p->w_kv;
+    ga.B = w.e;
+    ga.M = N;
+    ga.F = 2 * s.d;
+    ga.K = s.d_mem;
+    ga.group_m = 4;
+    ga.d = s.d;
+    ga.io_dtype = s.dtype;
+    ga.h = (const uint8_t*)hidden;
+    ga.gamma_q = p->gamma_q;
+    ga.gamma_k = p->gamma_k;
+    ga.partials = w.partials;
+    ga.k_out = saved ? (uint8_t*)saved->k : nullptr;
+    ga.v_out = w.v;
+    Timed tm("proj_gemm", hs);
+    if (launch_gemm(s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32, EPI_KV, ga, hs) != hipSuccess)
+      return ENGRAM_E_HIP;
+  }
+  {
+    GateConvArgs gc;
+    gc.B = B;
+    gc.T = T;
+    gc.d = s.d;
+    gc.taps = s.taps;
+    gc.nkt = s.d / kGemmBF;
+    gc.io_dtype = s.dtype;
+    gc.eps = cfg->rms_eps;
+    gc.partials = w.partials;
+    gc.v = w.v;
+    gc.conv_w = p->conv_w;
+    gc.y = (uint8_t*)y;
+    gc.stats = saved ? saved->stats : nullptr;
+    Timed tm("gate_conv", hs);
+    if (launch_gate_conv(gc, hs) != hipSuccess) return ENGRAM_E_HIP;
+  }
+  return ENGRAM_OK;
+}
+
+engram_status engram_backward_table_grad(const engram_config* cfg, const engram_params* p,
+                                         const void* hidden, const void* dy, int64_t B, int64_t T,
+                                         const engram_saved* saved, engram_table_grad* out,
+                                         void* workspace, size_t ws_bytes, void* stream) {
+  Shape s;
+  engram_status st = check_config(cfg, &s);
+  if (st != ENGRAM_OK) return st;
+  if (!p || !out || B < 0 || T < 0 || T > INT32_MAX || B > 65535) return ENGRAM_E_INVALID;
+  if (s.d / 4 > 1024) return ENGRAM_E_UNSUPPORTED;
+  if (out->mode < ENGRAM_GRAD_SORTED_SPARSE || out->mode > ENGRAM_GRAD_ATOMIC_DENSE)
+    return ENGRAM_E_INVALID;
+  const int64_t N = B * T;
+  if ((uint64_t)N * (uint64_t)s.J >= (uint64_t(1) << 31)) return ENGRAM_E_UNSUPPORTED;
+  if (out->mode == ENGRAM_GRAD_SORTED_SPARSE) {
+    if (!out->keys || !out->rows || !out->count || !aligned16(out->rows)) return ENGRAM_E_INVALID;
+  } else {
+    for (int j = 0; j < s.J; ++j)
+      if (!out->dense[j] || !aligned16(out->dense[j])) return ENGRAM_E_INVALID;
+  }
+  if (N > 0) {
+    if (!hidden || !dy || !saved || !saved->idx || !saved->stats || !saved->k || !saved->v)
+      return ENGRAM_E_INVALID;
+    if (!p->w_kv || !p->conv_w) return ENGRAM_E_INVALID;
+    if (!aligned16(hidden) || !aligned16(dy) || !aligned16(saved->k) || !aligned16(saved->v) ||
+        !aligned16(saved->stats) || !aligned16(p->w_kv))
+      return ENGRAM_E_INVALID;
+  }
+  const size_t need = backward_ws(s, N, nullptr, nullptr);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return ENGRAM_E_WORKSPACE;
+  BwdWs w;
+  backward_ws(s, N, &w, (uint8_t*)workspace);
+  hipStream_t hs = (hipStream_t)stream;
+  const bool bf = s.dtype == ENGRAM_BF16;
+
+  ScatterArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  sa.N = N;
+  sa.J = s.J;
+  sa.D = s.D;
+  sa.idx = saved ? saved->idx : nullptr;
+  sa.de = w.de;
+  sa.key_bits = s.key_bits;
+  for (int j = 0; j < s.J; ++j) sa.dense[j] = out->dense[j];
+  sa.keys_out = out->keys;
+  sa.rows_out = out->rows;
+  sa.count_out = out->count;
+  if (N > 0) {
+    {
+      BwdArgs ba;
+      ba.B = B;
+      ba.T = T;
+      ba.d = s.d;
+      ba.taps = s.taps;
+      ba.io_dtype = s.dtype;
+      ba.dy = (const uint8_t*)dy;
+      ba.v = (const uint8_t*)saved->v;
+      ba.k = (const uint8_t*)saved->k;
+      ba.h = (const uint8_t*)hidden;
+      ba.stats = saved->stats;
+      ba.conv_w = p->conv_w;
+      ba.gamma_q = p->gamma_q;
+      ba.gamma_k = p->gamma_k;
+      ba.dkv = w.dkv;
+      Timed tm("bwd_gate_conv", hs);
+      if (launch_bwd_gate_conv(ba, hs) != hipSuccess) return ENGRAM_E_HIP;
+    }
+    {
+      Timed tm("transpose_w", hs);
+      if (launch_transpose_w((const uint8_t*)p->w_kv, w.wt, 2 * s.d, s.d_mem, s.dtype, hs) !=
+          hipSuccess)
+        return ENGRAM_E_HIP;
+    }
+    {
+      GemmArgs ga;
+      std::memset(&ga, 0, sizeof(ga));
+      ga.A = w.wt;
+      ga.B = w.dkv;
+      ga.M = N;
+      ga.F = s.d_mem;
+      ga.K = 2 * s.d;
+      ga.group_m = 4;
+      ga.c_out = w.de;
+      Timed tm("de_gemm", hs);
+      if (launch_gemm(bf ? GEMM_F16 : GEMM_F32, EPI_STORE_F32, ga, hs) != hipSuccess)
+        return ENGRAM_E_HIP;
+    }
+  }
+  if (out->mode == ENGRAM_GRAD_ATOMIC_DENSE) {
+    Timed tm("atomic_scatter", hs);
+    return hip_status(launch_atomic_scatter(sa, hs));
+  }
+  SortBufs sb;
+  carve_sort(w.sort, N, s.J, &sb);
+  Timed tm("sorted_scatter", hs);
+  return hip_status(launch_sorted_scatter(sa, sb, out->mode, hs));
+}
+
+engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* canon_map_host,
+                                   const int32_t* tokens_host, int64_t B, int64_t T,
+                                   const void* const* host_tables, engram_compact* plan,
+                                   void* side_stream) {
+  Shape s;
+  engram_status st = check_config(cfg, &s);
+  if (st != ENGRAM_OK) return st;
+  if (!plan || B < 0 || T < 0) return ENGRAM_E_INVALID;
+  const int64_t N = B * T;
+  const int J = s.J;
+  if (N > 0 && (!canon_map_host || !tokens_host)) return ENGRAM_E_INVALID;
+  if (!plan->counts || !plan->uniq_host || !plan->inverse_host) return ENGRAM_E_INVALID;
+  if (plan->capacity_rows < 0) return ENGRAM_E_INVALID;
+  if (host_tables) {
+    if (!plan->staging_host || !plan->rows_dev || !plan->inverse_dev) return ENGRAM_E_INVALID;
+    for (int j = 0; j < J; ++j)
+      if (!host_tables[j]) return ENGRAM_E_INVALID;
+  }
+  for (int64_t n = 0; n < N; ++n)
+    if (tokens_host[n] < 0 || tokens_host[n] >= cfg->vocab) return ENGRAM_E_INVALID;
+  const HashArgs ha = make_hash_args(cfg, s);
+  const int nthr = (int)std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  auto parallel = [&](int64_t count, auto&& fn) {
+    const int64_t per = (count + nthr - 1) / nthr;
+    std::vector<std::thread> th;
+    for (int t = 0; t < nthr; ++t) {
+      const int64_t lo = t * per, hi = std::min(count, lo + per);
+      if (lo >= hi) break;
+      th.emplace_back([&, lo, hi] { fn(lo, hi); });
+    }
+    for (auto& x : th) x.join();
+  };
+
+  // 1. indices on the host, same hash as the device kernel
+  std::vector<int32_t> idx((size_t)N * J);
+  parallel(N, [&](int64_t lo, int64_t hi) {
+    for (int64_t n = lo; n < hi; ++n) {
+      const int64_t t = n % T;
+      uint32_t c[ENGRAM_MAX_ORDERS] = {0, 0, 0, 0};
+      for (int i = 0; i < s.max_order; ++i)
+        c[i] = (t - i >= 0) ? (uint32_t)canon_map_host[tokens_host[n - i]] : (uint32_t)cfg->pad_id;
+      int j = 0;
+      for (int o = 0; o < cfg->num_orders; ++o)
+        for (int k = 0; k < cfg->heads; ++k, ++j)
+          idx[(size_t)n * J + j] = (int32_t)hash_one(ha, j, cfg->orders[o], c);
+    }
+  });
+  // 2. distinct rows of every table, ascending
+  std::vector<std::vector<int32_t>> uniq(J);
+  parallel(J, [&](int64_t lo, int64_t hi) {
+    for (int64_t j = lo; j < hi; ++j) {
+      std::vector<int32_t>& u = uniq[j];
+      u.resize((size_t)N);
+      for (int64_t n = 0; n < N; ++n) u[n] = idx[(size_t)n * J + j];
+      std::sort(u.begin(), u.end());
+      u.erase(std::unique(u.begin(), u.end()), u.end());
+    }
+  });
+  std::vector<int64_t> base(J + 1, 0);
+  for (int j = 0; j < J; ++j) base[j + 1] = base[j] + (int64_t)uniq[j].size();
+  const int64_t total = base[J];
+  if (total > plan->capacity_rows) return ENGRAM_E_INVALID;
+  for (int j = 0; j < J; ++j) {
+    plan->counts[j] = (int64_t)uniq[j].size();
+    if (!uniq[j].empty())
+      std::memcpy(plan->uniq_host + base[j], uniq[j].data(), uniq[j].size() * sizeof(int32_t));
+  }
+  plan->total_rows = total;
+  // 3. inverse map into the compact buffer
+  parallel(N, [&](int64_t lo, int64_t hi) {
+    for (int64_t n = lo; n < hi; ++n)
+      for (int j = 0; j < J; ++j) {
+        const int32_t key = idx[(size_t)n * J + j];
+        const auto it = std::lower_bound(uniq[j].begin(), uniq[j].end(), key);
+        plan->inverse_host[(size_t)n * J + j] = (int32_t)(base[j] + (it - uniq[j].begin()));
+      }
+  });
+  if (!host_tables) return ENGRAM_OK;
+  // 4. gather the rows into pinned staging, then the async copies
+  const size_t rb = (size_t)s.D * s.es;
+  parallel(total, [&](int64_t lo, int64_t hi) {
+    int j = (int)(std::upper_bound(base.begin(), base.end(), lo) - base.begin()) - 1;
+    for (int64_t u = lo; u < hi; ++u) {
+      while (u >= base[j + 1]) ++j;
+      const int32_t row = plan->uniq_host[u];
+      std::memcpy((uint8_t*)plan->staging_host + (size_t)u * rb,
+                  (const uint8_t*)host_tables[j] + (size_t)row * rb, rb);
+    }
+  });
+  hipStream_t hs = (hipStream_t)side_stream;
+  if (total > 0 &&
+      hipMemcpyAsync(plan->rows_dev, plan->staging_host, (size_t)total * rb, hipMemcpyHostToDevice,
+                     hs) != hipSuccess)
+    return ENGRAM_E_HIP;
+  if (N > 0 && hipMemcpyAsync(plan->inverse_dev, plan->inverse_host, (size_t)N * J * 4,
+                              hipMemcpyHostToDevice, hs) != hipSuccess)
+    return ENGRAM_E_HIP;
+  if (plan->ready_event && hipEventRecord((hipEvent_t)plan->ready_event, hs) != hipSuccess)
+    return ENGRAM_E_HIP;
+  return ENGRAM_OK;
+}
+
+void engram_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> l(g_prof_mu);
+  g_prof_on = on != 0;
+}
+
+void engram_profile_reset(void) {
+  std::lock_guard<std::mutex> l(g_prof_mu);
+  for (auto& r : g_prof) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+}
+
+int32_t engram_profile_read(char* names, size_t names_len, int64_t* launches, double* total_ms,
+                            int32_t max_entries) {
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> l(g_prof_mu);
+    recs.swap(g_prof);
+  }
+  std::vector<std::string> keys;
+  std::vector<int64_t> cnt;
+  std::vector<double> ms;
+  int32_t rc = 0;
+  for (auto& r : recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      rc = -1;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+    size_t i = 0;
+    while (i < keys.size() && keys[i] != r.name) ++i;
+    if (i == keys.size()) {
+      keys.push_back(r.name);
+      cnt.push_back(0);
+      ms.push_back(0.0);
+    }
+    cnt[i] += 1;
+    ms[i] += t;
+  }
+  if (rc < 0) return -1;
+  size_t off = 0;
+  int32_t n = 0;
+  for (size_t i = 0; i < keys.size() && n < max_entries; ++i) {
+    if (names) {
+      if (off + keys[i].size() + 1 > names_len) break;
+      std::memcpy(names + off, keys[i].c_str(), keys[i].size() + 1);
+      off += keys[i].size() + 1;
+    }
+    if (launches) launches[n] = cnt[i];
+    if (total_ms) total_ms[n] = ms[i];
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

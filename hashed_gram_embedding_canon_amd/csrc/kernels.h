@@ -1,0 +1,111 @@
+// Launchers of the Engram HIP kernels (internal to libengram.so).
+#pragma once
+
+#include "common.h"
+
+namespace engram {
+
+// ---------------------------------------------------------------- hashing
+hipError_t launch_hash(const int32_t* tokens, const int32_t* canon, int64_t N, int32_t T,
+                       int32_t* idx, const HashArgs& args, hipStream_t s);
+
+// ---------------------------------------------------------------- gather
+// e[n][j*D..(j+1)*D) = base[j][idx[n][j]] for J tables of rows of row_bytes.
+struct GatherArgs {
+  const uint8_t* base[ENGRAM_MAX_TABLES];
+  int32_t J;
+  int32_t row_chunks;  // row_bytes / 16
+};
+hipError_t launch_gather(const int32_t* idx, uint8_t* e, int64_t N, const GatherArgs& g,
+                         hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+// C^T[f][m] = sum_k A[f][k] * B[m][k]; A: [F][K] (weights), B: [M][K] (tokens).
+enum GemmType { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 };
+enum GemmEpilogue {
+  EPI_KV = 0,   // forward: f < d -> gate partial sums (and optional k), f >= d -> v
+  EPI_STORE_F32 = 1  // plain fp32 store of C[m][f] (backward de)
+};
+struct GemmArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  int64_t M;
+  int32_t F, K;
+  int32_t group_m;     // token tiles walked per f-tile inside one XCD group
+  // EPI_KV
+  int32_t d;           // hidden width: f < d is the key, f >= d the value
+  int32_t io_dtype;    // ENGRAM_F32 / ENGRAM_BF16 of h, k_out, v_out
+  const uint8_t* h;    // [M][d]
+  const float* gamma_q;
+  const float* gamma_k;
+  float* partials;     // [M][d/BF][3]: sum k^2, sum g_q g_k h k, sum h^2
+  uint8_t* k_out;      // [M][d] or null
+  uint8_t* v_out;      // [M][d]
+  // EPI_STORE_F32
+  float* c_out;        // [M][F]
+};
+// Feature-tile width of the GEMM (the k/v boundary and partials use it).
+constexpr int kGemmBF = 256;
+hipError_t launch_gemm(GemmType type, GemmEpilogue epi, const GemmArgs& g, hipStream_t s);
+
+// ---------------------------------------------------------------- gate + conv
+struct GateConvArgs {
+  int64_t B, T;
+  int32_t d, taps, nkt, io_dtype;
+  float eps;
+  const float* partials;  // [N][nkt][3]
+  const uint8_t* v;       // [N][d]
+  const float* conv_w;    // [d][taps]
+  uint8_t* y;             // [N][d]
+  float* stats;           // [N][4] or null
+};
+hipError_t launch_gate_conv(const GateConvArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+struct BwdArgs {
+  int64_t B, T;
+  int32_t d, taps, io_dtype;
+  const uint8_t* dy;      // [N][d]
+  const uint8_t* v;       // [N][d]
+  const uint8_t* k;       // [N][d]
+  const uint8_t* h;       // [N][d]
+  const float* stats;     // [N][4]
+  const float* conv_w;    // [d][taps]
+  const float* gamma_q;
+  const float* gamma_k;
+  uint8_t* dkv;           // [N][2d] fp16 (bf16 io) or fp32 (f32 io)
+};
+hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s);
+
+// W_kv [2d][d_mem] (io dtype) -> Wt [d_mem][2d] (fp16 for bf16 io, fp32 for f32 io)
+hipError_t launch_transpose_w(const uint8_t* w, uint8_t* wt, int32_t rows, int32_t cols,
+                              int32_t io_dtype, hipStream_t s);
+
+// Sort-by-row + segmented reduction of the table gradient.
+struct SortBufs {
+  uint32_t* keys[2];   // [J][N] ping-pong
+  uint32_t* vals[2];   // [J][N]
+  uint32_t* hist;      // [J][256][nblk]
+  uint32_t* seg_count; // [J][nblk2] per-block head counts, then scanned
+  uint32_t* seg_start; // [N*J]
+  uint64_t* seg_key;   // [N*J]
+  uint32_t* total;     // [1]
+};
+struct ScatterArgs {
+  int64_t N;
+  int32_t J, D;
+  const int32_t* idx;     // [N][J]
+  const float* de;        // [N][J*D]
+  int32_t key_bits;       // bits of the largest row index
+  float* dense[ENGRAM_MAX_TABLES];
+  int64_t* keys_out;      // sparse
+  float* rows_out;
+  int64_t* count_out;
+};
+size_t sort_workspace_bytes(int64_t N, int32_t J);
+void carve_sort(uint8_t* base, int64_t N, int32_t J, SortBufs* b);
+hipError_t launch_sorted_scatter(const ScatterArgs& a, const SortBufs& b, int32_t mode,
+                                 hipStream_t s);
+hipError_t launch_atomic_scatter(const ScatterArgs& a, hipStream_t s);
+
+}  // namespace engram

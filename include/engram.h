@@ -1,0 +1,229 @@
+/*
+ * engram.h -- C ABI of the MI355X (gfx950) Engram conditional-memory library
+ * (libengram.so).
+ *
+ * The operation is the Engram module described on the pages about DeepSeek's
+ * "Conditional Memory via Scalable Lookup":
+ *   - "DeepSeek AI II" (taking-lying-flat blog), section "DeepSeek Engram":
+ *     tokenizer compression (a surjection P from raw to canonical ids), suffix
+ *     N-grams g_{t,n} of canonical ids, K hash heads per order n, each with its
+ *     own table E_{n,k} of prime size M_{n,k}, a multiplicative-XOR hash, the
+ *     concatenated memory vector e_t, key/value projections W_K, W_V, RMSNorm
+ *     on query h_t and key k_t before a scalar gate alpha_t in (0,1), the
+ *     gated value alpha_t v_t, a short depthwise causal convolution, and the
+ *     residual add H <- H + Y;
+ *   - same page, system-efficiency part: retrieval depends on token ids only,
+ *     so indices are known before the forward pass; training sends the row
+ *     gradients back to the table rows; inference can keep the tables in host
+ *     memory and fetch the needed rows over PCIe ahead of use;
+ *   - the QbitAI mirror of the paper: one independent table per hash head.
+ * The pages print no formulas; the forms used here are:
+ *   c_t      = P[x_t]  (c_t = pad_id for t < 0, per sequence)
+ *   idx_j(t) = (XOR_{i<n} (m_{j,i} * c_{t-i} mod 2^64)) mod M_j,  j = o*K + k
+ *   e_t      = concat_j E_j[idx_j(t)]                     (d_mem = J*D)
+ *   k_t = W_K e_t,  v_t = W_V e_t                          (W_* is [d][d_mem])
+ *   alpha_t  = sigmoid(<g_q h_t rq_t, g_k k_t rk_t> / sqrt(d)),
+ *              rq_t = (mean(h_t^2)+eps)^-1/2,  rk_t = (mean(k_t^2)+eps)^-1/2
+ *   vt_t     = alpha_t v_t
+ *   z_t      = sum_{i<taps} w[:,i] * vt_{t-i}               (vt = 0 before t=0)
+ *   Y_t      = SiLU(z_t) + vt_t
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller allocates every device, pinned-host and workspace
+ *     buffer; the library never allocates or frees memory.
+ *   - Streams: work is queued on the caller's hipStream_t (passed as void*,
+ *     NULL = the default stream) without host synchronisation.  Calls are
+ *     reentrant and may run on several streams at once if their buffers do
+ *     not overlap.
+ *   - Errors: arguments are validated on the host before any GPU work; a
+ *     rejected call returns a non-zero engram_status and queues nothing.  A
+ *     failed launch returns ENGRAM_E_HIP; faults inside kernels surface when
+ *     the caller synchronises.  Token ids must lie in [0, vocab): this is a
+ *     precondition, not checked on the device.
+ *   - Layout: row-major, densely packed; N = B*T tokens, token n = b*T + t.
+ *     Every pointer must be 16-byte aligned.
+ *   - dtype: ENGRAM_F32 (float) or ENGRAM_BF16 (bfloat16) for tables,
+ *     weights, hidden states, outputs and upstream gradients; the gate and
+ *     conv arithmetic is always fp32, GEMMs accumulate in fp32.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ENGRAM_OK = 0,
+  ENGRAM_E_INVALID = 1,     /* null pointer, bad size/shape, misalignment */
+  ENGRAM_E_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle */
+  ENGRAM_E_WORKSPACE = 3,   /* workspace missing or smaller than engram_workspace_size() */
+  ENGRAM_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} engram_status;
+
+enum { ENGRAM_F32 = 0, ENGRAM_BF16 = 1 };
+
+#define ENGRAM_MAX_ORDERS 4
+#define ENGRAM_MAX_TABLES 32
+
+/* Shapes and addressing constants.  Host struct, read during the call only. */
+typedef struct {
+  int32_t vocab;          /* raw ids lie in [0, vocab) */
+  int32_t canon_vocab;    /* canonical ids lie in [0, canon_vocab) */
+  int32_t num_orders;     /* 1..ENGRAM_MAX_ORDERS */
+  int32_t orders[ENGRAM_MAX_ORDERS]; /* N-gram orders, strictly ascending, each 1..4 */
+  int32_t heads;          /* K hash heads per order; J = num_orders*heads <= 32 */
+  int32_t dim;            /* D columns per table row; D*sizeof(dtype) % 16 == 0, J*D % 128 == 0 */
+  int32_t hidden;         /* d, width of h_t, k_t, v_t, Y_t; d % 256 == 0 */
+  int32_t conv_kernel;    /* taps of the causal depthwise conv, 1..8 */
+  int32_t dtype;          /* ENGRAM_F32 or ENGRAM_BF16 */
+  float rms_eps;          /* eps inside both RMSNorms (e.g. 1e-6) */
+  int32_t pad_id;         /* canonical id used for positions before t = 0 */
+  const int64_t* table_rows;   /* host [J]: M_j, 1 <= M_j < 2^31 (prime by design) */
+  const uint64_t* multipliers; /* host [J][max order]: m_{j,i} multiplies c_{t-i} */
+} engram_config;
+
+/* Learned parameters (device pointers). */
+typedef struct {
+  const int32_t* canon_map;               /* [vocab] raw id -> canonical id */
+  const void* tables[ENGRAM_MAX_TABLES];  /* table j: [M_j][D] dtype */
+  const void* w_kv;       /* [2d][d_mem] dtype: rows 0..d-1 are W_K, rows d..2d-1 are W_V */
+  const float* gamma_q;   /* [d] RMSNorm scale of the query, NULL = all ones */
+  const float* gamma_k;   /* [d] RMSNorm scale of the key, NULL = all ones */
+  const float* conv_w;    /* [d][conv_kernel] fp32, tap i multiplies vt_{t-i} */
+} engram_params;
+
+/* Optional forward outputs (device).  NULL members are not written.  The
+ * table-gradient backward needs idx, stats, k and v. */
+typedef struct {
+  int32_t* idx;   /* [N][J] row indices idx_j(t) (table-local; compact-local in compact mode) */
+  float* stats;   /* [N][4]: alpha_t, rq_t, rk_t, <g_q h_t, g_k k_t> (the last without rq, rk) */
+  void* k;        /* [N][d] dtype */
+  void* v;        /* [N][d] dtype */
+  void* e;        /* [N][d_mem] dtype, the gathered memory vectors */
+} engram_saved;
+
+/*
+ * Compact row buffer produced by engram_prefetch_plan() and consumed by
+ * engram_forward() when the tables live in host memory.  All buffers are
+ * caller-owned; capacity_rows >= N*J always suffices.
+ */
+typedef struct {
+  int64_t capacity_rows;  /* rows that uniq_host, staging_host and rows_dev hold */
+  int64_t total_rows;     /* out: unique rows over all tables */
+  int64_t* counts;        /* host [J], out: unique rows per table */
+  int32_t* uniq_host;     /* host [capacity_rows], out: ascending table-local rows, table after table */
+  int32_t* inverse_host;  /* pinned host [N][J], out: row of token n, table j, in the compact buffer */
+  void* staging_host;     /* pinned host [capacity_rows][D] dtype, out: the unique rows */
+  void* rows_dev;         /* device [capacity_rows][D] dtype: async-copy destination of the rows */
+  int32_t* inverse_dev;   /* device [N][J]: async-copy destination of inverse_host */
+  void* ready_event;      /* hipEvent_t recorded on the side stream after the copies
+                             (engram_forward waits on it when non-NULL) */
+} engram_compact;
+
+/* Table-gradient output of engram_backward_table_grad(). */
+enum {
+  ENGRAM_GRAD_SORTED_SPARSE = 0, /* sort by (table,row) + segmented fp32 reduce -> {keys, rows, count} */
+  ENGRAM_GRAD_SORTED_DENSE = 1,  /* same reduction, each unique row added into dense[j] (deterministic) */
+  ENGRAM_GRAD_ATOMIC_DENSE = 2   /* fp32 atomicAdd of every token's slice into dense[j] (order varies) */
+};
+
+typedef struct {
+  int32_t mode;          /* ENGRAM_GRAD_* */
+  int64_t* keys;         /* SPARSE: device [N*J], out: (j << 32) | row, ascending */
+  float* rows;           /* SPARSE: device [N*J][D], out: summed gradient of each key */
+  int64_t* count;        /* SPARSE: device [1], out: number of keys */
+  float* dense[ENGRAM_MAX_TABLES]; /* DENSE: device [M_j][D] fp32, gradients are ADDED (caller zeroes) */
+} engram_table_grad;
+
+enum { ENGRAM_OP_FORWARD = 0, ENGRAM_OP_BACKWARD = 1 };
+
+/* Bytes of device workspace the operation needs for B x T tokens (0 on bad config). */
+size_t engram_workspace_size(const engram_config* cfg, int64_t B, int64_t T, int32_t op);
+
+/* Static text for a status code. */
+const char* engram_status_string(engram_status s);
+
+/*
+ * Canonicalisation + multi-head hashing ("DeepSeek AI II", section "DeepSeek
+ * Engram": tokenizer compression, suffix N-grams, multi-head hashing into
+ * prime-sized tables).  tokens: device [B][T] raw ids; canon_map: device
+ * [vocab]; idx: device [B*T][J] int32 output.  Each batch row is its own
+ * sequence (positions before its start read pad_id).
+ */
+engram_status engram_hash_indices(const engram_config* cfg, const int32_t* canon_map,
+                                  const int32_t* tokens, int64_t B, int64_t T, int32_t* idx,
+                                  void* stream);
+
+/*
+ * Forward pass: hashing, row gather and concatenation, key/value projection,
+ * RMSNorm-dot-sigmoid gate, gated value, causal depthwise conv + SiLU +
+ * residual ("DeepSeek AI II", section "DeepSeek Engram": retrieval, then
+ * context-aware gating and the short causal convolution).
+ *   tokens: device [B][T] (ignored in compact mode); hidden: device [B][T][d]
+ *   dtype; y: device [B][T][d] dtype output (Y only; the caller adds it to H);
+ *   saved: NULL or buffers to keep (see engram_saved);
+ *   compact: NULL, or the plan of engram_prefetch_plan(): rows are read from
+ *   compact->rows_dev through compact->inverse_dev instead of params->tables;
+ *   workspace: device, >= engram_workspace_size(cfg, B, T, ENGRAM_OP_FORWARD).
+ */
+engram_status engram_forward(const engram_config* cfg, const engram_params* params,
+                             const int32_t* tokens, const void* hidden, int64_t B, int64_t T,
+                             void* y, const engram_saved* saved, const engram_compact* compact,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Table-gradient backward ("DeepSeek AI II", system-efficiency part: in
+ * training the gradients of the gathered rows are dispatched back to the rows
+ * they came from).  Chain rule through the conv, the gate, the RMSNorm of the
+ * key and both projections to de_t, then dE_j[r] = sum_{t: idx_j(t)=r}
+ * de_t[j*D:(j+1)*D] with fp32 accumulation.
+ *   hidden, dy: device [B][T][d] dtype; saved: idx, stats, k, v from
+ *   engram_forward on the same inputs (required); out: see engram_table_grad;
+ *   workspace: >= engram_workspace_size(cfg, B, T, ENGRAM_OP_BACKWARD).
+ */
+engram_status engram_backward_table_grad(const engram_config* cfg, const engram_params* params,
+                                         const void* hidden, const void* dy, int64_t B, int64_t T,
+                                         const engram_saved* saved, engram_table_grad* out,
+                                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Prefetch plan for tables held in host memory ("DeepSeek AI II",
+ * system-efficiency part: indices are fixed by the token ids before the
+ * forward pass, so rows are fetched asynchronously over PCIe while earlier
+ * layers compute).  Runs on host threads: hashes tokens_host, sorts the
+ * distinct rows of every table (plan->uniq_host, plan->counts), builds the
+ * compact inverse map (plan->inverse_host), and -- when host_tables is not
+ * NULL -- gathers the rows from the host tables into plan->staging_host and
+ * queues hipMemcpyAsync of rows and inverse map to the device buffers on
+ * side_stream, then records plan->ready_event there.  Returns when the host
+ * work is done; the copies run asynchronously.
+ *   canon_map_host: host [vocab]; tokens_host: host [B][T];
+ *   host_tables: NULL (plan only) or host [J] pointers to [M_j][D] dtype
+ *   (pinned memory makes the copy a true async DMA).
+ */
+engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* canon_map_host,
+                                   const int32_t* tokens_host, int64_t B, int64_t T,
+                                   const void* const* host_tables, engram_compact* plan,
+                                   void* side_stream);
+
+/*
+ * Kernel timing for measurement: while enabled, every kernel the library
+ * launches is bracketed by a pair of hipEvents on its stream.
+ * engram_profile_read() synchronises those events and returns, per kernel
+ * name, the number of launches and the summed milliseconds (at most
+ * max_entries entries; names are written NUL-separated into names).
+ * Returns the number of entries, or -1 on error.
+ */
+void engram_profile_enable(int32_t on);
+void engram_profile_reset(void);
+int32_t engram_profile_read(char* names, size_t names_len, int64_t* launches, double* total_ms,
+                            int32_t max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ENGRAM_H */

@@ -1,0 +1,195 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/engram.h declares, validates arguments before any
+GPU work, sizes workspaces, and its host prefetch planner (which runs the
+same hash as the device kernel) matches the oracle bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def eg():
+    import hashed_gram_embedding_canon_amd as eg
+    if not os.path.exists(eg.LIB_PATH):
+        pytest.fail("libengram.so is not built: run __graft_entry__.build()")
+    eg.lib()
+    return eg
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "engram.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(eg):
+    names = _declared_functions()
+    assert len(names) == 9, names
+    L = ctypes.CDLL(eg.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(eg.EXPORTS)
+
+
+def test_status_strings(eg):
+    assert eg.engram_status_string(0) == "ok"
+    for s in range(1, 5):
+        assert eg.engram_status_string(s) not in ("ok", "unknown status")
+    assert eg.engram_status_string(99) == "unknown status"
+
+
+def _cfg(eg, **over):
+    wl = synth.get_workload("tiny")
+    inp = synth.Inputs(wl)
+    kw = dict(vocab=wl.vocab, canon_vocab=wl.canon_vocab, orders=wl.orders, heads=wl.heads,
+              dim=wl.dim, hidden=wl.hidden, table_rows=inp.table_rows, multipliers=inp.multipliers,
+              dtype=eg.ENGRAM_F32, conv_kernel=4)
+    kw.update(over)
+    return eg.Config(**kw)
+
+
+def test_workspace_sizes(eg):
+    cfg = _cfg(eg)
+    f = eg.engram_workspace_size(cfg, 2, 100, eg.ENGRAM_OP_FORWARD)
+    b = eg.engram_workspace_size(cfg, 2, 100, eg.ENGRAM_OP_BACKWARD)
+    assert f > 200 * 256 * 4 and b > f  # e alone is N*d_mem*4 bytes
+    assert eg.engram_workspace_size(cfg, 2, 100, 7) == 0
+    assert eg.engram_workspace_size(_cfg(eg, hidden=200), 2, 100, 0) == 0
+    assert eg.engram_workspace_size(cfg, -1, 100, 0) == 0
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; validation fails before any use
+
+
+def _fwd(eg, cfg, **over):
+    p = eg.make_params(canon_map=FAKE, tables=[FAKE] * cfg.J, w_kv=FAKE, conv_w=FAKE)
+    kw = dict(tokens=FAKE, hidden=FAKE, B=2, T=8, y=FAKE, workspace=FAKE, ws_bytes=1 << 40)
+    kw.update(over)
+    return eg.lib().engram_forward(cfg.ref, ctypes.byref(p), kw["tokens"], kw["hidden"], kw["B"],
+                                   kw["T"], kw["y"], None, None, kw["workspace"], kw["ws_bytes"], None)
+
+
+def test_forward_validation(eg):
+    bad_orders = _cfg(eg, orders=(3, 2))
+    assert _fwd(eg, bad_orders) == eg.ENGRAM_E_INVALID
+    assert _fwd(eg, _cfg(eg, orders=(2, 5))) == eg.ENGRAM_E_INVALID
+    assert _fwd(eg, _cfg(eg, dtype=7)) == eg.ENGRAM_E_UNSUPPORTED
+    assert _fwd(eg, _cfg(eg, hidden=300)) == eg.ENGRAM_E_UNSUPPORTED
+    assert _fwd(eg, _cfg(eg, dim=6)) == eg.ENGRAM_E_UNSUPPORTED  # 24-byte rows
+    assert _fwd(eg, _cfg(eg, conv_kernel=9)) == eg.ENGRAM_E_UNSUPPORTED
+    assert _fwd(eg, _cfg(eg, heads=9)) == eg.ENGRAM_E_UNSUPPORTED  # J = 18 -> d_mem 576
+    cfg = _cfg(eg)
+    assert _fwd(eg, cfg, hidden=None) == eg.ENGRAM_E_INVALID
+    assert _fwd(eg, cfg, y=FAKE + 4) == eg.ENGRAM_E_INVALID  # misaligned
+    assert _fwd(eg, cfg, B=-1) == eg.ENGRAM_E_INVALID
+    assert _fwd(eg, cfg, workspace=None) == eg.ENGRAM_E_WORKSPACE
+    assert _fwd(eg, cfg, ws_bytes=1000) == eg.ENGRAM_E_WORKSPACE
+    assert _fwd(eg, cfg, B=0) == eg.ENGRAM_OK  # empty batch: nothing to do
+    assert _fwd(eg, cfg, T=0) == eg.ENGRAM_OK
+    rows = np.array([10007] * 7 + [0], np.int64)
+    assert _fwd(eg, _cfg(eg, table_rows=rows)) == eg.ENGRAM_E_INVALID
+
+
+def test_backward_and_hash_validation(eg):
+    cfg = _cfg(eg)
+    L = eg.lib()
+    p = eg.make_params(canon_map=FAKE, tables=[FAKE] * cfg.J, w_kv=FAKE, conv_w=FAKE)
+    out = eg.engram_table_grad()
+    out.mode = 5
+    assert L.engram_backward_table_grad(cfg.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, None,
+                                        ctypes.byref(out), FAKE, 1 << 40, None) == eg.ENGRAM_E_INVALID
+    out.mode = eg.ENGRAM_GRAD_SORTED_SPARSE
+    out.keys = out.rows = out.count = FAKE
+    # saved tensors are required
+    assert L.engram_backward_table_grad(cfg.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, None,
+                                        ctypes.byref(out), FAKE, 1 << 40, None) == eg.ENGRAM_E_INVALID
+    sv = eg.make_saved(idx=FAKE, stats=FAKE, k=FAKE, v=FAKE)
+    assert L.engram_backward_table_grad(cfg.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, ctypes.byref(sv),
+                                        ctypes.byref(out), FAKE, 16, None) == eg.ENGRAM_E_WORKSPACE
+    out.mode = eg.ENGRAM_GRAD_ATOMIC_DENSE  # dense pointers missing
+    assert L.engram_backward_table_grad(cfg.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, ctypes.byref(sv),
+                                        ctypes.byref(out), FAKE, 1 << 40, None) == eg.ENGRAM_E_INVALID
+    assert L.engram_hash_indices(cfg.ref, None, FAKE, 2, 8, FAKE, None) == eg.ENGRAM_E_INVALID
+    assert L.engram_hash_indices(cfg.ref, FAKE, FAKE, 0, 8, FAKE, None) == eg.ENGRAM_OK
+
+
+def _plan(eg, cfg, tokens, canon, J):
+    N = tokens.size
+    cap = N * J
+    counts = np.zeros(J, np.int64)
+    uniq = np.zeros(max(cap, 1), np.int32)
+    inv = np.zeros((N, J), np.int32)
+    plan = eg.engram_compact()
+    plan.capacity_rows = cap
+    plan.counts, plan.uniq_host, plan.inverse_host = counts.ctypes.data, uniq.ctypes.data, inv.ctypes.data
+    eg.engram_prefetch_plan(cfg, canon, tokens, B=tokens.shape[0], T=tokens.shape[1], plan=plan)
+    return uniq[: plan.total_rows], counts, inv
+
+
+@pytest.mark.parametrize("name,B,T", [("tiny", 1, 512), ("tiny", 3, 77), ("small", 2, 1500)])
+def test_host_plan_matches_oracle(eg, oracle_lib, name, B, T):
+    """Host planner (same hash code as the device kernel) vs the oracle: bit-exact."""
+    wl = synth.get_workload(name).with_shape(B, T)
+    inp = synth.Inputs(wl)
+    cfg = eg.Config(vocab=wl.vocab, canon_vocab=wl.canon_vocab, orders=wl.orders, heads=wl.heads,
+                    dim=wl.dim, hidden=wl.hidden, table_rows=inp.table_rows,
+                    multipliers=inp.multipliers, dtype=eg.ENGRAM_BF16 if wl.dtype == "bf16" else 0)
+    tabs = [np.zeros((int(m), 1), np.float32) for m in inp.table_rows]  # rows are not read
+    p = oracle_lib.Problem(orders=wl.orders, heads=wl.heads, mult=inp.multipliers,
+                           table_rows=inp.table_rows, pad_id=wl.pad_id, canon_map=inp.canon_map,
+                           tokens=inp.tokens, tables=tabs)
+    idx = p.hash()
+    u_ref, c_ref, inv_ref = oracle_lib.prefetch_plan(idx)
+    u, c, inv = _plan(eg, cfg, inp.tokens, inp.canon_map, wl.J)
+    assert np.array_equal(c, c_ref)
+    assert np.array_equal(u, u_ref)
+    base = np.concatenate([[0], np.cumsum(c_ref)[:-1]])
+    assert np.array_equal(inv, inv_ref + base[None, :].astype(np.int32))
+
+
+def test_host_plan_adversarial_multipliers(eg, oracle_lib):
+    """Multipliers near 2^64 and large ids stress the 64-bit wrap and the mod-prime reduction."""
+    V = 1 << 17
+    J = 4
+    rows = np.array([2147483647, 4450003, 13, 1000003], np.int64)  # includes 2^31-1
+    mult = np.array([[2**64 - 1, 2**63 + 1, 3], [2**64 - 3, 1, 2**62 + 7], [5, 7, 2**64 - 5],
+                     [2**63 - 1, 2**64 - 7, 9]], dtype=np.uint64)
+    tokens = (synth.u64_stream(3, 2 * 300) % np.uint64(V)).astype(np.int32).reshape(2, 300)
+    tokens[0, :4] = V - 1
+    canon = np.arange(V, dtype=np.int32)
+    cfg = eg.Config(vocab=V, canon_vocab=V, orders=(2, 3), heads=2, dim=64, hidden=256,
+                    table_rows=rows, multipliers=mult, dtype=eg.ENGRAM_BF16)
+    tabs = [np.zeros((1, 1), np.float32)] * J
+    # a hash-only oracle problem: tables are never read by hash()
+    p = oracle_lib.Problem(orders=(2, 3), heads=2, mult=mult, table_rows=[1] * J, pad_id=0,
+                           canon_map=canon, tokens=tokens, tables=tabs)
+    p.table_rows[:] = rows  # the hash reads M_j through this array
+    idx = p.hash()
+    u_ref, c_ref, inv_ref = oracle_lib.prefetch_plan(idx)
+    u, c, inv = _plan(eg, cfg, tokens, canon, J)
+    assert np.array_equal(c, c_ref) and np.array_equal(u, u_ref)
+    # brute force of a few positions with Python integers
+    for (b, t) in ((0, 0), (0, 3), (1, 299)):
+        ctx = [int(tokens[b, t - i]) if t - i >= 0 else 0 for i in range(3)]
+        j = 0
+        for n in (2, 3):
+            for _ in range(2):
+                x = 0
+                for i in range(n):
+                    x ^= (int(mult[j, i]) * ctx[i]) % (1 << 64)
+                assert idx[b * 300 + t, j] == x % int(rows[j])
+                j += 1
+
+
+def test_profile_api_without_launches(eg):
+    eg.engram_profile_enable(True)
+    eg.engram_profile_reset()
+    assert eg.engram_profile_read() == {}
+    eg.engram_profile_enable(False)
