@@ -39,6 +39,10 @@ def kernel_units(wl, N):
         "gather": {"bound": "hbm", "bytes": N * J * 4 + 2 * N * dm * es},
         "proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * 2 * d,
                       "bytes": N * dm * es + 2 * d * dm * es + 2 * N * d * es + N * nkt * 12},
+        # the same projection reading the table rows itself (row gather fused)
+        "gather_proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * 2 * d,
+                             "bytes": N * J * 4 + N * dm * es + 2 * d * dm * es + 2 * N * d * es
+                             + N * nkt * 12},
         "gate_conv": {"bound": "hbm", "bytes": 2 * N * d * es + N * nkt * 12},
     }
 
@@ -66,6 +70,25 @@ def cpu_baseline(inp, budget_s: float):
                       f"(each: hash, gather, both projections, gate of 4 tokens, conv), {dt:.1f} s"}
 
 
+def copy_calibration(nbytes: int):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(5):
+        start.record()
+        dst.copy_(src)
+        end.record()
+        torch.cuda.synchronize()
+        ms.append(start.elapsed_time(end))
+    best = min(ms)
+    print(json.dumps({"copy_bytes": nbytes, "best_ms": best,
+                      "GBps_read_plus_write": round(2 * nbytes / (best * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -74,7 +97,16 @@ def main():
     ap.add_argument("--workload", default="engram27b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--materialize-e", action="store_true",
+                    help="gather e into memory and run the projection on it (instead of the "
+                         "projection reading the table rows itself)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 5 times (the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU table sharding is a design note, not a code path", file=sys.stderr)
@@ -97,8 +129,9 @@ def main():
     log(f"[bench] inputs resident in HBM after {time.perf_counter() - t:.1f} s")
     y = torch.empty(wl.B, wl.T, wl.hidden, dtype=dp.tdtype, device="cuda")
     ws = dp.workspace(eg.ENGRAM_OP_FORWARD)
+    saved = dp.alloc_saved(("e",)) if args.materialize_e else None
     for _ in range(args.warmup):
-        dp.forward(ws=ws, y=y)
+        dp.forward(saved, ws=ws, y=y)
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
@@ -109,7 +142,7 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        dp.forward(ws=ws, y=y)
+        dp.forward(saved, ws=ws, y=y)
     end.record()
     torch.cuda.synchronize()
     eg.engram_profile_enable(False)
@@ -143,8 +176,9 @@ def main():
             ach = u["bytes"] / avg_s / 1e9
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    mem_ms = sum(prof[k][1] / prof[k][0] for k in ("gather", "gate_conv") if k in prof)
-    mem_bytes = sum(units[k]["bytes"] for k in ("gather", "gate_conv"))
+    mem_names = [k for k in ("gather", "gate_conv") if k in prof]
+    mem_ms = sum(prof[k][1] / prof[k][0] for k in mem_names)
+    mem_bytes = sum(units[k]["bytes"] for k in mem_names)
     es = 2 if wl.dtype == "bf16" else 4
     alg_per_token = wl.J * wl.dim * es + 2 * wl.hidden * es + 4  # rows + h + Y + token id
 
@@ -161,12 +195,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
+        "config": {"workload": wl.name, "row_gather": "materialized e" if args.materialize_e else "fused into projection", "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
                    "rows_per_table": list(wl.rows[:1]) + ["..."], "dim": wl.dim,
                    "d_mem": wl.d_mem, "hidden": wl.hidden, "table_params": wl.table_params,
                    "zipf_s": wl.zipf_s, "vocab": wl.vocab, "canon_vocab": wl.canon_vocab},
         "roofline": roof,
-        "hbm_gather_gate_conv": {"alg_GBps": round(mem_bytes / (mem_ms * 1e-3) / 1e9, 1) if mem_ms else None,
+        "hbm_gather_gate_conv": {"kernels": mem_names, "alg_GBps": round(mem_bytes / (mem_ms * 1e-3) / 1e9, 1) if mem_ms else None,
                                  "frac": round(mem_bytes / (mem_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if mem_ms else None,
                                  "ms": round(mem_ms, 4)},
         "end_to_end_alg_GBps": round(alg_per_token * N / (ms * 1e-3) / 1e9, 1),

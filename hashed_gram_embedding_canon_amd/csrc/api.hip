@@ -130,7 +130,23 @@ struct FwdWs {
   float* partials;
 };
 
-size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out, uint8_t* base) {
+// The projection reads the table rows directly (row gather fused into its B
+// operand) unless the caller asks for e or the shape is outside what the
+// fused loads handle; then e is gathered into memory first.
+bool fused_gather(const Shape& s, const engram_saved* sv) {
+  if (sv && sv->e) return false;
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.F = 2 * s.d;
+  ga.K = s.d_mem;
+  ga.group_m = 1;
+  ga.J = s.J;
+  ga.D = s.D;
+  return gemm_supported(s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32, ga, true);
+}
+
+size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out, uint8_t* base,
+                  bool worst_case = false) {
   size_t off = 0;
   auto take = [&](size_t bytes) -> uint8_t* {
     uint8_t* p = base ? base + off : nullptr;
@@ -139,7 +155,12 @@ size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out,
   };
   FwdWs w{};
   w.idx = (sv && sv->idx) ? sv->idx : (int32_t*)take((size_t)N * s.J * 4);
-  w.e = (sv && sv->e) ? (uint8_t*)sv->e : take((size_t)N * s.d_mem * s.es);
+  if (sv && sv->e)
+    w.e = (uint8_t*)sv->e;
+  else if (worst_case || !fused_gather(s, sv))
+    w.e = take((size_t)N * s.d_mem * s.es);
+  else
+    w.e = nullptr;
   w.v = (sv && sv->v) ? (uint8_t*)sv->v : take((size_t)N * s.d * s.es);
   w.partials = (float*)take((size_t)N * (s.d / kGemmBF) * 3 * 4);
   if (out) *out = w;
@@ -178,7 +199,7 @@ size_t engram_workspace_size(const engram_config* cfg, int64_t B, int64_t T, int
   Shape s;
   if (check_config(cfg, &s) != ENGRAM_OK || B < 0 || T < 0) return 0;
   const int64_t N = B * T;
-  if (op == ENGRAM_OP_FORWARD) return forward_ws(s, N, nullptr, nullptr, nullptr);
+  if (op == ENGRAM_OP_FORWARD) return forward_ws(s, N, nullptr, nullptr, nullptr, true);
   if (op == ENGRAM_OP_BACKWARD) return backward_ws(s, N, nullptr, nullptr);
   return 0;
 }
@@ -274,7 +295,8 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
       return ENGRAM_E_HIP;
     for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
   }
-  {
+  const bool fused = w.e == nullptr;
+  if (!fused) {
     Timed tm("gather", hs);
     if (launch_gather(idx, w.e, N, g, hs) != hipSuccess) return ENGRAM_E_HIP;
   }
@@ -283,6 +305,12 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     std::memset(&ga, 0, sizeof(ga));
     ga.A = (const uint8_t*)p->w_kv;
     ga.B = w.e;
+    if (fused) {
+      ga.idx = idx;
+      ga.J = s.J;
+      ga.D = s.D;
+      for (int j = 0; j < s.J; ++j) ga.tables[j] = g.base[j];
+    }
     ga.M = N;
     ga.F = 2 * s.d;
     ga.K = s.d_mem;
@@ -295,7 +323,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     ga.partials = w.partials;
     ga.k_out = saved ? (uint8_t*)saved->k : nullptr;
     ga.v_out = w.v;
-    Timed tm("proj_gemm", hs);
+    Timed tm(fused ? "gather_proj_gemm" : "proj_gemm", hs);
     if (launch_gemm(s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32, EPI_KV, ga, hs) != hipSuccess)
       return ENGRAM_E_HIP;
   }

@@ -43,9 +43,14 @@ struct GemmArgs {
   uint8_t* v_out;      // [M][d]
   // EPI_STORE_F32
   float* c_out;        // [M][F]
+  // B gathered from tables (forward only): B[m][j*D + c] = tables[j][idx[m][j]][c]
+  const int32_t* idx;  // [M][J] or null (then B is read as a dense matrix)
+  const uint8_t* tables[ENGRAM_MAX_TABLES];
+  int32_t J, D;
 };
 // Feature-tile width of the GEMM (the k/v boundary and partials use it).
 constexpr int kGemmBF = 256;
+bool gemm_supported(GemmType type, const GemmArgs& g, bool gather);
 hipError_t launch_gemm(GemmType type, GemmEpilogue epi, const GemmArgs& g, hipStream_t s);
 
 // ---------------------------------------------------------------- gate + conv
