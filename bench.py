@@ -97,9 +97,9 @@ def main():
     ap.add_argument("--workload", default="engram27b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--materialize-e", action="store_true",
-                    help="gather e into memory and run the projection on it (instead of the "
-                         "projection reading the table rows itself)")
+    ap.add_argument("--fused-gather", action="store_true",
+                    help="let the projection read the table rows itself (ENGRAM_FLAG_FUSED_GATHER) "
+                         "instead of gathering e into the workspace first")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -124,12 +124,12 @@ def main():
         f"table params={wl.table_params / 1e9:.2f}B; generating inputs")
     t = time.perf_counter()
     inp = synth.Inputs(wl)
-    dp = H.DeviceProblem(inp)
+    dp = H.DeviceProblem(inp, flags=eg.ENGRAM_FLAG_FUSED_GATHER if args.fused_gather else 0)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM after {time.perf_counter() - t:.1f} s")
     y = torch.empty(wl.B, wl.T, wl.hidden, dtype=dp.tdtype, device="cuda")
     ws = dp.workspace(eg.ENGRAM_OP_FORWARD)
-    saved = dp.alloc_saved(("e",)) if args.materialize_e else None
+    saved = None
     for _ in range(args.warmup):
         dp.forward(saved, ws=ws, y=y)
     torch.cuda.synchronize()
@@ -195,7 +195,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "row_gather": "materialized e" if args.materialize_e else "fused into projection", "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
+        "config": {"workload": wl.name, "row_gather": "fused into projection" if args.fused_gather else "gathered into workspace", "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
                    "rows_per_table": list(wl.rows[:1]) + ["..."], "dim": wl.dim,
                    "d_mem": wl.d_mem, "hidden": wl.hidden, "table_params": wl.table_params,
                    "zipf_s": wl.zipf_s, "vocab": wl.vocab, "canon_vocab": wl.canon_vocab},

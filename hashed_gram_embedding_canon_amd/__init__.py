@@ -19,6 +19,7 @@ ENGRAM_OK, ENGRAM_E_INVALID, ENGRAM_E_UNSUPPORTED, ENGRAM_E_WORKSPACE, ENGRAM_E_
 ENGRAM_F32, ENGRAM_BF16 = 0, 1
 ENGRAM_MAX_ORDERS = 4
 ENGRAM_MAX_TABLES = 32
+ENGRAM_FLAG_FUSED_GATHER = 1
 ENGRAM_GRAD_SORTED_SPARSE, ENGRAM_GRAD_SORTED_DENSE, ENGRAM_GRAD_ATOMIC_DENSE = 0, 1, 2
 ENGRAM_OP_FORWARD, ENGRAM_OP_BACKWARD = 0, 1
 
@@ -40,6 +41,7 @@ class engram_config(ctypes.Structure):
         ("pad_id", ctypes.c_int32),
         ("table_rows", _vp),
         ("multipliers", _vp),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -159,7 +161,7 @@ class Config:
     """engram_config plus the host arrays it points at (kept alive here)."""
 
     def __init__(self, *, vocab, canon_vocab, orders, heads, dim, hidden, table_rows, multipliers,
-                 dtype=ENGRAM_BF16, conv_kernel=4, rms_eps=1e-6, pad_id=0):
+                 dtype=ENGRAM_BF16, conv_kernel=4, rms_eps=1e-6, pad_id=0, flags=0):
         import numpy as np
         self.table_rows = np.ascontiguousarray(table_rows, dtype=np.int64)
         self.multipliers = np.ascontiguousarray(multipliers, dtype=np.uint64)
@@ -173,6 +175,7 @@ class Config:
         c.rms_eps, c.pad_id = float(rms_eps), int(pad_id)
         c.table_rows = self.table_rows.ctypes.data
         c.multipliers = self.multipliers.ctypes.data
+        c.flags = int(flags)
         self.c = c
         self.J = len(orders) * int(heads)
         self.d_mem = self.J * int(dim)

@@ -20,9 +20,12 @@ struct Shape {
   int J, D, d, d_mem, taps, max_order, es;
   int32_t dtype;
   int key_bits;
+  uint32_t flags;
 };
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// LDS stage shape of the MFMA GEMMs (bytes of K per stage; see gemm.hip)
+constexpr int32_t kGemmStageBytes = 128;
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 engram_status check_config(const engram_config* c, Shape* s) {
@@ -43,6 +46,7 @@ engram_status check_config(const engram_config* c, Shape* s) {
   if (c->dim < 1 || c->hidden < 1) return ENGRAM_E_INVALID;
   if (c->conv_kernel < 1 || c->conv_kernel > 8) return ENGRAM_E_UNSUPPORTED;
   if (!(c->rms_eps >= 0.f)) return ENGRAM_E_INVALID;
+  if (c->flags & ~(uint32_t)ENGRAM_FLAG_FUSED_GATHER) return ENGRAM_E_INVALID;
   const int es = (int)dtype_size(c->dtype);
   if ((c->dim * es) % 16 != 0) return ENGRAM_E_UNSUPPORTED;
   const int d_mem = J * c->dim;
@@ -65,6 +69,7 @@ engram_status check_config(const engram_config* c, Shape* s) {
   s->es = es;
   s->dtype = c->dtype;
   s->key_bits = bits;
+  s->flags = c->flags;
   return ENGRAM_OK;
 }
 
@@ -130,16 +135,19 @@ struct FwdWs {
   float* partials;
 };
 
-// The projection reads the table rows directly (row gather fused into its B
-// operand) unless the caller asks for e or the shape is outside what the
-// fused loads handle; then e is gathered into memory first.
+// By default e is gathered into memory and the projection reads it as a dense
+// matrix.  With ENGRAM_FLAG_FUSED_GATHER the projection reads the table rows
+// directly (row gather fused into its B operand) unless the caller asks for e
+// or the shape is outside what the fused loads handle.
 bool fused_gather(const Shape& s, const engram_saved* sv) {
+  if (!(s.flags & ENGRAM_FLAG_FUSED_GATHER)) return false;
   if (sv && sv->e) return false;
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.F = 2 * s.d;
   ga.K = s.d_mem;
   ga.group_m = 1;
+  ga.stage_bytes = kGemmStageBytes;
   ga.J = s.J;
   ga.D = s.D;
   return gemm_supported(s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32, ga, true);
@@ -253,7 +261,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     return ENGRAM_E_INVALID;
   if (compact) {
     if (!compact->rows_dev || !compact->inverse_dev) return ENGRAM_E_INVALID;
-    if (!aligned16(compact->rows_dev)) return ENGRAM_E_INVALID;
+    if (!aligned16(compact->rows_dev) || !aligned16(compact->inverse_dev)) return ENGRAM_E_INVALID;
   } else {
     if (!tokens || !p->canon_map) return ENGRAM_E_INVALID;
     for (int j = 0; j < s.J; ++j)
@@ -315,6 +323,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     ga.F = 2 * s.d;
     ga.K = s.d_mem;
     ga.group_m = 4;
+    ga.stage_bytes = kGemmStageBytes;
     ga.d = s.d;
     ga.io_dtype = s.dtype;
     ga.h = (const uint8_t*)hidden;
@@ -428,6 +437,7 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
       ga.F = s.d_mem;
       ga.K = 2 * s.d;
       ga.group_m = 4;
+      ga.stage_bytes = kGemmStageBytes;
       ga.c_out = w.de;
       Timed tm("de_gemm", hs);
       if (launch_gemm(bf ? GEMM_F16 : GEMM_F32, EPI_STORE_F32, ga, hs) != hipSuccess)

@@ -82,6 +82,15 @@ __device__ inline void store4(uint8_t* base, int64_t i, int io, float a, float b
   }
 }
 
+// One accumulator value copied out of its AGPR at the point of use.  Left to
+// itself the register allocator moves all 256 accumulators into VGPRs when
+// the epilogue does arithmetic on them, and spills.
+__device__ inline float acc_read(float x) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(x));
+  return r;
+}
+
 // 16-byte direct-to-LDS global load: lane l's 16 bytes land at lds_dst + 16*l
 // (lds_dst is wave-uniform and goes through M0).  Written as asm so that the
 // compiler does not treat every later LDS read as aliasing the write and wait
@@ -115,34 +124,49 @@ __device__ inline void load_lds16(const void* src, void* lds_dst) {
 constexpr int kBF = kGemmBF;  // features per tile
 constexpr int kBT = 256;      // tokens per tile
 constexpr int kNT = 256;      // threads (4 waves)
-constexpr int kStageBytes = 64;
-constexpr int kStages = 4;
-constexpr int kTileStage = 256 * kStageBytes;  // one operand, one stage
 constexpr int kGatherMaxJ = 16;
+constexpr int kRedFloats = 2 * 2 * 4 * 32 * 3;  // [2 wf][2 wt][4 blocks][32 tokens][3 sums]
 
-__device__ inline int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Stage shapes: SB bytes of K per row and stage.  64-byte stages use a
+// 4-deep ring (loads 3 stages ahead), 128-byte stages a 2-deep ring; both
+// fill 128 KB of LDS.  16-byte pieces of a row are XOR-swizzled so that the
+// fragment reads of 32 consecutive rows hit distinct banks for both 8- and
+// 16-lane LDS phases (found by exhaustive search over XOR maps of the row
+// bits 0..3).
+template <int SB>
+struct Stage {
+  static constexpr int kStages = SB == 64 ? 4 : 2;
+  static constexpr int kOperandBytes = 256 * SB;   // one operand, one stage
+  static constexpr int kPieces = SB / 16;          // 16-byte pieces per row
+  static constexpr int kRowsPerLoad = 1024 / SB;   // rows one wave-wide load fills
+  static constexpr int kLoadsPerOperand = SB / 16; // per wave and stage
+  static constexpr int kKSteps = SB / 32;          // 16-element (bf16) MFMA steps
+  __device__ static int swz(int r) {
+    if constexpr (SB == 64)
+      return ((r >> 1) ^ (r >> 3)) & 3;
+    else
+      return (r & 7) ^ ((r >> 3) & 1);
+  }
+};
 
-template <int GT, int EPI, bool GATHER>
+template <int GT, int EPI, bool GATHER, int SB>
 __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
+  using S = Stage<SB>;
+  constexpr int NS = S::kStages;
   constexpr int ES = (GT == GEMM_F32) ? 4 : 2;
   constexpr int FB = 4, TB = 4;  // 32-blocks per wave along f and tokens
+  constexpr int kTS = S::kOperandBytes;
   // One LDS object per stage (A then B): the compiler tracks the direct-to-LDS
   // writes of each object separately, so reading stage k does not make it
   // wait for the loads still in flight into the other stages.  The epilogue
-  // reuses st0.
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kTileStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kTileStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[2 * kTileStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[2 * kTileStage];
-  uint8_t* const sA0 = st0;
-  uint8_t* const sA1 = st1;
-  uint8_t* const sA2 = st2;
-  uint8_t* const sA3 = st3;
-  uint8_t* const sB0 = st0 + kTileStage;
-  uint8_t* const sB1 = st1 + kTileStage;
-  uint8_t* const sB2 = st2 + kTileStage;
-  uint8_t* const sB3 = st3 + kTileStage;
-  __shared__ int32_t sIdx[GATHER ? kBT * kGatherMaxJ : 1];
+  // reuses them.
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kTS];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kTS];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[NS > 2 ? 2 * kTS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[NS > 2 ? 2 * kTS : 16];
+  // row indices of the tile (fused gather), later the gate reduction buffer
+  __shared__ __attribute__((aligned(16))) int32_t sIdx[GATHER ? kBT * kGatherMaxJ : kRedFloats];
+  int32_t* const sIdxOrRed = sIdx;
   __shared__ const uint8_t* sTab[GATHER ? kGatherMaxJ : 1];
 
   // ---- workgroup id -> (token tile, feature tile), XCD-grouped
@@ -167,30 +191,37 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int wf = wave & 1;
   const int wt = wave >> 1;
   const int64_t row_bytes = (int64_t)g.K * ES;
-  const int nk = (int)(row_bytes / kStageBytes);
+  const int nk = (int)(row_bytes / SB);
 
+  static_assert(kBT == kNT, "one thread per token of the tile");
   if constexpr (GATHER) {
+    // thread r stages the J row indices of token m0 + r
     const int J = g.J;
-    for (int i = tid; i < kBT * J; i += kNT) {
-      const int r = i / J, j = i - r * J;
-      int64_t m = m0 + r;
-      m = m < g.M ? m : g.M - 1;
-      sIdx[r * kGatherMaxJ + j] = g.idx[m * J + j];
+    int64_t m = m0 + tid;
+    m = m < g.M ? m : g.M - 1;
+    const int32_t* src = g.idx + m * J;
+    if ((J & 3) == 0) {
+      for (int j = 0; j < J; j += 4)
+        *reinterpret_cast<u32x4*>(sIdx + tid * kGatherMaxJ + j) = *reinterpret_cast<const u32x4*>(src + j);
+    } else {
+      for (int j = 0; j < J; ++j) sIdx[tid * kGatherMaxJ + j] = src[j];
     }
     if (tid < J) sTab[tid] = g.tables[tid];
     __syncthreads();
   }
 
-  // ---- per-lane load descriptors: piece i of this wave covers rows
-  //      ch*16 + lane/4 (ch = wave + 4i), physical 16-byte slot lane&3
-  const uint8_t* srcA[4];
-  const uint8_t* srcB[4];
-  int gj[4], gw[4], grow[4];  // GATHER: table, element offset and local row of the piece at stage 0
+  // ---- per-lane load descriptors: wave-wide load i of this wave fills rows
+  //      ch*kRowsPerLoad .. (ch = wave + 4i); lane -> row ch*kRowsPerLoad +
+  //      lane/kPieces, physical 16-byte slot lane % kPieces
+  constexpr int NL = S::kLoadsPerOperand;
+  const uint8_t* srcA[NL];
+  const uint8_t* srcB[NL];
+  int gj[NL], gw[NL], grow[NL];  // GATHER: table, element offset and local row of the piece at stage 0
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NL; ++i) {
     const int ch = wave + 4 * i;
-    const int row = ch * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz(row);
+    const int row = ch * S::kRowsPerLoad + lane / S::kPieces;
+    const int c = (lane % S::kPieces) ^ S::swz(row);
     srcA[i] = g.A + (int64_t)(f0 + row) * row_bytes + c * 16;
     int64_t m = m0 + row;
     m = m < g.M ? m : g.M - 1;
@@ -205,27 +236,28 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       gj[i] = gw[i] = grow[i] = 0;
     }
   }
-  constexpr int kStageElems = kStageBytes / ES;
+  constexpr int kStageElems = SB / ES;
   const int64_t dbytes = (int64_t)g.D * ES;
 
   // GATHER: (gj, gw) = table and element of piece i at the next stage to
   // issue, (nrow, nbase) = its row index and table base, read from LDS one
   // stage ahead so the loads never wait on those LDS reads.  issue() must be
   // called for kt = 0, 1, 2, ... in order.
-  int32_t nrow[4];
-  const uint8_t* nbase[4];
+  int32_t nrow[NL];
+  const uint8_t* nbase[NL];
   if constexpr (GATHER) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NL; ++i) {
       nrow[i] = sIdx[grow[i] * kGatherMaxJ + gj[i]];
       nbase[i] = sTab[gj[i]];
     }
   }
-  auto issue = [&](int kt, uint8_t* sa, uint8_t* sb) __attribute__((always_inline)) {
+  // issue loads i0 .. i0+cnt-1 of stage kt (all of a stage = issue(kt, .., 0, NL))
+  auto issue = [&](int kt, uint8_t* sa, uint8_t* sb, int i0, int cnt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = i0; i < i0 + cnt; ++i) {
       const int ch = wave + 4 * i;
-      load_lds16(srcA[i] + (int64_t)kt * kStageBytes, sa + ch * 1024);
+      load_lds16(srcA[i] + (int64_t)kt * SB, sa + ch * 1024);
       if constexpr (GATHER) {
         load_lds16(nbase[i] + (int64_t)nrow[i] * dbytes + (int64_t)gw[i] * ES, sb + ch * 1024);
         // advance to the next stage: D >= kStageElems, so at most one table boundary
@@ -237,7 +269,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         nrow[i] = sIdx[grow[i] * kGatherMaxJ + jn];
         nbase[i] = sTab[jn];
       } else {
-        load_lds16(srcB[i] + (int64_t)kt * kStageBytes, sb + ch * 1024);
+        load_lds16(srcB[i] + (int64_t)kt * SB, sb + ch * 1024);
       }
     }
   };
@@ -250,166 +282,338 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
 
   const int l32 = lane & 31;
   const int lhalf = lane >> 5;
-  const int swl = swz(l32);  // fragment rows are blk*32 + l32: one swizzle for every blk
+  const int swl = S::swz(l32);  // fragment rows are blk*32 + l32; the swizzle reads bits 0..4 only
 
   auto frag = [&](const uint8_t* sa, const uint8_t* sb, int ss, u32x4* af, u32x4* bf)
                   __attribute__((always_inline)) {
     const int phys = ((ss * 2 + lhalf) ^ swl) * 16;
 #pragma unroll
     for (int a = 0; a < FB; ++a)
-      af[a] = *reinterpret_cast<const u32x4*>(sa + ((wf * FB + a) * 32 + l32) * kStageBytes + phys);
+      af[a] = *reinterpret_cast<const u32x4*>(sa + ((wf * FB + a) * 32 + l32) * SB + phys);
 #pragma unroll
     for (int b = 0; b < TB; ++b)
-      bf[b] = *reinterpret_cast<const u32x4*>(sb + ((wt * TB + b) * 32 + l32) * kStageBytes + phys);
+      bf[b] = *reinterpret_cast<const u32x4*>(sb + ((wt * TB + b) * 32 + l32) * SB + phys);
   };
-  // two 16-element K steps per stage; the fragments of the second are read
-  // from LDS while the 16 MFMAs of the first run
-  auto compute = [&](const uint8_t* sa, const uint8_t* sb) __attribute__((always_inline)) {
-    u32x4 af0[FB], bf0[TB], af1[FB], bf1[TB];
-    frag(sa, sb, 0, af0, bf0);
-    frag(sa, sb, 1, af1, bf1);
+  // kKSteps 16-element K steps per stage; the fragments of step s+1 are read
+  // from LDS while the 16 MFMAs of step s run.  The loads of a later stage
+  // (nxt >= 0) go out in one burst before the first step, except for the
+  // row-gather loads, which are spread over the steps (each one needs its own
+  // address arithmetic, which then overlaps the MFMAs).
+  auto compute = [&](const uint8_t* sa, const uint8_t* sb, int nxt, uint8_t* na, uint8_t* nb)
+                     __attribute__((always_inline)) {
+    constexpr int KS = S::kKSteps;
+    // spread only the row-gather loads: the dense ones measured no faster spread
+    constexpr int PER = GATHER ? (NL + KS - 1) / KS : NL;  // loads issued per step
+    constexpr int MPER = GT == GEMM_F32 ? 4 : 1;  // MFMA instructions per fragment pair
+    u32x4 af[2][FB], bf[2][TB];
+    if (!GATHER && nxt >= 0) issue(nxt, na, nb, 0, NL);
+    frag(sa, sb, 0, af[0], bf[0]);
 #pragma unroll
-    for (int a = 0; a < FB; ++a)
+    for (int ss = 0; ss < KS; ++ss) {
+      if (ss + 1 < KS) frag(sa, sb, ss + 1, af[(ss + 1) & 1], bf[(ss + 1) & 1]);
 #pragma unroll
-      for (int b = 0; b < TB; ++b) Mma<GT>::run(af0[a], bf0[b], acc[a][b]);
+      for (int a = 0; a < FB; ++a)
 #pragma unroll
-    for (int a = 0; a < FB; ++a)
+        for (int b = 0; b < TB; ++b) Mma<GT>::run(af[ss & 1][a], bf[ss & 1][b], acc[a][b]);
+      if (ss + 1 < KS) {
 #pragma unroll
-      for (int b = 0; b < TB; ++b) Mma<GT>::run(af1[a], bf1[b], acc[a][b]);
-    // schedule: the 8 reads of the first K step, then its 16 MFMAs with the 8
-    // reads of the second step slotted in between, then the second 16 MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * MPER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 16 * MPER, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (GATHER && nxt >= 0 && ss * PER < NL) issue(nxt, na, nb, ss * PER, (ss + 1) * PER <= NL ? PER : NL - ss * PER);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16 * (GT == GEMM_F32 ? 4 : 1), 0);
   };
 
-  // ---- 4-stage ring: stage k lives in buffer k % 4; loads run 3 stages ahead.
-  // Each wave issues 8 loads per stage, so "stage k landed" is vmcnt <= 8 * (stages after k).
-  if (0 < nk) issue(0, sA0, sB0);
-  if (1 < nk) issue(1, sA1, sB1);
-  if (2 < nk) issue(2, sA2, sB2);
-#define ENGRAM_STEP(k, SA, SB, SAN, SBN)        \
-  {                                             \
-    const int left_ = nk - 1 - (k);             \
-    if (left_ >= 2)                             \
-      ENGRAM_WAIT_VM(16);                       \
-    else if (left_ == 1)                        \
-      ENGRAM_WAIT_VM(8);                        \
-    else                                        \
-      ENGRAM_WAIT_VM(0);                        \
-    ENGRAM_BARRIER();                           \
-    if ((k) + 3 < nk) issue((k) + 3, SAN, SBN); \
-    compute(SA, SB);                            \
+  // ---- ring: stage k lives in buffer k % NS; loads run NS-1 stages ahead.
+  // Each wave issues 2*NL loads per stage, so "stage k landed" is
+  // vmcnt <= 2*NL * (stages issued after k).
+  uint8_t* const sA0 = st0;
+  uint8_t* const sB0 = st0 + kTS;
+  uint8_t* const sA1 = st1;
+  uint8_t* const sB1 = st1 + kTS;
+  if constexpr (NS == 4) {
+    uint8_t* const sA2 = st2;
+    uint8_t* const sB2 = st2 + kTS;
+    uint8_t* const sA3 = st3;
+    uint8_t* const sB3 = st3 + kTS;
+    if (0 < nk) issue(0, sA0, sB0, 0, NL);
+    if (1 < nk) issue(1, sA1, sB1, 0, NL);
+    if (2 < nk) issue(2, sA2, sB2, 0, NL);
+#define ENGRAM_STEP(k, SA, SB_, SAN, SBN)         \
+  {                                               \
+    const int left_ = nk - 1 - (k);               \
+    if (left_ >= 2)                               \
+      ENGRAM_WAIT_VM(4 * NL);                     \
+    else if (left_ == 1)                          \
+      ENGRAM_WAIT_VM(2 * NL);                     \
+    else                                          \
+      ENGRAM_WAIT_VM(0);                          \
+    ENGRAM_BARRIER();                             \
+    compute(SA, SB_, (k) + 3 < nk ? (k) + 3 : -1, SAN, SBN); \
   }
-  for (int kt = 0; kt < nk; kt += 4) {
-    ENGRAM_STEP(kt, sA0, sB0, sA3, sB3);
-    ENGRAM_STEP(kt + 1, sA1, sB1, sA0, sB0);
-    ENGRAM_STEP(kt + 2, sA2, sB2, sA1, sB1);
-    ENGRAM_STEP(kt + 3, sA3, sB3, sA2, sB2);
-  }
+    for (int kt = 0; kt < nk; kt += 4) {
+      ENGRAM_STEP(kt, sA0, sB0, sA3, sB3);
+      ENGRAM_STEP(kt + 1, sA1, sB1, sA0, sB0);
+      ENGRAM_STEP(kt + 2, sA2, sB2, sA1, sB1);
+      ENGRAM_STEP(kt + 3, sA3, sB3, sA2, sB2);
+    }
 #undef ENGRAM_STEP
+  } else {
+    if (0 < nk) issue(0, sA0, sB0, 0, NL);
+#define ENGRAM_STEP(k, SA, SB_, SAN, SBN)         \
+  {                                               \
+    ENGRAM_WAIT_VM(0);                            \
+    ENGRAM_BARRIER();                             \
+    compute(SA, SB_, (k) + 1 < nk ? (k) + 1 : -1, SAN, SBN); \
+  }
+    for (int kt = 0; kt < nk; kt += 2) {
+      ENGRAM_STEP(kt, sA0, sB0, sA1, sB1);
+      ENGRAM_STEP(kt + 1, sA1, sB1, sA0, sB0);
+    }
+#undef ENGRAM_STEP
+  }
   __syncthreads();  // stage buffers are free from here on
 
   // ---- epilogues.  acc[a][b][q*4+r] holds C^T[f][m] with
   //      f = f0 + (wf*FB + a)*32 + q*8 + lhalf*4 + r,  m = m0 + (wt*TB + b)*32 + l32
-  if constexpr (EPI == EPI_KV) {
-    // Through LDS, 32 tokens x 256 features (fp32, 1 KB per token row, the
-    // 16-byte pieces XOR-swizzled by the row) at a time: the two waves owning
-    // those tokens write their accumulators, then 32 lanes per token read 8
-    // features each, so h is read and k / v are written as whole rows.
-    const int io = g.io_dtype;
+  if constexpr (EPI == EPI_KV && GT == GEMM_BF16) {
+    // bf16: the whole 256-token x 256-feature tile goes through LDS as bf16,
+    // token rows of 512 bytes (64 rows per stage buffer), 16-byte pieces
+    // XOR-swizzled by (token & 31).  h is brought in and v goes out as whole
+    // rows (a wave moves two 512-byte rows per instruction).
     const int d = g.d;
-    const bool key_tile = f0 < d;
-    const int tg = tid >> 5;         // token of this thread within a round of 8
-    const int c0 = (tid & 31) * 2;   // its two 16-byte pieces (8 features)
-    uint8_t* const stage = st0;
-    floatx4 g4[2] = {floatx4{1.f, 1.f, 1.f, 1.f}, floatx4{1.f, 1.f, 1.f, 1.f}};
-    if (key_tile) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        if (g.gamma_q) g4[h2] *= *reinterpret_cast<const floatx4*>(g.gamma_q + f0 + c0 * 4 + 4 * h2);
-        if (g.gamma_k) g4[h2] *= *reinterpret_cast<const floatx4*>(g.gamma_k + f0 + c0 * 4 + 4 * h2);
-      }
-    }
-    // h of this thread's 4 tokens in pass p (8 features each), loaded one pass ahead
-    auto load_h = [&](int p, floatx4* hb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int round = 0; round < 4; ++round) {
-        int64_t m = m0 + p * 32 + round * 8 + tg;
-        m = m < g.M ? m : g.M - 1;
-        hb[2 * round] = load4(g.h, m * d + f0 + c0 * 4, io);
-        hb[2 * round + 1] = load4(g.h, m * d + f0 + c0 * 4 + 4, io);
+    uint8_t* const bufs0 = st0;
+    // token rows of 512 bytes; each stage buffer (2*kTS bytes) holds SB of them
+    auto trow = [&](int t) __attribute__((always_inline)) -> uint8_t* {
+      if constexpr (NS == 4) {
+        const int k = t >> 6;
+        uint8_t* base = k == 0 ? bufs0 : (k == 1 ? st1 : (k == 2 ? st2 : st3));
+        return base + (t & 63) * 512;
+      } else {
+        return (t < 128 ? bufs0 : st1) + (t & 127) * 512;
       }
     };
-    floatx4 hcur[8], hnext[8];
-    if (key_tile) load_h(0, hnext);
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {  // tokens p*32 .. p*32+31 of the tile
-      if (key_tile) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hcur[i] = hnext[i];
-        if (p + 1 < 8) load_h(p + 1, hnext);
+    if (f0 < d) {
+      // h tile -> LDS: instruction i of wave w fills rows t0, t0+1 (t0 = 2(32w+i))
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const int t0 = (wave * 32 + i) * 2;
+        const int t = t0 + (lane >> 5);
+        const int c16 = (lane & 31) ^ (t & 31);  // logical piece landing at slot lane&31
+        int64_t m = m0 + t;
+        m = m < g.M ? m : g.M - 1;
+        load_lds16(g.h + ((m * d + f0) + c16 * 8) * 2, trow(t0));
       }
-      if (wt == (p >> 2)) {
-        const int b = p & 3;
+      ENGRAM_WAIT_VM(0);
+      __syncthreads();
+      float* red = reinterpret_cast<float*>(sIdxOrRed);  // [2 wf][2 wt][TB][32][3]
 #pragma unroll
-        for (int a = 0; a < FB; ++a)
+      for (int b = 0; b < TB; ++b) {
+        const int t = (wt * TB + b) * 32 + l32;
+        const int64_t m = m0 + t;
+        const bool valid = m < g.M;
+        const uint8_t* hrow = trow(t);
+        float skk = 0.f, shk = 0.f, shh = 0.f;
+#pragma unroll
+        for (int a = 0; a < FB; ++a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int piece = ((wf * FB + a) * 32 + q * 8 + lhalf * 4) >> 2;
-            *reinterpret_cast<floatx4*>(stage + l32 * 1024 + ((piece ^ (l32 & 15)) << 4)) =
-                floatx4{acc[a][b][q * 4], acc[a][b][q * 4 + 1], acc[a][b][q * 4 + 2],
-                        acc[a][b][q * 4 + 3]};
-          }
-      }
-      __syncthreads();
+            const int c16 = (wf * FB + a) * 4 + q;
+            const int f = f0 + c16 * 8 + lhalf * 4;
+            const u32x2 hr =
+                *reinterpret_cast<const u32x2*>(hrow + ((c16 ^ (t & 31)) << 4) + lhalf * 8);
+            const floatx4 hx = floatx4{__uint_as_float(hr[0] << 16), __uint_as_float(hr[0] & 0xFFFF0000u),
+                                       __uint_as_float(hr[1] << 16), __uint_as_float(hr[1] & 0xFFFF0000u)};
+            floatx4 gg = floatx4{1.f, 1.f, 1.f, 1.f};
+            if (g.gamma_q) gg *= *reinterpret_cast<const floatx4*>(g.gamma_q + f);
+            if (g.gamma_k) gg *= *reinterpret_cast<const floatx4*>(g.gamma_k + f);
+            float kv[4];
 #pragma unroll
-      for (int round = 0; round < 4; ++round) {
-        const int tl = round * 8 + tg;
-        const int64_t m = m0 + p * 32 + tl;
-        const uint8_t* row = stage + tl * 1024;
-        const floatx4 x0 = *reinterpret_cast<const floatx4*>(row + ((c0 ^ (tl & 15)) << 4));
-        const floatx4 x1 = *reinterpret_cast<const floatx4*>(row + (((c0 + 1) ^ (tl & 15)) << 4));
-        const bool valid = m < g.M;
-        const int f = c0 * 4;  // feature offset inside the tile
-        if (key_tile) {
-          const floatx4 h0 = hcur[2 * round];
-          const floatx4 h1 = hcur[2 * round + 1];
-          float skk = 0.f, shk = 0.f, shh = 0.f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            skk += x0[r] * x0[r] + x1[r] * x1[r];
-            shk += g4[0][r] * h0[r] * x0[r] + g4[1][r] * h1[r] * x1[r];
-            shh += h0[r] * h0[r] + h1[r] * h1[r];
-          }
-#pragma unroll
-          for (int o = 16; o > 0; o >>= 1) {
-            skk += __shfl_xor(skk, o);
-            shk += __shfl_xor(shk, o);
-            shh += __shfl_xor(shh, o);
-          }
-          if (valid) {
-            if ((tid & 31) == 0) {
-              float* out = g.partials + (m * (d / kBF) + tf) * 3;
-              out[0] = skk;
-              out[1] = shk;
-              out[2] = shh;
+            for (int r = 0; r < 4; ++r) {
+              kv[r] = acc_read(acc[a][b][q * 4 + r]);
+              skk += kv[r] * kv[r];
+              shk += gg[r] * hx[r] * kv[r];
+              shh += hx[r] * hx[r];
             }
-            if (g.k_out) {
-              store4(g.k_out, m * d + f0 + f, io, x0[0], x0[1], x0[2], x0[3]);
-              store4(g.k_out, m * d + f0 + f + 4, io, x1[0], x1[1], x1[2], x1[3]);
-            }
+            if (g.k_out && valid) store4(g.k_out, m * d + f, ENGRAM_BF16, kv[0], kv[1], kv[2], kv[3]);
           }
-        } else if (valid) {
-          store4(g.v_out, m * d + (f0 - d) + f, io, x0[0], x0[1], x0[2], x0[3]);
-          store4(g.v_out, m * d + (f0 - d) + f + 4, io, x1[0], x1[1], x1[2], x1[3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        skk += __shfl_xor(skk, 32);
+        shk += __shfl_xor(shk, 32);
+        shh += __shfl_xor(shh, 32);
+        if (lhalf == 0) {
+          float* p = red + ((((wf * 2) + wt) * TB + b) * 32 + l32) * 3;
+          p[0] = skk;
+          p[1] = shk;
+          p[2] = shh;
         }
       }
       __syncthreads();
+      {  // 2 wt x TB x 32 = 256 tokens, one per thread; add the two feature halves
+        const int wt2 = tid >> 7, b = (tid >> 5) & 3, l = tid & 31;
+        const int64_t m = m0 + (wt2 * TB + b) * 32 + l;
+        if (m < g.M) {
+          const float* p0 = red + (((0 + wt2) * TB + b) * 32 + l) * 3;
+          const float* p1 = red + (((2 + wt2) * TB + b) * 32 + l) * 3;
+          float* out = g.partials + (m * (d / kBF) + tf) * 3;
+          out[0] = p0[0] + p1[0];
+          out[1] = p0[1] + p1[1];
+          out[2] = p0[2] + p1[2];
+        }
+      }
+    } else {
+      // value tile: accumulators -> bf16 rows in LDS -> whole rows to v
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        const int t = (wt * TB + b) * 32 + l32;
+        uint8_t* row = trow(t);
+#pragma unroll
+        for (int a = 0; a < FB; ++a) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c16 = (wf * FB + a) * 4 + q;
+            u32x2 u;
+            u[0] = (uint32_t)f32_to_bf16_bits(acc_read(acc[a][b][q * 4])) |
+                   ((uint32_t)f32_to_bf16_bits(acc_read(acc[a][b][q * 4 + 1])) << 16);
+            u[1] = (uint32_t)f32_to_bf16_bits(acc_read(acc[a][b][q * 4 + 2])) |
+                   ((uint32_t)f32_to_bf16_bits(acc_read(acc[a][b][q * 4 + 3])) << 16);
+            *reinterpret_cast<u32x2*>(row + ((c16 ^ (t & 31)) << 4) + lhalf * 8) = u;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();
+      // 256 rows x 32 pieces of 16 bytes; a wave writes two rows per instruction
+#pragma unroll 4
+      for (int i = 0; i < 32; ++i) {
+        const int t = (wave * 32 + i) * 2 + (lane >> 5);
+        const int c16 = lane & 31;
+        const int64_t m = m0 + t;
+        if (m < g.M) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(trow(t) + ((c16 ^ (t & 31)) << 4));
+          *reinterpret_cast<u32x4*>(g.v_out + (m * d + (f0 - d) + c16 * 8) * 2) = x;
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_KV) {
+    // fp32 (small shapes): straight from the accumulators
+    const int io = g.io_dtype;
+    const int d = g.d;
+    if (f0 < d) {
+      // Key tile: per-token partial sums of the gate straight from the
+      // accumulators (each lane owns one token and 64 of this wave's 128
+      // features), h of the next token block loaded while this one is summed.
+      float* red = reinterpret_cast<float*>(st0);  // [2 wf][2 wt][TB][32][3]
+      // raw h bits (2 words per 4 bf16, 4 per 4 fp32), widened at use
+      constexpr int HW = (GT == GEMM_BF16) ? 2 : 4;
+      typedef uint32_t hraw_t __attribute__((ext_vector_type(HW)));
+      hraw_t hb[2][FB * 4];
+      auto load_hb = [&](int b, hraw_t* dst) __attribute__((always_inline)) {
+        int64_t m = m0 + (wt * TB + b) * 32 + l32;
+        m = m < g.M ? m : g.M - 1;
+#pragma unroll
+        for (int a = 0; a < FB; ++a)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            // element (m, f) of h sits at byte (m*d + f) * element size, and the
+            // element size is HW bytes (4 elements = HW words)
+            dst[a * 4 + q] = *reinterpret_cast<const hraw_t*>(
+                g.h + (m * d + f0 + (wf * FB + a) * 32 + q * 8 + lhalf * 4) * (int64_t)HW);
+      };
+      // bf16 h is prefetched one token block ahead; fp32 h (twice the
+      // registers) is loaded per block
+      constexpr bool kPrefetchH = GT == GEMM_BF16;
+      if (kPrefetchH) load_hb(0, hb[0]);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        if (kPrefetchH) {
+          if (b + 1 < TB) load_hb(b + 1, hb[(b + 1) & 1]);
+        } else {
+          load_hb(b, hb[b & 1]);
+        }
+        const int64_t m = m0 + (wt * TB + b) * 32 + l32;
+        const bool valid = m < g.M;
+        float skk = 0.f, shk = 0.f, shh = 0.f;
+#pragma unroll
+        for (int a = 0; a < FB; ++a) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int f = f0 + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
+            floatx4 gg = floatx4{1.f, 1.f, 1.f, 1.f};
+            if (g.gamma_q) gg *= *reinterpret_cast<const floatx4*>(g.gamma_q + f);
+            if (g.gamma_k) gg *= *reinterpret_cast<const floatx4*>(g.gamma_k + f);
+            const hraw_t hr = hb[b & 1][a * 4 + q];
+            floatx4 hx;
+            if constexpr (GT == GEMM_BF16) {
+              hx = floatx4{__uint_as_float(hr[0] << 16), __uint_as_float(hr[0] & 0xFFFF0000u),
+                           __uint_as_float(hr[1] << 16), __uint_as_float(hr[1] & 0xFFFF0000u)};
+            } else {
+              hx = floatx4{__uint_as_float(hr[0]), __uint_as_float(hr[1]), __uint_as_float(hr[2]),
+                           __uint_as_float(hr[3])};
+            }
+            float kv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              kv[r] = acc_read(acc[a][b][q * 4 + r]);
+              skk += kv[r] * kv[r];
+              shk += gg[r] * hx[r] * kv[r];
+              shh += hx[r] * hx[r];
+            }
+            if (g.k_out && valid) store4(g.k_out, m * d + f, io, kv[0], kv[1], kv[2], kv[3]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        skk += __shfl_xor(skk, 32);
+        shk += __shfl_xor(shk, 32);
+        shh += __shfl_xor(shh, 32);
+        if (lhalf == 0) {
+          float* p = red + ((((wf * 2) + wt) * TB + b) * 32 + l32) * 3;
+          p[0] = skk;
+          p[1] = shk;
+          p[2] = shh;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      {  // 2 wt x TB x 32 = 256 tokens, one per thread; add the two feature halves
+        const int wt2 = tid >> 7, b = (tid >> 5) & 3, l = tid & 31;
+        const int64_t m = m0 + (wt2 * TB + b) * 32 + l;
+        if (m < g.M) {
+          const float* p0 = red + (((0 + wt2) * TB + b) * 32 + l) * 3;
+          const float* p1 = red + (((2 + wt2) * TB + b) * 32 + l) * 3;
+          float* out = g.partials + (m * (d / kBF) + tf) * 3;
+          out[0] = p0[0] + p1[0];
+          out[1] = p0[1] + p1[1];
+          out[2] = p0[2] + p1[2];
+        }
+      }
+    } else {
+      // Value tile: stored straight from the accumulators (4 features per
+      // lane per store; the pieces of a token row meet in L2)
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        const int64_t m = m0 + (wt * TB + b) * 32 + l32;
+        if (m < g.M) {
+#pragma unroll
+          for (int a = 0; a < FB; ++a) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int f = f0 - d + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
+              store4(g.v_out, m * d + f, io, acc_read(acc[a][b][q * 4]),
+                     acc_read(acc[a][b][q * 4 + 1]), acc_read(acc[a][b][q * 4 + 2]),
+                     acc_read(acc[a][b][q * 4 + 3]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
     }
   } else {
 #pragma unroll
@@ -437,16 +641,20 @@ static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles_m_x = (tiles_m + 7) / 8;
   const int64_t groups = (tiles_m_x + g.group_m - 1) / g.group_m;
   const int64_t blocks = 8 * groups * g.group_m * tiles_f;
-  hipLaunchKernelGGL((gemm_kernel<GT, EPI, GATHER>), dim3((unsigned)blocks), dim3(kNT), 0, s, g);
+  if (g.stage_bytes == 128)
+    hipLaunchKernelGGL((gemm_kernel<GT, EPI, GATHER, 128>), dim3((unsigned)blocks), dim3(kNT), 0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_kernel<GT, EPI, GATHER, 64>), dim3((unsigned)blocks), dim3(kNT), 0, s, g);
   return hipGetLastError();
 }
 
 bool gemm_supported(GemmType type, const GemmArgs& g, bool gather) {
   const int es = type == GEMM_F32 ? 4 : 2;
   if (g.F % kBF != 0 || g.group_m < 1) return false;
-  if (((int64_t)g.K * es) % (kStageBytes * kStages) != 0) return false;
+  if (g.stage_bytes != 64 && g.stage_bytes != 128) return false;
+  if (((int64_t)g.K * es) % 256 != 0) return false;  // whole ring turns for either stage shape
   if (gather) {
-    if (g.J < 1 || g.J > kGatherMaxJ || g.D * es < kStageBytes) return false;
+    if (g.J < 1 || g.J > kGatherMaxJ || g.D * es < g.stage_bytes) return false;
     if (((int64_t)g.D * es) % 16 != 0) return false;
     if ((int64_t)g.J * g.D != g.K) return false;
   }

@@ -69,6 +69,15 @@ enum { ENGRAM_F32 = 0, ENGRAM_BF16 = 1 };
 #define ENGRAM_MAX_ORDERS 4
 #define ENGRAM_MAX_TABLES 32
 
+/* engram_config.flags */
+enum {
+  /* Forward: read table rows inside the projection's operand loads instead of
+   * gathering e into the workspace first (saves e's write and re-read, but the
+   * row-indexed loads cost the projection more than the gather costs).  Ignored
+   * when saved->e is requested or the shape is outside the fused loads. */
+  ENGRAM_FLAG_FUSED_GATHER = 1u
+};
+
 /* Shapes and addressing constants.  Host struct, read during the call only. */
 typedef struct {
   int32_t vocab;          /* raw ids lie in [0, vocab) */
@@ -76,7 +85,7 @@ typedef struct {
   int32_t num_orders;     /* 1..ENGRAM_MAX_ORDERS */
   int32_t orders[ENGRAM_MAX_ORDERS]; /* N-gram orders, strictly ascending, each 1..4 */
   int32_t heads;          /* K hash heads per order; J = num_orders*heads <= 32 */
-  int32_t dim;            /* D columns per table row; D*sizeof(dtype) % 16 == 0, J*D % 128 == 0 */
+  int32_t dim;            /* D columns per table row; D*sizeof(dtype) % 16 == 0, J*D % 256 == 0 */
   int32_t hidden;         /* d, width of h_t, k_t, v_t, Y_t; d % 256 == 0 */
   int32_t conv_kernel;    /* taps of the causal depthwise conv, 1..8 */
   int32_t dtype;          /* ENGRAM_F32 or ENGRAM_BF16 */
@@ -84,6 +93,7 @@ typedef struct {
   int32_t pad_id;         /* canonical id used for positions before t = 0 */
   const int64_t* table_rows;   /* host [J]: M_j, 1 <= M_j < 2^31 (prime by design) */
   const uint64_t* multipliers; /* host [J][max order]: m_{j,i} multiplies c_{t-i} */
+  uint32_t flags;              /* ENGRAM_FLAG_* bits, 0 for the defaults */
 } engram_config;
 
 /* Learned parameters (device pointers). */

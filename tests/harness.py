@@ -30,7 +30,7 @@ def to_host_f64(t) -> np.ndarray:
 class DeviceProblem:
     """One workload on the GPU: config, parameters, tokens and hidden states."""
 
-    def __init__(self, inp: synth.Inputs, device="cuda", upload_tables=True, tokens=None):
+    def __init__(self, inp: synth.Inputs, device="cuda", upload_tables=True, tokens=None, flags=0):
         import hashed_gram_embedding_canon_amd as eg
         torch = torch_mod()
         self.eg = eg
@@ -42,7 +42,7 @@ class DeviceProblem:
                              heads=wl.heads, dim=wl.dim, hidden=wl.hidden,
                              table_rows=inp.table_rows, multipliers=inp.multipliers,
                              dtype=self.dtype_code, conv_kernel=wl.taps, rms_eps=wl.rms_eps,
-                             pad_id=wl.pad_id)
+                             pad_id=wl.pad_id, flags=flags)
         self.tokens_host = np.ascontiguousarray(inp.tokens if tokens is None else tokens, dtype=np.int32)
         self.B, self.T = self.tokens_host.shape
         self.tokens = to_dev(self.tokens_host, device)

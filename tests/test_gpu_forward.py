@@ -28,12 +28,13 @@ def torch():
     return torch
 
 
-def _run_full(torch, wl, tokens=None, hidden=None, saved=("idx", "stats", "e")):
-    """Forward with the requested saved tensors.  Asking for e makes the
-    library gather e into memory and run the projection on it; without e the
-    projection reads the table rows itself (fused gather)."""
+def _run_full(torch, wl, tokens=None, hidden=None, saved=("idx", "stats", "e"), flags=0):
+    """Forward with the requested saved tensors.  By default the library
+    gathers e (into saved e or its workspace) and runs the projection on it;
+    with ENGRAM_FLAG_FUSED_GATHER and no saved e the projection reads the table
+    rows itself."""
     inp = synth.Inputs(wl)
-    dp = H.DeviceProblem(inp, tokens=tokens)
+    dp = H.DeviceProblem(inp, tokens=tokens, flags=flags)
     if hidden is not None:
         dp.hidden = H.to_dev(hidden)
     bufs = dp.alloc_saved(saved)
@@ -85,12 +86,16 @@ def test_deterministic_and_hash_entry_point(torch):
                                              ("tiny", "f32", 1, 512), ("small", "bf16", 2, 1024)])
 def test_fused_gather_matches_materialized(torch, oracle_lib, name, dtype, B, T):
     """The projection fed straight from the tables gives bit-identical Y to the
-    one fed from the gathered e, and matches the oracle."""
+    one fed from the gathered e (saved or workspace), and matches the oracle."""
+    import hashed_gram_embedding_canon_amd as eg
     wl = dataclasses.replace(synth.get_workload(name), dtype=dtype).with_shape(B, T)
-    inp, dp, bufs, y_mat = _run_full(torch, wl, saved=("idx", "e"))
+    inp, dp, bufs, y_mat = _run_full(torch, wl, saved=("idx", "e"), flags=eg.ENGRAM_FLAG_FUSED_GATHER)
     y_fused = dp.forward(dp.alloc_saved(("idx",)))
+    dp.cfg.c.flags = 0
+    y_ws = dp.forward(dp.alloc_saved(("idx",)))
     torch.cuda.synchronize()
     assert torch.equal(y_fused, y_mat)
+    assert torch.equal(y_ws, y_mat)
     if name == "tiny":
         ref = H.oracle_problem(inp).forward(want=("y",))["y"]
         err = H.rel_max_err(H.to_host_f64(y_fused).reshape(-1, wl.hidden), ref)
