@@ -28,6 +28,15 @@ __host__ __device__ inline uint16_t f32_to_bf16_bits(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+// Two floats -> packed bf16 pair (a in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950, the same result as f32_to_bf16_bits for
+// finite inputs.
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 r = __builtin_convertvector(floatx2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
 
 // ------------------------------------------------------- exact x mod prime
 // x mod p for a 64-bit x and 1 <= p < 2^31 without a 64-bit divide.

@@ -42,7 +42,7 @@ __device__ inline void store_vec(uint8_t* base, int64_t elem, const float* v) {
     u32x4 u;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      u[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
+      u[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     *reinterpret_cast<u32x4*>(base + elem * 2) = u;
   } else {
     *reinterpret_cast<floatx4*>(base + elem * 4) = floatx4{v[0], v[1], v[2], v[3]};

@@ -26,6 +26,8 @@
 // v_mfma_f32_32x32x2f32 per 16-byte fragment.  Workgroup ids reach the 8
 // XCDs round-robin; the id -> tile map keeps the f-tiles of a small group of
 // token tiles on one XCD so they share rows and weight slabs in its L2.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace engram {
@@ -74,8 +76,8 @@ __device__ inline floatx4 load4(const uint8_t* base, int64_t i, int io) {
 __device__ inline void store4(uint8_t* base, int64_t i, int io, float a, float b, float c, float d) {
   if (io == ENGRAM_BF16) {
     u32x2 u;
-    u.x = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-    u.y = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
+    u.x = pack_bf16x2(a, b);
+    u.y = pack_bf16x2(c, d);
     *reinterpret_cast<u32x2*>(base + i * 2) = u;
   } else {
     *reinterpret_cast<floatx4*>(base + i * 4) = floatx4{a, b, c, d};
@@ -91,18 +93,37 @@ __device__ inline float acc_read(float x) {
   return r;
 }
 
-// 16-byte direct-to-LDS global load: lane l's 16 bytes land at lds_dst + 16*l
-// (lds_dst is wave-uniform and goes through M0).  Written as asm so that the
-// compiler does not treat every later LDS read as aliasing the write and wait
-// for all loads in flight; the ring below waits with explicit vmcnt counts.
-// The instruction has no destination register, so nothing the compiler
-// allocates can be overwritten while it is in flight.
-__device__ inline void load_lds16(const void* src, void* lds_dst) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst);
+// LDS byte address of a __shared__ object.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Wave-uniform 64-bit value, held in SGPRs.
+__device__ inline const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte direct-to-LDS global loads: lane l's 16 bytes land at LDS address
+// m0v + 16*l (m0v is wave-uniform and goes through M0).  Written as asm so
+// that the compiler does not treat every later LDS read as aliasing the write
+// and wait for all loads in flight; the ring below waits with explicit vmcnt
+// counts.  The instructions have no destination register, so nothing the
+// compiler allocates can be overwritten while they are in flight.
+//   load_lds16:   per-lane 64-bit address
+//   load_lds16_s: wave-uniform 64-bit base (SGPRs) + per-lane 32-bit offset,
+//                 so a stage's loads need no per-lane address arithmetic
+__device__ inline void load_lds16(const void* src, uint32_t m0v) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(m0v)
+               : "memory");
+}
+__device__ inline void load_lds16_s(uint32_t voff, const void* sbase, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0v)
                : "memory");
 }
 
@@ -149,6 +170,13 @@ struct Stage {
   }
 };
 
+#ifndef ENGRAM_GEMM_SPREAD
+#define ENGRAM_GEMM_SPREAD 1
+#endif
+// Spread the next stage's load instructions between MFMA groups (1) or issue
+// them in one burst at the start of a stage (0).
+constexpr bool kSpreadLoads = ENGRAM_GEMM_SPREAD != 0;
+
 template <int GT, int EPI, bool GATHER, int SB>
 __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   using S = Stage<SB>;
@@ -165,7 +193,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t st2[NS > 2 ? 2 * kTS : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[NS > 2 ? 2 * kTS : 16];
   // row indices of the tile (fused gather), later the gate reduction buffer
-  __shared__ __attribute__((aligned(16))) int32_t sIdx[GATHER ? kBT * kGatherMaxJ : kRedFloats];
+  __shared__ __attribute__((aligned(16))) int32_t sIdx[GATHER ? kBT * kGatherMaxJ : kRedFloats + kBF];
   int32_t* const sIdxOrRed = sIdx;
   __shared__ const uint8_t* sTab[GATHER ? kGatherMaxJ : 1];
 
@@ -186,7 +214,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int64_t m0 = tm * kBT;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int wf = wave & 1;
   const int wt = wave >> 1;
@@ -214,28 +242,29 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   //      ch*kRowsPerLoad .. (ch = wave + 4i); lane -> row ch*kRowsPerLoad +
   //      lane/kPieces, physical 16-byte slot lane % kPieces
   constexpr int NL = S::kLoadsPerOperand;
-  const uint8_t* srcA[NL];
-  const uint8_t* srcB[NL];
+  // byte offsets of piece i inside the tile's rows (A: rows f0.., B: rows m0..)
+  uint32_t voffA[NL], voffB[NL];
   int gj[NL], gw[NL], grow[NL];  // GATHER: table, element offset and local row of the piece at stage 0
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int ch = wave + 4 * i;
     const int row = ch * S::kRowsPerLoad + lane / S::kPieces;
     const int c = (lane % S::kPieces) ^ S::swz(row);
-    srcA[i] = g.A + (int64_t)(f0 + row) * row_bytes + c * 16;
+    voffA[i] = (uint32_t)(row * row_bytes + c * 16);
     int64_t m = m0 + row;
     m = m < g.M ? m : g.M - 1;
+    voffB[i] = (uint32_t)((m - m0) * row_bytes + c * 16);
     if constexpr (GATHER) {
       const int e0 = c * 16 / ES;
       gj[i] = e0 / g.D;
       gw[i] = e0 - gj[i] * g.D;
       grow[i] = row;
-      srcB[i] = nullptr;
     } else {
-      srcB[i] = g.B + m * row_bytes + c * 16;
       gj[i] = gw[i] = grow[i] = 0;
     }
   }
+  const uint8_t* const tileA = g.A + (int64_t)f0 * row_bytes;
+  const uint8_t* const tileB = GATHER ? nullptr : g.B + m0 * row_bytes;
   constexpr int kStageElems = SB / ES;
   const int64_t dbytes = (int64_t)g.D * ES;
 
@@ -252,25 +281,39 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       nbase[i] = sTab[gj[i]];
     }
   }
-  // issue loads i0 .. i0+cnt-1 of stage kt (all of a stage = issue(kt, .., 0, NL))
-  auto issue = [&](int kt, uint8_t* sa, uint8_t* sb, int i0, int cnt) __attribute__((always_inline)) {
+  // One load instruction of stage kt: piece i of operand A (op 0) or B (op 1)
+  // into the stage buffer at LDS address la (A) / la + kTS (B).
+  // bA / bB: uniform_ptr(tileA / tileB + kt * SB), the stage's row bases.
+  auto issue_one = [&](const void* bA, const void* bB, uint32_t la, int i, int op)
+                       __attribute__((always_inline)) {
+    const uint32_t m0v = la + (uint32_t)((wave + 4 * i) * 1024);
+    if (op == 0) {
+      load_lds16_s(voffA[i], bA, m0v);
+    } else if constexpr (GATHER) {
+      load_lds16(nbase[i] + (int64_t)nrow[i] * dbytes + (int64_t)gw[i] * ES, m0v + kTS);
+      // advance to the next stage: D >= kStageElems, so at most one table boundary
+      gw[i] += kStageElems;
+      const bool wrap = gw[i] >= g.D;
+      gw[i] = wrap ? gw[i] - g.D : gw[i];
+      gj[i] = wrap ? gj[i] + 1 : gj[i];
+      const int jn = gj[i] < g.J ? gj[i] : g.J - 1;  // past the last stage: any valid entry
+      nrow[i] = sIdx[grow[i] * kGatherMaxJ + jn];
+      nbase[i] = sTab[jn];
+    } else {
+      load_lds16_s(voffB[i], bB, m0v + kTS);
+    }
+  };
+  auto stage_base = [&](const uint8_t* tile, int kt) __attribute__((always_inline)) -> const void* {
+    return GATHER && tile == nullptr ? nullptr : uniform_ptr(tile + (int64_t)kt * SB);
+  };
+  // all 2*NL load instructions of stage kt
+  auto issue = [&](int kt, uint32_t la) __attribute__((always_inline)) {
+    const void* bA = stage_base(tileA, kt);
+    const void* bB = GATHER ? nullptr : stage_base(tileB, kt);
 #pragma unroll
-    for (int i = i0; i < i0 + cnt; ++i) {
-      const int ch = wave + 4 * i;
-      load_lds16(srcA[i] + (int64_t)kt * SB, sa + ch * 1024);
-      if constexpr (GATHER) {
-        load_lds16(nbase[i] + (int64_t)nrow[i] * dbytes + (int64_t)gw[i] * ES, sb + ch * 1024);
-        // advance to the next stage: D >= kStageElems, so at most one table boundary
-        gw[i] += kStageElems;
-        const bool wrap = gw[i] >= g.D;
-        gw[i] = wrap ? gw[i] - g.D : gw[i];
-        gj[i] = wrap ? gj[i] + 1 : gj[i];
-        const int jn = gj[i] < g.J ? gj[i] : g.J - 1;  // past the last stage: any valid entry
-        nrow[i] = sIdx[grow[i] * kGatherMaxJ + jn];
-        nbase[i] = sTab[jn];
-      } else {
-        load_lds16(srcB[i] + (int64_t)kt * SB, sb + ch * 1024);
-      }
+    for (int i = 0; i < NL; ++i) {
+      issue_one(bA, bB, la, i, 0);
+      issue_one(bA, bB, la, i, 1);
     }
   };
 
@@ -284,6 +327,12 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int lhalf = lane >> 5;
   const int swl = S::swz(l32);  // fragment rows are blk*32 + l32; the swizzle reads bits 0..4 only
 
+  auto frag_one = [&](const uint8_t* sa, const uint8_t* sb, int ss, int blk, u32x4& af, u32x4& bf)
+                      __attribute__((always_inline)) {
+    const int phys = ((ss * 2 + lhalf) ^ swl) * 16;
+    af = *reinterpret_cast<const u32x4*>(sa + ((wf * FB + blk) * 32 + l32) * SB + phys);
+    bf = *reinterpret_cast<const u32x4*>(sb + ((wt * TB + blk) * 32 + l32) * SB + phys);
+  };
   auto frag = [&](const uint8_t* sa, const uint8_t* sb, int ss, u32x4* af, u32x4* bf)
                   __attribute__((always_inline)) {
     const int phys = ((ss * 2 + lhalf) ^ swl) * 16;
@@ -294,39 +343,51 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     for (int b = 0; b < TB; ++b)
       bf[b] = *reinterpret_cast<const u32x4*>(sb + ((wt * TB + b) * 32 + l32) * SB + phys);
   };
-  // kKSteps 16-element K steps per stage; the fragments of step s+1 are read
-  // from LDS while the 16 MFMAs of step s run.  The loads of a later stage
-  // (nxt >= 0) go out in one burst before the first step, except for the
-  // row-gather loads, which are spread over the steps (each one needs its own
-  // address arithmetic, which then overlaps the MFMAs).
-  auto compute = [&](const uint8_t* sa, const uint8_t* sb, int nxt, uint8_t* na, uint8_t* nb)
+  // kKSteps 16-element K steps per stage, each FB groups of TB MFMAs (one
+  // feature block against the TB token blocks).  The fragments of step s+1
+  // are read from LDS during step s, and the 2*NL load instructions of a
+  // later stage (nxt >= 0) are spread one per group (or in one burst before
+  // the first step): with one wave per SIMD a wave stalled on a full
+  // vector-memory queue issues no MFMA, so the loads go out in small pieces
+  // between MFMA groups.
+  auto compute = [&](const uint8_t* sa, const uint8_t* sb, int nxt, uint32_t nla)
                      __attribute__((always_inline)) {
     constexpr int KS = S::kKSteps;
-    // spread only the row-gather loads: the dense ones measured no faster spread
-    constexpr int PER = GATHER ? (NL + KS - 1) / KS : NL;  // loads issued per step
+    constexpr int NG = KS * FB;           // MFMA groups per stage
+    constexpr int NI = 2 * NL;            // load instructions per stage
     constexpr int MPER = GT == GEMM_F32 ? 4 : 1;  // MFMA instructions per fragment pair
+    static_assert(FB == TB, "one A and one B fragment of the next step per group");
     u32x4 af[2][FB], bf[2][TB];
-    if (!GATHER && nxt >= 0) issue(nxt, na, nb, 0, NL);
+    if (!kSpreadLoads && nxt >= 0) issue(nxt, nla);
+    const int kn = nxt >= 0 ? nxt : 0;
+    const void* bA = stage_base(tileA, kn);
+    const void* bB = GATHER ? nullptr : stage_base(tileB, kn);
     frag(sa, sb, 0, af[0], bf[0]);
 #pragma unroll
     for (int ss = 0; ss < KS; ++ss) {
-      if (ss + 1 < KS) frag(sa, sb, ss + 1, af[(ss + 1) & 1], bf[(ss + 1) & 1]);
+      const int cur = ss & 1, nx = (ss + 1) & 1;
 #pragma unroll
-      for (int a = 0; a < FB; ++a)
+      for (int a = 0; a < FB; ++a) {
 #pragma unroll
-        for (int b = 0; b < TB; ++b) Mma<GT>::run(af[ss & 1][a], bf[ss & 1][b], acc[a][b]);
-      if (ss + 1 < KS) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int b = 0; b < TB; ++b) Mma<GT>::run(af[cur][a], bf[cur][b], acc[a][b]);
+        if (ss + 1 < KS) {
+          frag_one(sa, sb, ss + 1, a, af[nx][a], bf[nx][a]);
           __builtin_amdgcn_sched_group_barrier(0x008, 2 * MPER, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * MPER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, TB * MPER, 0);
         }
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 16 * MPER, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kSpreadLoads && nxt >= 0) {
+          constexpr int PER = (NI + NG - 1) / NG;
+#pragma unroll
+          for (int j = (ss * FB + a) * PER; j < (ss * FB + a + 1) * PER && j < NI; ++j)
+            issue_one(bA, bB, nla, j >> 1, j & 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (GATHER && nxt >= 0 && ss * PER < NL) issue(nxt, na, nb, ss * PER, (ss + 1) * PER <= NL ? PER : NL - ss * PER);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -337,15 +398,17 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   uint8_t* const sB0 = st0 + kTS;
   uint8_t* const sA1 = st1;
   uint8_t* const sB1 = st1 + kTS;
+  const uint32_t l0 = lds_addr(st0), l1 = lds_addr(st1);
   if constexpr (NS == 4) {
     uint8_t* const sA2 = st2;
     uint8_t* const sB2 = st2 + kTS;
     uint8_t* const sA3 = st3;
     uint8_t* const sB3 = st3 + kTS;
-    if (0 < nk) issue(0, sA0, sB0, 0, NL);
-    if (1 < nk) issue(1, sA1, sB1, 0, NL);
-    if (2 < nk) issue(2, sA2, sB2, 0, NL);
-#define ENGRAM_STEP(k, SA, SB_, SAN, SBN)         \
+    const uint32_t l2 = lds_addr(st2), l3 = lds_addr(st3);
+    if (0 < nk) issue(0, l0);
+    if (1 < nk) issue(1, l1);
+    if (2 < nk) issue(2, l2);
+#define ENGRAM_STEP(k, SA, SB_, LN)               \
   {                                               \
     const int left_ = nk - 1 - (k);               \
     if (left_ >= 2)                               \
@@ -355,26 +418,26 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     else                                          \
       ENGRAM_WAIT_VM(0);                          \
     ENGRAM_BARRIER();                             \
-    compute(SA, SB_, (k) + 3 < nk ? (k) + 3 : -1, SAN, SBN); \
+    compute(SA, SB_, (k) + 3 < nk ? (k) + 3 : -1, LN); \
   }
     for (int kt = 0; kt < nk; kt += 4) {
-      ENGRAM_STEP(kt, sA0, sB0, sA3, sB3);
-      ENGRAM_STEP(kt + 1, sA1, sB1, sA0, sB0);
-      ENGRAM_STEP(kt + 2, sA2, sB2, sA1, sB1);
-      ENGRAM_STEP(kt + 3, sA3, sB3, sA2, sB2);
+      ENGRAM_STEP(kt, sA0, sB0, l3);
+      ENGRAM_STEP(kt + 1, sA1, sB1, l0);
+      ENGRAM_STEP(kt + 2, sA2, sB2, l1);
+      ENGRAM_STEP(kt + 3, sA3, sB3, l2);
     }
 #undef ENGRAM_STEP
   } else {
-    if (0 < nk) issue(0, sA0, sB0, 0, NL);
-#define ENGRAM_STEP(k, SA, SB_, SAN, SBN)         \
+    if (0 < nk) issue(0, l0);
+#define ENGRAM_STEP(k, SA, SB_, LN)               \
   {                                               \
     ENGRAM_WAIT_VM(0);                            \
     ENGRAM_BARRIER();                             \
-    compute(SA, SB_, (k) + 1 < nk ? (k) + 1 : -1, SAN, SBN); \
+    compute(SA, SB_, (k) + 1 < nk ? (k) + 1 : -1, LN); \
   }
     for (int kt = 0; kt < nk; kt += 2) {
-      ENGRAM_STEP(kt, sA0, sB0, sA1, sB1);
-      ENGRAM_STEP(kt + 1, sA1, sB1, sA0, sB0);
+      ENGRAM_STEP(kt, sA0, sB0, l1);
+      ENGRAM_STEP(kt + 1, sA1, sB1, l0);
     }
 #undef ENGRAM_STEP
   }
@@ -408,52 +471,84 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         const int c16 = (lane & 31) ^ (t & 31);  // logical piece landing at slot lane&31
         int64_t m = m0 + t;
         m = m < g.M ? m : g.M - 1;
-        load_lds16(g.h + ((m * d + f0) + c16 * 8) * 2, trow(t0));
+        load_lds16(g.h + ((m * d + f0) + c16 * 8) * 2, lds_addr(trow(t0)));
+      }
+      float* red = reinterpret_cast<float*>(sIdxOrRed);  // [2 wf][2 wt][TB][32][3]
+      float* const sg = red + kRedFloats;                 // [256] gamma_q * gamma_k of the tile
+      const bool has_gamma = g.gamma_q || g.gamma_k;
+      if (has_gamma) {
+        const int f = f0 + tid;
+        sg[tid] = (g.gamma_q ? g.gamma_q[f] : 1.f) * (g.gamma_k ? g.gamma_k[f] : 1.f);
       }
       ENGRAM_WAIT_VM(0);
       __syncthreads();
-      float* red = reinterpret_cast<float*>(sIdxOrRed);  // [2 wf][2 wt][TB][32][3]
+      // Per token (lane column), over this wave's 128 features: sum k^2,
+      // sum g h k (g = gamma_q gamma_k), sum h^2.  Variants without gamma and
+      // without the k store keep those branches out of the unrolled body.
+      auto key_sums = [&](auto kGamma, auto kStoreK) __attribute__((always_inline)) {
+        constexpr bool G = decltype(kGamma)::value;
+        constexpr bool SK = decltype(kStoreK)::value;
 #pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        const int t = (wt * TB + b) * 32 + l32;
-        const int64_t m = m0 + t;
-        const bool valid = m < g.M;
-        const uint8_t* hrow = trow(t);
-        float skk = 0.f, shk = 0.f, shh = 0.f;
+        for (int b = 0; b < TB; ++b) {
+          const int t = (wt * TB + b) * 32 + l32;
+          const int64_t m = m0 + t;
+          const uint8_t* hrow = trow(t);
+          u32x2 hr[FB * 4];
 #pragma unroll
-        for (int a = 0; a < FB; ++a) {
+          for (int j = 0; j < FB * 4; ++j) {
+            const int c16 = wf * FB * 4 + j;
+            hr[j] = *reinterpret_cast<const u32x2*>(hrow + ((c16 ^ (t & 31)) << 4) + lhalf * 8);
+          }
+          float skk = 0.f, shk = 0.f, shh = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c16 = (wf * FB + a) * 4 + q;
-            const int f = f0 + c16 * 8 + lhalf * 4;
-            const u32x2 hr =
-                *reinterpret_cast<const u32x2*>(hrow + ((c16 ^ (t & 31)) << 4) + lhalf * 8);
-            const floatx4 hx = floatx4{__uint_as_float(hr[0] << 16), __uint_as_float(hr[0] & 0xFFFF0000u),
-                                       __uint_as_float(hr[1] << 16), __uint_as_float(hr[1] & 0xFFFF0000u)};
-            floatx4 gg = floatx4{1.f, 1.f, 1.f, 1.f};
-            if (g.gamma_q) gg *= *reinterpret_cast<const floatx4*>(g.gamma_q + f);
-            if (g.gamma_k) gg *= *reinterpret_cast<const floatx4*>(g.gamma_k + f);
-            float kv[4];
+          for (int a = 0; a < FB; ++a) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              kv[r] = acc_read(acc[a][b][q * 4 + r]);
-              skk += kv[r] * kv[r];
-              shk += gg[r] * hx[r] * kv[r];
-              shh += hx[r] * hx[r];
+            for (int q = 0; q < 4; ++q) {
+              const u32x2 h2 = hr[a * 4 + q];
+              floatx4 hx = floatx4{__uint_as_float(h2[0] << 16), __uint_as_float(h2[0] & 0xFFFF0000u),
+                                   __uint_as_float(h2[1] << 16), __uint_as_float(h2[1] & 0xFFFF0000u)};
+              shh += hx[0] * hx[0];
+              shh += hx[1] * hx[1];
+              shh += hx[2] * hx[2];
+              shh += hx[3] * hx[3];
+              if constexpr (G) {
+                const int fl = (wf * FB + a) * 32 + q * 8 + lhalf * 4;
+                hx *= *reinterpret_cast<const floatx4*>(sg + fl);
+              }
+              float kv[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                kv[r] = acc_read(acc[a][b][q * 4 + r]);
+                skk += kv[r] * kv[r];
+                shk += hx[r] * kv[r];
+              }
+              if constexpr (SK) {
+                if (m < g.M) {
+                  const int f = f0 + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
+                  *reinterpret_cast<u32x2*>(g.k_out + (m * d + f) * 2) =
+                      u32x2{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
+                }
+              }
             }
-            if (g.k_out && valid) store4(g.k_out, m * d + f, ENGRAM_BF16, kv[0], kv[1], kv[2], kv[3]);
           }
           __builtin_amdgcn_sched_barrier(0);
+          skk += __shfl_xor(skk, 32);
+          shk += __shfl_xor(shk, 32);
+          shh += __shfl_xor(shh, 32);
+          if (lhalf == 0) {
+            float* p = red + ((((wf * 2) + wt) * TB + b) * 32 + l32) * 3;
+            p[0] = skk;
+            p[1] = shk;
+            p[2] = shh;
+          }
         }
-        skk += __shfl_xor(skk, 32);
-        shk += __shfl_xor(shk, 32);
-        shh += __shfl_xor(shh, 32);
-        if (lhalf == 0) {
-          float* p = red + ((((wf * 2) + wt) * TB + b) * 32 + l32) * 3;
-          p[0] = skk;
-          p[1] = shk;
-          p[2] = shh;
-        }
+      };
+      using T_ = std::true_type;
+      using F_ = std::false_type;
+      if (has_gamma) {
+        if (g.k_out) key_sums(T_{}, T_{}); else key_sums(T_{}, F_{});
+      } else {
+        if (g.k_out) key_sums(F_{}, T_{}); else key_sums(F_{}, F_{});
       }
       __syncthreads();
       {  // 2 wt x TB x 32 = 256 tokens, one per thread; add the two feature halves
@@ -480,10 +575,8 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
           for (int q = 0; q < 4; ++q) {
             const int c16 = (wf * FB + a) * 4 + q;
             u32x2 u;
-            u[0] = (uint32_t)f32_to_bf16_bits(acc_read(acc[a][b][q * 4])) |
-                   ((uint32_t)f32_to_bf16_bits(acc_read(acc[a][b][q * 4 + 1])) << 16);
-            u[1] = (uint32_t)f32_to_bf16_bits(acc_read(acc[a][b][q * 4 + 2])) |
-                   ((uint32_t)f32_to_bf16_bits(acc_read(acc[a][b][q * 4 + 3])) << 16);
+            u[0] = pack_bf16x2(acc_read(acc[a][b][q * 4]), acc_read(acc[a][b][q * 4 + 1]));
+            u[1] = pack_bf16x2(acc_read(acc[a][b][q * 4 + 2]), acc_read(acc[a][b][q * 4 + 3]));
             *reinterpret_cast<u32x2*>(row + ((c16 ^ (t & 31)) << 4) + lhalf * 8) = u;
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -653,6 +746,8 @@ bool gemm_supported(GemmType type, const GemmArgs& g, bool gather) {
   if (g.F % kBF != 0 || g.group_m < 1) return false;
   if (g.stage_bytes != 64 && g.stage_bytes != 128) return false;
   if (((int64_t)g.K * es) % 256 != 0) return false;  // whole ring turns for either stage shape
+  // per-lane 32-bit byte offsets inside a 256-row tile
+  if ((int64_t)g.K * es * kBT >= (int64_t(1) << 31)) return false;
   if (gather) {
     if (g.J < 1 || g.J > kGatherMaxJ || g.D * es < g.stage_bytes) return false;
     if (((int64_t)g.D * es) % 16 != 0) return false;
