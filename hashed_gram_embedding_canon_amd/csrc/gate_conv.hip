@@ -18,11 +18,15 @@ namespace engram {
 constexpr int kGcTokens = 64;   // R
 constexpr int kMaxTaps = 8;
 
+// raw 16 bytes of VEC features (8 bf16 or 4 fp32), widened at use
 template <int VEC, bool BF16>
-__device__ inline void load_vec(const uint8_t* base, int64_t elem, float* out) {
+__device__ inline u32x4 load_raw(const uint8_t* base, int64_t elem) {
+  return *reinterpret_cast<const u32x4*>(base + elem * (BF16 ? 2 : 4));
+}
+template <int VEC, bool BF16>
+__device__ inline void widen(const u32x4 u, float* out) {
   if constexpr (BF16) {
     static_assert(VEC == 8, "");
-    const u32x4 u = *reinterpret_cast<const u32x4*>(base + elem * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = __uint_as_float(u[i] << 16);
@@ -30,9 +34,8 @@ __device__ inline void load_vec(const uint8_t* base, int64_t elem, float* out) {
     }
   } else {
     static_assert(VEC == 4, "");
-    const floatx4 f = *reinterpret_cast<const floatx4*>(base + elem * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = f[i];
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(u[i]);
   }
 }
 
@@ -105,33 +108,45 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   const uint8_t* __restrict__ vsrc = a.v;
   uint8_t* __restrict__ ydst = a.y;
   const int64_t row0 = b * a.T;
-  float nxt[VEC];
-  if (tbeg < tend) load_vec<VEC, BF16>(vsrc, (row0 + tbeg) * d + f, nxt);
-  for (int64_t t = tbeg; t < tend; ++t) {
-    float cur[VEC];
+  // v rows stream through a ring of PD tokens loaded ahead (each wave keeps
+  // PD 1 KB loads in flight; HBM latency, not bandwidth, bounds a shallower
+  // ring at this occupancy)
+  constexpr int PD = 4;
+  u32x4 ring[PD];
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) cur[c] = nxt[c];
-    if (t + 1 < tend) load_vec<VEC, BF16>(vsrc, (row0 + t + 1) * d + f, nxt);  // one token ahead
-    const float al = alpha_s[t - (t0 - nh)];
+  for (int u = 0; u < PD; ++u)
+    if (tbeg + u < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + tbeg + u) * d + f);
+  for (int64_t tb = tbeg; tb < tend; tb += PD) {
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) cur[c] *= al;
-    if (t >= t0) {
-      float out[VEC];
+    for (int u = 0; u < PD; ++u) {
+      const int64_t t = tb + u;
+      if (t < tend) {
+        float cur[VEC];
+        widen<VEC, BF16>(ring[u], cur);
+        if (t + PD < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + t + PD) * d + f);
+        const float al = alpha_s[t - (t0 - nh)];
 #pragma unroll
-      for (int c = 0; c < VEC; ++c) {
-        float z = w[c][0] * cur[c];
+        for (int c = 0; c < VEC; ++c) cur[c] *= al;
+        if (t >= t0) {
+          float out[VEC];
 #pragma unroll
-        for (int i = 1; i < TAPS; ++i) z += w[c][i] * win[i - 1][c];
-        out[c] = z / (1.0f + expf(-z)) + cur[c];
+          for (int c = 0; c < VEC; ++c) {
+            float z = w[c][0] * cur[c];
+#pragma unroll
+            for (int i = 1; i < TAPS; ++i) z += w[c][i] * win[i - 1][c];
+            // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
+            out[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) + cur[c];
+          }
+          store_vec<VEC, BF16>(ydst, (row0 + t) * d + f, out);
+        }
+#pragma unroll
+        for (int i = NW - 1; i > 0; --i)
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) win[i][c] = win[i - 1][c];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) win[0][c] = cur[c];
       }
-      store_vec<VEC, BF16>(ydst, (row0 + t) * d + f, out);
     }
-#pragma unroll
-    for (int i = NW - 1; i > 0; --i)
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) win[i][c] = win[i - 1][c];
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) win[0][c] = cur[c];
   }
 }
 
