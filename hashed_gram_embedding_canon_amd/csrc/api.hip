@@ -254,6 +254,9 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
   const int64_t N = B * T;
   if (N == 0) return ENGRAM_OK;
   if ((uint64_t)N * (uint64_t)s.J >= (uint64_t(1) << 31)) return ENGRAM_E_UNSUPPORTED;
+  // 16-byte pieces of e are numbered in 32 bits by the gather
+  if ((uint64_t)N * (uint64_t)s.d_mem * (uint64_t)s.es / 16 >= (uint64_t(1) << 32) - 4096)
+    return ENGRAM_E_UNSUPPORTED;
   if (!hidden || !y || !p->w_kv || !p->conv_w) return ENGRAM_E_INVALID;
   if (!aligned16(hidden) || !aligned16(y) || !aligned16(p->w_kv) || !aligned16(p->conv_w))
     return ENGRAM_E_INVALID;

@@ -115,12 +115,15 @@ __device__ inline const void* uniform_ptr(const void* p) {
 //   load_lds16_s: wave-uniform 64-bit base (SGPRs) + per-lane 32-bit offset,
 //                 so a stage's loads need no per-lane address arithmetic
 __device__ inline void load_lds16(const void* src, uint32_t m0v) {
+  m0v = __builtin_amdgcn_readfirstlane(m0v);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(m0v)
                : "memory");
 }
 __device__ inline void load_lds16_s(uint32_t voff, const void* sbase, uint32_t m0v) {
+  m0v = __builtin_amdgcn_readfirstlane(m0v);
+  sbase = uniform_ptr(sbase);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(m0v)
@@ -131,16 +134,24 @@ __device__ inline void load_lds16_s(uint32_t voff, const void* sbase, uint32_t m
 // direct-to-LDS loads is complete once vmcnt says so (waited for explicitly
 // before the barrier), and LDS reads of the previous stage were consumed by
 // MFMAs before it.  __syncthreads() would also wait for every load in flight.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier (the s_barrier builtin itself is not a memory operation
+// to the optimizer).
 #define ENGRAM_BARRIER()                 \
   do {                                   \
+    asm volatile("" ::: "memory");       \
     __builtin_amdgcn_sched_barrier(0);   \
     __builtin_amdgcn_s_barrier();        \
     __builtin_amdgcn_sched_barrier(0);   \
+    asm volatile("" ::: "memory");       \
   } while (0)
 
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
 #define ENGRAM_WAIT_VM(n) \
   __builtin_amdgcn_s_waitcnt(((n)&0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
+// the same, and all of this wave's LDS operations complete
+#define ENGRAM_WAIT_VM_LDS(n) \
+  __builtin_amdgcn_s_waitcnt(((n)&0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4))
 
 constexpr int kBF = kGemmBF;  // features per tile
 constexpr int kBT = 256;      // tokens per tile
@@ -176,6 +187,8 @@ struct Stage {
 // Spread the next stage's load instructions between MFMA groups (1) or issue
 // them in one burst at the start of a stage (0).
 constexpr bool kSpreadLoads = ENGRAM_GEMM_SPREAD != 0;
+// what the load slots of a K stage carry
+constexpr int kSlotNext = 0, kSlotH0 = 1, kSlotNone = 2;
 
 template <int GT, int EPI, bool GATHER, int SB>
 __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
@@ -281,16 +294,50 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       nbase[i] = sTab[gj[i]];
     }
   }
-  // One load instruction of stage kt: piece i of operand A (op 0) or B (op 1)
-  // into the stage buffer at LDS address la (A) / la + kTS (B).
+  // ---- bf16 epilogue staging: 256 token rows of 512 bytes (the tile's 256
+  // features) in the stage buffers.  With two stage buffers, st0 holds tokens
+  // t with (t & 64) == 0 and st1 the others, so each wave's first two token
+  // blocks sit in st0 and the last two in st1.
+  constexpr bool kBf16Epi = EPI == EPI_KV && GT == GEMM_BF16;
+  auto trow = [&](int t) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (NS == 4) {
+      const int k = t >> 6;
+      uint8_t* base = k == 0 ? st0 : (k == 1 ? st1 : (k == 2 ? st2 : st3));
+      return base + (t & 63) * 512;
+    } else {
+      return (((t >> 6) & 1) ? st1 : st0) + ((((t >> 7) << 6) | (t & 63)) * 512);
+    }
+  };
+  // Key tiles with two stage buffers load h in two halves: the st0 half in
+  // the load slots of the last K stage (which computes from st1), the st1
+  // half while the first two token blocks are summed.  Row pair p (0..63) of
+  // half X covers tokens t0, t0+1, t0 = ((p >> 5) << 7) | (X << 6) | ((p & 31) << 1);
+  // lane l takes token t0 + l/32 (rows past M repeat the last one) and lands
+  // its 16-byte piece (l%32) ^ (t%32) at slot l%32 of the row.
+  constexpr bool kHOverlap = kBf16Epi && NS == 2;
+  const bool hov = kHOverlap && f0 < g.d;
+  auto h_t0 = [&](int X, int p) __attribute__((always_inline)) {
+    return ((p >> 5) << 7) | (X << 6) | ((p & 31) << 1);
+  };
+  auto h_voff = [&](int X, int p) __attribute__((always_inline)) -> uint32_t {
+    const int t = h_t0(X, p) + (lane >> 5);
+    const int c16 = (lane & 31) ^ (t & 31);
+    const int64_t tc = m0 + t < g.M ? t : g.M - 1 - m0;
+    return (uint32_t)((tc * g.d + c16 * 8) * 2);
+  };
+  const void* const hbase = kBf16Epi ? uniform_ptr(g.h + (m0 * g.d + f0) * 2) : nullptr;
+
+  // Load slot j of a stage (j = 2i + op): piece i of operand A (op 0) or B
+  // (op 1) into the stage buffer at LDS address la (A) / la + kTS (B).
   // bA / bB: uniform_ptr(tileA / tileB + kt * SB), the stage's row bases.
-  auto issue_one = [&](const void* bA, const void* bB, uint32_t la, int i, int op)
+  auto issue_one = [&](const void* bA, const void* bB, uint32_t la, int j)
                        __attribute__((always_inline)) {
-    const uint32_t m0v = la + (uint32_t)((wave + 4 * i) * 1024);
+    const int i = j >> 1, op = j & 1;
+    const uint32_t m0v = la + (uint32_t)((wave + 4 * i) * 1024) + (op ? kTS : 0);
     if (op == 0) {
       load_lds16_s(voffA[i], bA, m0v);
     } else if constexpr (GATHER) {
-      load_lds16(nbase[i] + (int64_t)nrow[i] * dbytes + (int64_t)gw[i] * ES, m0v + kTS);
+      load_lds16(nbase[i] + (int64_t)nrow[i] * dbytes + (int64_t)gw[i] * ES, m0v);
       // advance to the next stage: D >= kStageElems, so at most one table boundary
       gw[i] += kStageElems;
       const bool wrap = gw[i] >= g.D;
@@ -300,21 +347,24 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       nrow[i] = sIdx[grow[i] * kGatherMaxJ + jn];
       nbase[i] = sTab[jn];
     } else {
-      load_lds16_s(voffB[i], bB, m0v + kTS);
+      load_lds16_s(voffB[i], bB, m0v);
     }
   };
-  auto stage_base = [&](const uint8_t* tile, int kt) __attribute__((always_inline)) -> const void* {
-    return GATHER && tile == nullptr ? nullptr : uniform_ptr(tile + (int64_t)kt * SB);
+  // h row pair 16*wave + j of the st0 half (slot j of the last stage); value
+  // tiles (hov false) read the first 16 bytes of the h tile in every lane
+  auto issue_h0 = [&](int j) __attribute__((always_inline)) {
+    const int p = wave * 16 + j;
+    load_lds16_s(hov ? h_voff(0, p) : 0u, hbase, lds_addr(trow(h_t0(0, p))));
   };
-  // all 2*NL load instructions of stage kt
+  auto stage_base = [&](const uint8_t* tile, int kt) __attribute__((always_inline)) -> const void* {
+    return uniform_ptr(tile + (int64_t)kt * SB);
+  };
+  // all 2*NL load slots of stage kt
   auto issue = [&](int kt, uint32_t la) __attribute__((always_inline)) {
     const void* bA = stage_base(tileA, kt);
     const void* bB = GATHER ? nullptr : stage_base(tileB, kt);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      issue_one(bA, bB, la, i, 0);
-      issue_one(bA, bB, la, i, 1);
-    }
+    for (int j = 0; j < 2 * NL; ++j) issue_one(bA, bB, la, j);
   };
 
   floatx16 acc[FB][TB];
@@ -350,18 +400,28 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // the first step): with one wave per SIMD a wave stalled on a full
   // vector-memory queue issues no MFMA, so the loads go out in small pieces
   // between MFMA groups.
-  auto compute = [&](const uint8_t* sa, const uint8_t* sb, int nxt, uint32_t nla)
+  // hfill: this is the last stage of a key tile; its load slots bring in the
+  // st0 half of h instead.
+  // One K stage from (sa, sb).  kSlots (compile-time, so the unrolled body
+  // has no branches) says what its load slots carry: SLOT_NEXT = stage kl into
+  // the buffer at nla, SLOT_H0 = the st0 half of h, SLOT_NONE = nothing.
+  auto compute = [&](const uint8_t* sa, const uint8_t* sb, int kl, uint32_t nla, auto kSlots)
                      __attribute__((always_inline)) {
+    constexpr int SLOTS = decltype(kSlots)::value;
     constexpr int KS = S::kKSteps;
     constexpr int NG = KS * FB;           // MFMA groups per stage
-    constexpr int NI = 2 * NL;            // load instructions per stage
+    constexpr int NI = 2 * NL;            // load slots per stage
     constexpr int MPER = GT == GEMM_F32 ? 4 : 1;  // MFMA instructions per fragment pair
     static_assert(FB == TB, "one A and one B fragment of the next step per group");
+    static_assert(SLOTS != kSlotH0 || (kHOverlap && NI == 16), "16 h row pairs per wave");
     u32x4 af[2][FB], bf[2][TB];
-    if (!kSpreadLoads && nxt >= 0) issue(nxt, nla);
-    const int kn = nxt >= 0 ? nxt : 0;
-    const void* bA = stage_base(tileA, kn);
-    const void* bB = GATHER ? nullptr : stage_base(tileB, kn);
+    if constexpr (!kSpreadLoads && SLOTS == kSlotNext) issue(kl, nla);
+    if constexpr (!kSpreadLoads && SLOTS == kSlotH0) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) issue_h0(j);
+    }
+    const void* bA = SLOTS == kSlotNext ? stage_base(tileA, kl) : nullptr;
+    const void* bB = SLOTS == kSlotNext && !GATHER ? stage_base(tileB, kl) : nullptr;
     frag(sa, sb, 0, af[0], bf[0]);
 #pragma unroll
     for (int ss = 0; ss < KS; ++ss) {
@@ -380,20 +440,29 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
           __builtin_amdgcn_sched_group_barrier(0x008, TB * MPER, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (kSpreadLoads && nxt >= 0) {
+        if constexpr (kSpreadLoads && SLOTS != kSlotNone) {
           constexpr int PER = (NI + NG - 1) / NG;
 #pragma unroll
-          for (int j = (ss * FB + a) * PER; j < (ss * FB + a + 1) * PER && j < NI; ++j)
-            issue_one(bA, bB, nla, j >> 1, j & 1);
+          for (int j = (ss * FB + a) * PER; j < (ss * FB + a + 1) * PER && j < NI; ++j) {
+            if constexpr (SLOTS == kSlotNext)
+              issue_one(bA, bB, nla, j);
+            else
+              issue_h0(j);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
+  using SlotNext = std::integral_constant<int, kSlotNext>;
+  using SlotH0 = std::integral_constant<int, kSlotH0>;
+  using SlotNone = std::integral_constant<int, kSlotNone>;
 
   // ---- ring: stage k lives in buffer k % NS; loads run NS-1 stages ahead.
   // Each wave issues 2*NL loads per stage, so "stage k landed" is
-  // vmcnt <= 2*NL * (stages issued after k).
+  // vmcnt <= 2*NL * (stages issued after k).  nk is a multiple of NS
+  // (gemm_supported); the final stages are peeled so that the loop body
+  // always loads.
   uint8_t* const sA0 = st0;
   uint8_t* const sB0 = st0 + kTS;
   uint8_t* const sA1 = st1;
@@ -405,43 +474,53 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     uint8_t* const sA3 = st3;
     uint8_t* const sB3 = st3 + kTS;
     const uint32_t l2 = lds_addr(st2), l3 = lds_addr(st3);
-    if (0 < nk) issue(0, l0);
-    if (1 < nk) issue(1, l1);
-    if (2 < nk) issue(2, l2);
-#define ENGRAM_STEP(k, SA, SB_, LN)               \
-  {                                               \
-    const int left_ = nk - 1 - (k);               \
-    if (left_ >= 2)                               \
-      ENGRAM_WAIT_VM(4 * NL);                     \
-    else if (left_ == 1)                          \
-      ENGRAM_WAIT_VM(2 * NL);                     \
-    else                                          \
-      ENGRAM_WAIT_VM(0);                          \
-    ENGRAM_BARRIER();                             \
-    compute(SA, SB_, (k) + 3 < nk ? (k) + 3 : -1, LN); \
+    issue(0, l0);
+    issue(1, l1);
+    issue(2, l2);
+#define ENGRAM_STEP(k, SA, SB_, LN, W, SLOT) \
+  {                                          \
+    ENGRAM_WAIT_VM(W);                       \
+    ENGRAM_BARRIER();                        \
+    compute(SA, SB_, (k) + 3, LN, SLOT{});   \
   }
-    for (int kt = 0; kt < nk; kt += 4) {
-      ENGRAM_STEP(kt, sA0, sB0, l3);
-      ENGRAM_STEP(kt + 1, sA1, sB1, l0);
-      ENGRAM_STEP(kt + 2, sA2, sB2, l1);
-      ENGRAM_STEP(kt + 3, sA3, sB3, l2);
+    int kt = 0;
+    for (; kt + 4 < nk; kt += 4) {
+      ENGRAM_STEP(kt, sA0, sB0, l3, 4 * NL, SlotNext);
+      ENGRAM_STEP(kt + 1, sA1, sB1, l0, 4 * NL, SlotNext);
+      ENGRAM_STEP(kt + 2, sA2, sB2, l1, 4 * NL, SlotNext);
+      ENGRAM_STEP(kt + 3, sA3, sB3, l2, 4 * NL, SlotNext);
     }
+    ENGRAM_STEP(kt, sA0, sB0, l3, 4 * NL, SlotNext);
+    ENGRAM_STEP(kt + 1, sA1, sB1, l0, 4 * NL, SlotNone);
+    ENGRAM_STEP(kt + 2, sA2, sB2, l1, 2 * NL, SlotNone);
+    ENGRAM_STEP(kt + 3, sA3, sB3, l2, 0, SlotNone);
 #undef ENGRAM_STEP
   } else {
-    if (0 < nk) issue(0, l0);
-#define ENGRAM_STEP(k, SA, SB_, LN)               \
-  {                                               \
-    ENGRAM_WAIT_VM(0);                            \
-    ENGRAM_BARRIER();                             \
-    compute(SA, SB_, (k) + 1 < nk ? (k) + 1 : -1, LN); \
+    issue(0, l0);
+#define ENGRAM_STEP(k, SA, SB_, LN, SLOT) \
+  {                                       \
+    ENGRAM_WAIT_VM(0);                    \
+    ENGRAM_BARRIER();                     \
+    compute(SA, SB_, (k) + 1, LN, SLOT{}); \
   }
-    for (int kt = 0; kt < nk; kt += 2) {
-      ENGRAM_STEP(kt, sA0, sB0, l1);
-      ENGRAM_STEP(kt + 1, sA1, sB1, l0);
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+      ENGRAM_STEP(kt, sA0, sB0, l1, SlotNext);
+      ENGRAM_STEP(kt + 1, sA1, sB1, l0, SlotNext);
     }
+    ENGRAM_STEP(kt, sA0, sB0, l1, SlotNext);
+    // one code path for the last stage: value tiles fill their h slots with a
+    // repeated 16-byte read instead of branching around them
+    using LastSlots = std::conditional_t<kHOverlap, SlotH0, SlotNone>;
+    ENGRAM_STEP(kt + 1, sA1, sB1, l0, LastSlots);
 #undef ENGRAM_STEP
   }
-  __syncthreads();  // stage buffers are free from here on
+  // stage buffers are free from here on (the st0 half of h may be in flight)
+  if (hov) {
+    ENGRAM_BARRIER();
+  } else {
+    __syncthreads();
+  }
 
   // ---- epilogues.  acc[a][b][q*4+r] holds C^T[f][m] with
   //      f = f0 + (wf*FB + a)*32 + q*8 + lhalf*4 + r,  m = m0 + (wt*TB + b)*32 + l32
@@ -451,27 +530,25 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     // XOR-swizzled by (token & 31).  h is brought in and v goes out as whole
     // rows (a wave moves two 512-byte rows per instruction).
     const int d = g.d;
-    uint8_t* const bufs0 = st0;
-    // token rows of 512 bytes; each stage buffer (2*kTS bytes) holds SB of them
-    auto trow = [&](int t) __attribute__((always_inline)) -> uint8_t* {
-      if constexpr (NS == 4) {
-        const int k = t >> 6;
-        uint8_t* base = k == 0 ? bufs0 : (k == 1 ? st1 : (k == 2 ? st2 : st3));
-        return base + (t & 63) * 512;
-      } else {
-        return (t < 128 ? bufs0 : st1) + (t & 127) * 512;
-      }
-    };
     if (f0 < d) {
-      // h tile -> LDS: instruction i of wave w fills rows t0, t0+1 (t0 = 2(32w+i))
+      if (hov) {
+        // the st1 half of h (the st0 half went out in the last K stage)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int p = wave * 16 + j;
+          load_lds16_s(h_voff(1, p), hbase, lds_addr(trow(h_t0(1, p))));
+        }
+      } else {
+        // whole h tile: instruction i of wave w fills rows t0, t0+1 (t0 = 2(32w+i))
 #pragma unroll 4
-      for (int i = 0; i < 32; ++i) {
-        const int t0 = (wave * 32 + i) * 2;
-        const int t = t0 + (lane >> 5);
-        const int c16 = (lane & 31) ^ (t & 31);  // logical piece landing at slot lane&31
-        int64_t m = m0 + t;
-        m = m < g.M ? m : g.M - 1;
-        load_lds16(g.h + ((m * d + f0) + c16 * 8) * 2, lds_addr(trow(t0)));
+        for (int i = 0; i < 32; ++i) {
+          const int t0 = (wave * 32 + i) * 2;
+          const int t = t0 + (lane >> 5);
+          const int c16 = (lane & 31) ^ (t & 31);  // logical piece landing at slot lane&31
+          int64_t m = m0 + t;
+          m = m < g.M ? m : g.M - 1;
+          load_lds16(g.h + ((m * d + f0) + c16 * 8) * 2, lds_addr(trow(t0)));
+        }
       }
       float* red = reinterpret_cast<float*>(sIdxOrRed);  // [2 wf][2 wt][TB][32][3]
       float* const sg = red + kRedFloats;                 // [256] gamma_q * gamma_k of the tile
@@ -480,16 +557,21 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         const int f = f0 + tid;
         sg[tid] = (g.gamma_q ? g.gamma_q[f] : 1.f) * (g.gamma_k ? g.gamma_k[f] : 1.f);
       }
-      ENGRAM_WAIT_VM(0);
-      __syncthreads();
+      if (hov) {
+        ENGRAM_WAIT_VM_LDS(16);  // own st0-half loads landed, gamma written
+      } else {
+        ENGRAM_WAIT_VM_LDS(0);
+      }
+      ENGRAM_BARRIER();
       // Per token (lane column), over this wave's 128 features: sum k^2,
       // sum g h k (g = gamma_q gamma_k), sum h^2.  Variants without gamma and
       // without the k store keep those branches out of the unrolled body.
-      auto key_sums = [&](auto kGamma, auto kStoreK) __attribute__((always_inline)) {
+      // Token blocks [B0, B1) of this wave.
+      auto key_sums = [&](auto kGamma, auto kStoreK, auto kB0, auto kB1) __attribute__((always_inline)) {
         constexpr bool G = decltype(kGamma)::value;
         constexpr bool SK = decltype(kStoreK)::value;
 #pragma unroll
-        for (int b = 0; b < TB; ++b) {
+        for (int b = decltype(kB0)::value; b < decltype(kB1)::value; ++b) {
           const int t = (wt * TB + b) * 32 + l32;
           const int64_t m = m0 + t;
           const uint8_t* hrow = trow(t);
@@ -545,10 +627,24 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       };
       using T_ = std::true_type;
       using F_ = std::false_type;
-      if (has_gamma) {
-        if (g.k_out) key_sums(T_{}, T_{}); else key_sums(T_{}, F_{});
+      auto sums = [&](auto kB0, auto kB1) __attribute__((always_inline)) {
+        if (has_gamma) {
+          if (g.k_out) key_sums(T_{}, T_{}, kB0, kB1); else key_sums(T_{}, F_{}, kB0, kB1);
+        } else {
+          if (g.k_out) key_sums(F_{}, T_{}, kB0, kB1); else key_sums(F_{}, F_{}, kB0, kB1);
+        }
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I2 = std::integral_constant<int, 2>;
+      using I4 = std::integral_constant<int, TB>;
+      static_assert(TB == 4, "two token blocks per h half");
+      if (hov) {
+        sums(I0{}, I2{});       // blocks 0, 1: h rows in st0
+        ENGRAM_WAIT_VM(0);      // own st1-half loads landed
+        ENGRAM_BARRIER();
+        sums(I2{}, I4{});       // blocks 2, 3: h rows in st1
       } else {
-        if (g.k_out) key_sums(F_{}, T_{}); else key_sums(F_{}, F_{});
+        sums(I0{}, I4{});
       }
       __syncthreads();
       {  // 2 wt x TB x 32 = 256 tokens, one per thread; add the two feature halves

@@ -58,27 +58,47 @@ hipError_t launch_hash(const int32_t* tokens, const int32_t* canon, int64_t N, i
   return hipGetLastError();
 }
 
-// grid.y = table j (uniform per block); x walks (token, 16-byte piece) pairs.
+// Piece c of e (16 bytes) is piece c % rc of row idx[c / rc] of table
+// (c / rc) % J: e is written front to back and idx read in order.  Each
+// thread moves kGatherPer pieces, kGatherPer * 256 apart, with all its row
+// loads in flight together.  32-bit piece numbers (the host checks the size).
+constexpr int kGatherPer = 4;
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ idx,
-                                                     uint8_t* __restrict__ e, int64_t N,
+                                                     uint8_t* __restrict__ e, uint32_t pieces,
                                                      GatherArgs g) {
-  const int j = blockIdx.y;
-  const int rc = g.row_chunks;
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= N * rc) return;
-  const int64_t n = c / rc;
-  const int part = (int)(c - n * rc);
-  const int64_t row = idx[n * g.J + j];
-  const uint4* src = reinterpret_cast<const uint4*>(g.base[j] + row * rc * 16) + part;
-  uint4* dst = reinterpret_cast<uint4*>(e + (n * g.J + j) * rc * 16) + part;
-  *dst = *src;
+  __shared__ const uint8_t* base_s[ENGRAM_MAX_TABLES];
+  if (threadIdx.x < (unsigned)g.J) base_s[threadIdx.x] = g.base[threadIdx.x];
+  __syncthreads();
+  const uint32_t rc = (uint32_t)g.row_chunks;
+  const uint32_t J = (uint32_t)g.J;
+  const uint32_t c0 = blockIdx.x * (256u * kGatherPer) + threadIdx.x;
+  u32x4 v[kGatherPer];
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) {
+    const uint32_t c = c0 + u * 256u;
+    if (c < pieces) {
+      const uint32_t nj = c / rc;  // token * J + table
+      const uint32_t part = c - nj * rc;
+      const uint32_t j = nj % J;
+      const int64_t row = idx[nj];
+      v[u] = *(reinterpret_cast<const u32x4*>(base_s[j] + row * rc * 16) + part);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) {
+    const uint32_t c = c0 + u * 256u;
+    if (c < pieces) *(reinterpret_cast<u32x4*>(e) + c) = v[u];
+  }
 }
 
 hipError_t launch_gather(const int32_t* idx, uint8_t* e, int64_t N, const GatherArgs& g,
                          hipStream_t s) {
   if (N == 0) return hipSuccess;
-  const int64_t blocks = (N * g.row_chunks + 255) / 256;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks, g.J), dim3(256), 0, s, idx, e, N, g);
+  const int64_t pieces = N * g.J * g.row_chunks;
+  if (pieces >= (int64_t(1) << 32) - 256 * kGatherPer) return hipErrorInvalidValue;
+  const int64_t blocks = (pieces + 256 * kGatherPer - 1) / (256 * kGatherPer);
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, idx, e,
+                     (uint32_t)pieces, g);
   return hipGetLastError();
 }
 
