@@ -24,8 +24,12 @@ struct Shape {
 };
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-// LDS stage shape of the MFMA GEMMs (bytes of K per stage; see gemm.hip)
-constexpr int32_t kGemmStageBytes = 128;
+// LDS stage shape of the MFMA GEMMs (bytes of K per stage; see gemm.hip).
+// Two 128-byte stages: the four-deep ring of 64-byte stages hides more load
+// latency (fewer cycles per tile) but runs at a lower clock under the power
+// limit and measured slower.
+constexpr int32_t kFwdStageBytes = 128;
+constexpr int32_t kBwdStageBytes = 128;
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 engram_status check_config(const engram_config* c, Shape* s) {
@@ -147,7 +151,7 @@ bool fused_gather(const Shape& s, const engram_saved* sv) {
   ga.F = 2 * s.d;
   ga.K = s.d_mem;
   ga.group_m = 1;
-  ga.stage_bytes = kGemmStageBytes;
+  ga.stage_bytes = kFwdStageBytes;
   ga.J = s.J;
   ga.D = s.D;
   return gemm_supported(s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32, ga, true);
@@ -326,7 +330,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     ga.F = 2 * s.d;
     ga.K = s.d_mem;
     ga.group_m = 4;
-    ga.stage_bytes = kGemmStageBytes;
+    ga.stage_bytes = kFwdStageBytes;
     ga.d = s.d;
     ga.io_dtype = s.dtype;
     ga.h = (const uint8_t*)hidden;
@@ -440,7 +444,7 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
       ga.F = s.d_mem;
       ga.K = 2 * s.d;
       ga.group_m = 4;
-      ga.stage_bytes = kGemmStageBytes;
+      ga.stage_bytes = kBwdStageBytes;
       ga.c_out = w.de;
       Timed tm("de_gemm", hs);
       if (launch_gemm(bf ? GEMM_F16 : GEMM_F32, EPI_STORE_F32, ga, hs) != hipSuccess)

@@ -188,7 +188,9 @@ struct Stage {
 // them in one burst at the start of a stage (0).
 constexpr bool kSpreadLoads = ENGRAM_GEMM_SPREAD != 0;
 // what the load slots of a K stage carry
-constexpr int kSlotNext = 0, kSlotH0 = 1, kSlotNone = 2;
+constexpr int kSlotNext = 0, kSlotNone = 1, kSlotH = 2;  // kSlotH + X: part X of h
+template <int X>
+using SlotHPart = std::integral_constant<int, kSlotH + X>;
 
 template <int GT, int EPI, bool GATHER, int SB>
 __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
@@ -295,29 +297,36 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     }
   }
   // ---- bf16 epilogue staging: 256 token rows of 512 bytes (the tile's 256
-  // features) in the stage buffers.  With two stage buffers, st0 holds tokens
-  // t with (t & 64) == 0 and st1 the others, so each wave's first two token
-  // blocks sit in st0 and the last two in st1.
+  // features) in the stage buffers, part X = buffer X.  Token t = 128w +
+  // 64u + r (w: wave half, u: which 64 of it) lives in part u (two buffers,
+  // row 64w + r) or part 2u + w (four buffers, row r), so the first two
+  // token blocks of every wave (u = 0) sit in the first half of the parts.
   constexpr bool kBf16Epi = EPI == EPI_KV && GT == GEMM_BF16;
-  auto trow = [&](int t) __attribute__((always_inline)) -> uint8_t* {
-    if constexpr (NS == 4) {
-      const int k = t >> 6;
-      uint8_t* base = k == 0 ? st0 : (k == 1 ? st1 : (k == 2 ? st2 : st3));
-      return base + (t & 63) * 512;
-    } else {
-      return (((t >> 6) & 1) ? st1 : st0) + ((((t >> 7) << 6) | (t & 63)) * 512);
-    }
+  auto part_base = [&](int X) __attribute__((always_inline)) -> uint8_t* {
+    return X == 0 ? st0 : (X == 1 ? st1 : (X == 2 ? st2 : st3));
   };
-  // Key tiles with two stage buffers load h in two halves: the st0 half in
-  // the load slots of the last K stage (which computes from st1), the st1
-  // half while the first two token blocks are summed.  Row pair p (0..63) of
-  // half X covers tokens t0, t0+1, t0 = ((p >> 5) << 7) | (X << 6) | ((p & 31) << 1);
-  // lane l takes token t0 + l/32 (rows past M repeat the last one) and lands
-  // its 16-byte piece (l%32) ^ (t%32) at slot l%32 of the row.
-  constexpr bool kHOverlap = kBf16Epi && NS == 2;
+  auto trow = [&](int t) __attribute__((always_inline)) -> uint8_t* {
+    const int w = t >> 7, u = (t >> 6) & 1, r = t & 63;
+    if constexpr (NS == 4)
+      return part_base(2 * u + w) + r * 512;
+    else
+      return part_base(u) + (w * 64 + r) * 512;
+  };
+  // Key tiles load h part by part into buffers as the ring frees them: with
+  // two buffers part 0 in the load slots of the last K stage, with four
+  // parts 0, 1, 2 in those of the last three; the last part goes out after
+  // the loop and lands while the first two token blocks are summed.  Row pair
+  // p of part X covers tokens t0, t0+1 (h_t0); lane l takes token t0 + l/32
+  // (rows past M repeat the last one) and lands its 16-byte piece
+  // (l%32) ^ (t%32) at slot l%32 of the row.  A part is 2*NL row pairs per
+  // wave, one per load slot.
+  constexpr bool kHOverlap = kBf16Epi;
   const bool hov = kHOverlap && f0 < g.d;
   auto h_t0 = [&](int X, int p) __attribute__((always_inline)) {
-    return ((p >> 5) << 7) | (X << 6) | ((p & 31) << 1);
+    if constexpr (NS == 4)  // 32 pairs: part X = 2u + w
+      return ((X & 1) << 7) | ((X >> 1) << 6) | (p << 1);
+    else                    // 64 pairs: part X = u
+      return ((p >> 5) << 7) | (X << 6) | ((p & 31) << 1);
   };
   auto h_voff = [&](int X, int p) __attribute__((always_inline)) -> uint32_t {
     const int t = h_t0(X, p) + (lane >> 5);
@@ -350,11 +359,11 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       load_lds16_s(voffB[i], bB, m0v);
     }
   };
-  // h row pair 16*wave + j of the st0 half (slot j of the last stage); value
-  // tiles (hov false) read the first 16 bytes of the h tile in every lane
-  auto issue_h0 = [&](int j) __attribute__((always_inline)) {
-    const int p = wave * 16 + j;
-    load_lds16_s(hov ? h_voff(0, p) : 0u, hbase, lds_addr(trow(h_t0(0, p))));
+  // h row pair (2*NL)*wave + j of part X (load slot j); value tiles (hov
+  // false) read the first 16 bytes of the h tile in every lane instead
+  auto issue_h = [&](int X, int j) __attribute__((always_inline)) {
+    const int p = 2 * NL * wave + j;
+    load_lds16_s(hov ? h_voff(X, p) : 0u, hbase, lds_addr(trow(h_t0(X, p))));
   };
   auto stage_base = [&](const uint8_t* tile, int kt) __attribute__((always_inline)) -> const void* {
     return uniform_ptr(tile + (int64_t)kt * SB);
@@ -403,8 +412,8 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // hfill: this is the last stage of a key tile; its load slots bring in the
   // st0 half of h instead.
   // One K stage from (sa, sb).  kSlots (compile-time, so the unrolled body
-  // has no branches) says what its load slots carry: SLOT_NEXT = stage kl into
-  // the buffer at nla, SLOT_H0 = the st0 half of h, SLOT_NONE = nothing.
+  // has no branches) says what its load slots carry: kSlotNext = stage kl into
+  // the buffer at nla, kSlotH + X = part X of h, kSlotNone = nothing.
   auto compute = [&](const uint8_t* sa, const uint8_t* sb, int kl, uint32_t nla, auto kSlots)
                      __attribute__((always_inline)) {
     constexpr int SLOTS = decltype(kSlots)::value;
@@ -413,12 +422,12 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     constexpr int NI = 2 * NL;            // load slots per stage
     constexpr int MPER = GT == GEMM_F32 ? 4 : 1;  // MFMA instructions per fragment pair
     static_assert(FB == TB, "one A and one B fragment of the next step per group");
-    static_assert(SLOTS != kSlotH0 || (kHOverlap && NI == 16), "16 h row pairs per wave");
+    static_assert(SLOTS < kSlotH || kHOverlap, "h parts only in the bf16 key/value epilogue");
     u32x4 af[2][FB], bf[2][TB];
     if constexpr (!kSpreadLoads && SLOTS == kSlotNext) issue(kl, nla);
-    if constexpr (!kSpreadLoads && SLOTS == kSlotH0) {
+    if constexpr (!kSpreadLoads && SLOTS >= kSlotH) {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) issue_h0(j);
+      for (int j = 0; j < NI; ++j) issue_h(SLOTS - kSlotH, j);
     }
     const void* bA = SLOTS == kSlotNext ? stage_base(tileA, kl) : nullptr;
     const void* bB = SLOTS == kSlotNext && !GATHER ? stage_base(tileB, kl) : nullptr;
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
             if constexpr (SLOTS == kSlotNext)
               issue_one(bA, bB, nla, j);
             else
-              issue_h0(j);
+              issue_h(SLOTS - kSlotH, j);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -455,7 +464,6 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     }
   };
   using SlotNext = std::integral_constant<int, kSlotNext>;
-  using SlotH0 = std::integral_constant<int, kSlotH0>;
   using SlotNone = std::integral_constant<int, kSlotNone>;
 
   // ---- ring: stage k lives in buffer k % NS; loads run NS-1 stages ahead.
@@ -491,9 +499,17 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       ENGRAM_STEP(kt + 3, sA3, sB3, l2, 4 * NL, SlotNext);
     }
     ENGRAM_STEP(kt, sA0, sB0, l3, 4 * NL, SlotNext);
-    ENGRAM_STEP(kt + 1, sA1, sB1, l0, 4 * NL, SlotNone);
-    ENGRAM_STEP(kt + 2, sA2, sB2, l1, 2 * NL, SlotNone);
-    ENGRAM_STEP(kt + 3, sA3, sB3, l2, 0, SlotNone);
+    if constexpr (kHOverlap) {
+      // h parts 0, 1, 2 into the buffers of stages nk-4, nk-3, nk-2 as they
+      // free up; they count like stage loads in the waits
+      ENGRAM_STEP(kt + 1, sA1, sB1, l0, 4 * NL, SlotHPart<0>);
+      ENGRAM_STEP(kt + 2, sA2, sB2, l1, 4 * NL, SlotHPart<1>);
+      ENGRAM_STEP(kt + 3, sA3, sB3, l2, 4 * NL, SlotHPart<2>);
+    } else {
+      ENGRAM_STEP(kt + 1, sA1, sB1, l0, 4 * NL, SlotNone);
+      ENGRAM_STEP(kt + 2, sA2, sB2, l1, 2 * NL, SlotNone);
+      ENGRAM_STEP(kt + 3, sA3, sB3, l2, 0, SlotNone);
+    }
 #undef ENGRAM_STEP
   } else {
     issue(0, l0);
@@ -511,7 +527,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     ENGRAM_STEP(kt, sA0, sB0, l1, SlotNext);
     // one code path for the last stage: value tiles fill their h slots with a
     // repeated 16-byte read instead of branching around them
-    using LastSlots = std::conditional_t<kHOverlap, SlotH0, SlotNone>;
+    using LastSlots = std::conditional_t<kHOverlap, SlotHPart<0>, SlotNone>;
     ENGRAM_STEP(kt + 1, sA1, sB1, l0, LastSlots);
 #undef ENGRAM_STEP
   }
@@ -532,12 +548,9 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     const int d = g.d;
     if (f0 < d) {
       if (hov) {
-        // the st1 half of h (the st0 half went out in the last K stage)
+        // the last part of h (the others went out in the last K stages)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int p = wave * 16 + j;
-          load_lds16_s(h_voff(1, p), hbase, lds_addr(trow(h_t0(1, p))));
-        }
+        for (int j = 0; j < 2 * NL; ++j) issue_h(NS - 1, j);
       } else {
         // whole h tile: instruction i of wave w fills rows t0, t0+1 (t0 = 2(32w+i))
 #pragma unroll 4
@@ -558,7 +571,10 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         sg[tid] = (g.gamma_q ? g.gamma_q[f] : 1.f) * (g.gamma_k ? g.gamma_k[f] : 1.f);
       }
       if (hov) {
-        ENGRAM_WAIT_VM_LDS(16);  // own st0-half loads landed, gamma written
+        // parts of the first two token blocks landed (at most the last 16
+        // h loads, the parts of blocks 2 and 3, still in flight), gamma written
+        static_assert(NS == 2 ? 2 * NL == 16 : 4 * NL == 16, "h part sizes");
+        ENGRAM_WAIT_VM_LDS(16);
       } else {
         ENGRAM_WAIT_VM_LDS(0);
       }
