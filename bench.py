@@ -70,6 +70,231 @@ def cpu_baseline(inp, budget_s: float):
                       f"(each: hash, gather, both projections, gate of 4 tokens, conv), {dt:.1f} s"}
 
 
+# ------------------------------------------------------------ rocprofv3 summaries
+def kernel_key(name: str) -> str:
+    """The bench's name for a rocprofv3 kernel name (empty for other kernels)."""
+    base = name.split("(")[0]
+    if "gemm_kernel<" in base:
+        targs = base.split("<", 1)[1].rstrip(">").replace(" ", "").split(",")
+        gt, epi, gather = targs[0], targs[1], targs[2]
+        if epi == "1":
+            return "de_gemm"
+        return "gather_proj_gemm" if gather == "true" else "proj_gemm"
+    for key in ("bwd_gate_conv", "gate_conv", "gather", "hash", "transpose_w", "atomic_scatter"):
+        if f"{key}_kernel" in base:
+            return key
+    for key in ("sort_", "seg_"):
+        if "engram::" + key in base:
+            return "sorted_scatter"
+    if "copyBuffer" in base:
+        return "copy"
+    return ""
+
+
+def csrc_digest() -> str:
+    """sha256 over the library sources; traffic figures are tied to it."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "hashed_gram_embedding_canon_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    with open(os.path.join(ROOT, "include", "engram.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# bench names made of several dispatches per call: the kernel that runs once per call
+GROUP_LEADER = {"sorted_scatter": "sort_init_kernel"}
+
+
+def _pmc_per_kernel(csv_dir: str, counter: str) -> dict:
+    """Counter value per call of each bench kernel (summed over the dispatches
+    of one call where a bench name covers several kernels)."""
+    import csv
+    import glob
+    total: dict = {}
+    calls: dict = {}
+    for path in glob.glob(os.path.join(csv_dir, "*counter_collection.csv")):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = kernel_key(r["Kernel_Name"])
+                if not k:
+                    continue
+                total[k] = total.get(k, 0.0) + float(r["Counter_Value"])
+                leader = GROUP_LEADER.get(k)
+                if leader is None or leader in r["Kernel_Name"]:
+                    calls[k] = calls.get(k, 0) + 1
+    return {k: total[k] / calls[k] for k in total if calls.get(k)}
+
+
+def summarize_trace(trace_dir: str) -> str:
+    """Per-kernel durations of a rocprofv3 --kernel-trace run (bench kernels
+    only; several dispatches of one bench name in a row count as one call)."""
+    import csv
+    import glob
+    import statistics
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "*kernel_trace.csv")):
+        with open(path) as fh:
+            rows += [r for r in csv.DictReader(fh)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    calls: dict = {}
+    names: dict = {}
+    prev_key, cur = None, None
+    for r in rows:
+        k = kernel_key(r["Kernel_Name"])
+        if not k or k == "copy":
+            prev_key = None
+            continue
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        names.setdefault(k, set()).add(r["Kernel_Name"].split("(")[0])
+        if k == prev_key and k in GROUP_LEADER and GROUP_LEADER[k] not in r["Kernel_Name"]:
+            cur[-1] += ns
+        else:
+            cur = calls.setdefault(k, [])
+            cur.append(ns)
+        prev_key = k
+    lines = [f"{'kernel':<16} {'calls':>5} {'mean_us':>9} {'median_us':>10} {'min_us':>9} {'max_us':>9}  kernels"]
+    for k, v in sorted(calls.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{k:<16} {len(v):>5} {statistics.mean(v) / 1e3:>9.2f} {statistics.median(v) / 1e3:>10.2f} "
+                     f"{min(v) / 1e3:>9.2f} {max(v) / 1e3:>9.2f}  {'; '.join(sorted(names[k]))}")
+    return "\n".join(lines)
+
+
+def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes) -> str:
+    """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by
+    what the same counter reads for a plain device copy of copy_bytes."""
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    cf = _pmc_per_kernel(copy_fetch_dir, "FETCH_SIZE")["copy"]
+    cw = _pmc_per_kernel(copy_write_dir, "WRITE_SIZE")["copy"]
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    out = [f"source {csrc_digest()}",
+           f"copy_calibration bytes {copy_bytes} fetch_kib {cf:.1f} write_kib {cw:.1f} "
+           f"fetch_scale {f_scale:.4f} write_scale {w_scale:.4f}",
+           f"{'kernel':<18} {'fetch_kib':>14} {'write_kib':>14} {'traffic_bytes':>16}"]
+    for k in sorted(set(fetch) & set(write)):
+        if k == "copy":
+            continue
+        t = fetch[k] * 1024.0 * f_scale + write[k] * 1024.0 * w_scale
+        out.append(f"{k:<18} {fetch[k]:>14.1f} {write[k]:>14.1f} {t:>16.0f}")
+    return "\n".join(out)
+
+
+def traffic_from_profile(workload: str) -> dict:
+    """{kernel: HBM bytes per launch} from profiles/traffic_<workload>.txt when
+    that file was taken from the current sources, else {}."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    rows, src = {}, None
+    with open(path) as fh:
+        for ln in fh:
+            parts = ln.split()
+            if not parts or ln.startswith("#"):
+                continue
+            if parts[0] == "source":
+                src = parts[1]
+            elif len(parts) == 4 and parts[0] not in ("kernel", "copy_calibration"):
+                rows[parts[0]] = float(parts[3])
+    return rows if src == csrc_digest() else {}
+
+
+def backward_units(wl, N):
+    """Algorithmic bytes / flops per launch of each table-gradient backward kernel."""
+    es = 2 if wl.dtype == "bf16" else 4
+    eg_ = 2 if wl.dtype == "bf16" else 4          # fp16 / fp32 GEMM operands
+    J, d, dm, D = wl.J, wl.hidden, wl.d_mem, wl.dim
+    return {
+        # dy, v, k, h in; stats; dk|dv out
+        "bwd_gate_conv": {"bound": "hbm", "bytes": 4 * N * d * es + N * 16 + N * 2 * d * eg_},
+        "transpose_w": {"bound": "hbm", "bytes": 2 * d * dm * es + 2 * d * dm * eg_},
+        "de_gemm": {"bound": "mfma", "flops": 2 * N * 2 * d * dm,
+                    "bytes": N * 2 * d * eg_ + 2 * d * dm * eg_ + N * dm * 4},
+        # idx + de in, at most one fp32 row + key per (token, table) out
+        "sorted_scatter": {"bound": "hbm", "bytes": N * J * 4 + N * dm * 4 + N * J * (D * 4 + 8)},
+        "atomic_scatter": {"bound": "hbm", "bytes": N * J * 4 + N * dm * 4 + N * J * D * 4},
+    }
+
+
+def bench_backward(dp, inp, steps: int) -> dict:
+    """Table-gradient backward of the same workload: sorted segmented reduce
+    (sparse rows) and the dense-atomic variant, per-kernel times and rates."""
+    import torch
+
+    import hashed_gram_embedding_canon_amd as eg
+    from tests import harness as H
+    wl, N = dp.wl, dp.N
+    saved = dp.alloc_saved(("idx", "stats", "k", "v"))
+    dp.forward(saved)
+    dy = H.to_dev(inp.dy)
+    ws = dp.workspace(eg.ENGRAM_OP_BACKWARD)
+    units = backward_units(wl, N)
+    res = {}
+    for mode, label in ((eg.ENGRAM_GRAD_SORTED_SPARSE, "sorted_sparse"),
+                        (eg.ENGRAM_GRAD_ATOMIC_DENSE, "atomic_dense")):
+        out = dp.backward(saved, dy, mode, ws=ws)  # warm-up; allocates the outputs
+        torch.cuda.synchronize()
+        tg = eg.engram_table_grad()
+        tg.mode = mode
+        if mode == eg.ENGRAM_GRAD_SORTED_SPARSE:
+            tg.keys, tg.rows, tg.count = (out["keys"].data_ptr(), out["rows"].data_ptr(),
+                                          out["count"].data_ptr())
+        else:
+            for j, t in enumerate(out["dense"]):
+                tg.dense[j] = t.data_ptr()
+        zero_ms = None
+        if mode == eg.ENGRAM_GRAD_ATOMIC_DENSE:
+            z0, z1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            z0.record()
+            for t in out["dense"]:
+                t.zero_()
+            z1.record()
+            torch.cuda.synchronize()
+            zero_ms = z0.elapsed_time(z1)
+        sv = eg.make_saved(**saved)
+        eg.engram_profile_reset()
+        eg.engram_profile_enable(True)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            eg.engram_backward_table_grad(dp.cfg, dp.params, dp.hidden, dy, B=dp.B, T=dp.T,
+                                          saved=sv, out=tg, workspace=ws)
+        t1.record()
+        torch.cuda.synchronize()
+        eg.engram_profile_enable(False)
+        prof = eg.engram_profile_read()
+        ms = t0.elapsed_time(t1) / steps
+        kern = {}
+        for name, (count, tot) in prof.items():
+            avg = tot / max(count, 1)
+            ent = {"launches": count, "avg_ms": round(avg, 5)}
+            u = units.get(name, {})
+            if "bytes" in u and u["bound"] == "hbm":
+                ent["alg_GBps"] = round(u["bytes"] / (avg * 1e-3) / 1e9, 1)
+                ent["hbm_frac"] = round(ent["alg_GBps"] / HBM_PEAK_GBS, 4)
+            if "flops" in u:
+                ent["TFLOPs"] = round(u["flops"] / (avg * 1e-3) / 1e12, 1)
+            kern[name] = ent
+        entry = {"ms_per_step": round(ms, 4), "tokens_per_s": round(N / (ms * 1e-3), 1),
+                 "kernels": kern}
+        if mode == eg.ENGRAM_GRAD_SORTED_SPARSE:
+            entry["unique_rows"] = int(out["count"].item())
+            entry["token_table_pairs"] = N * wl.J
+        if zero_ms is not None:
+            entry["zero_dense_ms_excluded"] = round(zero_ms, 3)
+            entry["note"] = "accumulates into the caller's dense fp32 tables without zeroing them"
+        res[label] = entry
+        del out
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(nbytes: int):
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -97,13 +322,29 @@ def main():
     ap.add_argument("--workload", default="engram27b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the table-gradient backward block")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--fused-gather", action="store_true",
                     help="let the projection read the table rows itself (ENGRAM_FLAG_FUSED_GATHER) "
                          "instead of gathering e into the workspace first")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the kernel table of a rocprofv3 --kernel-trace --stats csv run")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="print HBM bytes per dispatch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "csv runs of the bench and of --copy-calibration")
+    ap.add_argument("--calibration-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, args.calibration_bytes))
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -162,6 +403,11 @@ def main():
         if "flops" in u:
             ent["TFLOPs"] = round(u["flops"] / (avg * 1e-3) / 1e12, 1)
         kernels[name] = ent
+    traffic = traffic_from_profile(wl.name)
+    for name, ent in kernels.items():
+        if name in traffic:
+            ent["counter_bytes"] = int(traffic[name])
+            ent["counter_GBps"] = round(traffic[name] / (ent["avg_ms"] * 1e-3) / 1e9, 1)
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0] if prof else None
     roof = None
     if dom is not None:
@@ -171,16 +417,26 @@ def main():
             peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
             ach = u["flops"] / avg_s / 1e12
             roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                    "traffic": int(traffic[dom]) if dom in traffic else None}
         else:
             ach = u["bytes"] / avg_s / 1e9
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": int(traffic[dom]) if dom in traffic else None}
     mem_names = [k for k in ("gather", "gate_conv") if k in prof]
     mem_ms = sum(prof[k][1] / prof[k][0] for k in mem_names)
     mem_bytes = sum(units[k]["bytes"] for k in mem_names)
     es = 2 if wl.dtype == "bf16" else 4
     alg_per_token = wl.J * wl.dim * es + 2 * wl.hidden * es + 4  # rows + h + Y + token id
+    hbm_block = {"kernels": mem_names, "ms": round(mem_ms, 4)}
+    if mem_ms:
+        hbm_block["alg_GBps"] = round(mem_bytes / (mem_ms * 1e-3) / 1e9, 1)
+        hbm_block["frac"] = round(hbm_block["alg_GBps"] / HBM_PEAK_GBS, 4)
+        if all(k in traffic for k in mem_names):
+            cb = sum(traffic[k] for k in mem_names)
+            hbm_block["counter_GBps"] = round(cb / (mem_ms * 1e-3) / 1e9, 1)
+            hbm_block["counter_frac"] = round(hbm_block["counter_GBps"] / HBM_PEAK_GBS, 4)
 
     out = {
         "metric": "Engram fwd tokens/s + achieved HBM GB/s (gather+gate+conv), 27B-scale table",
@@ -200,12 +456,13 @@ def main():
                    "d_mem": wl.d_mem, "hidden": wl.hidden, "table_params": wl.table_params,
                    "zipf_s": wl.zipf_s, "vocab": wl.vocab, "canon_vocab": wl.canon_vocab},
         "roofline": roof,
-        "hbm_gather_gate_conv": {"kernels": mem_names, "alg_GBps": round(mem_bytes / (mem_ms * 1e-3) / 1e9, 1) if mem_ms else None,
-                                 "frac": round(mem_bytes / (mem_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if mem_ms else None,
-                                 "ms": round(mem_ms, 4)},
+        "hbm_gather_gate_conv": hbm_block,
         "end_to_end_alg_GBps": round(alg_per_token * N / (ms * 1e-3) / 1e9, 1),
         "kernels": kernels,
     }
+    if not args.no_backward:
+        log(f"[bench] table-gradient backward, {args.backward_steps} steps per mode")
+        out["backward"] = bench_backward(dp, inp, args.backward_steps)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on host cores for ~{args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
