@@ -11,31 +11,43 @@
 //   dk_t   = ca g_k g_q h_t - cb k_t,  ca = ds rq rk / sqrt(d),
 //            cb = rk^3 ds rq P / (sqrt(d) d),  P = <g_q h_t, g_k k_t>
 // (the RMSNorm backward of the key with its projection onto k folded into
-// cb).  One workgroup owns R tokens and all d features of one sequence and
-// walks u = t0-taps+1 .. t0+R+taps-2, keeping the last taps values of v, G,
-// dz and the gated value in registers; each output token needs one
-// workgroup-wide sum (dalpha).  dk and dv leave as fp16 (bf16 io) or fp32
-// (fp32 io): the operands of the de GEMM.
+// cb).  One workgroup owns R tokens and all d features of one sequence, a
+// lane 4 neighbouring features, in two passes:
+//   A: walk u = t0-taps+1 .. t0+R+taps-2 with the last taps-1 gated values
+//      and the last taps dz in registers; v and G stream through a ring of
+//      loads issued a few tokens ahead.  Token t = u-taps+1 is then final:
+//      dv_t = alpha_t dvt_t goes out, and the lane's share of dalpha_t joins
+//      a batch of 8 tokens that is summed over the wave in 10 shuffles.
+//   B: dalpha_t from the per-wave sums; dk_t from h_t and k_t, whose loads
+//      do not depend on each other.
+// dk and dv leave as fp16 (bf16 io) or fp32 (fp32 io): the de GEMM operands.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace engram {
 
-constexpr int kBwTokens = 32;
+constexpr int kBwTokens = 64;   // R
+constexpr int kBwBatch = 8;     // tokens per dalpha reduction batch
+constexpr int kBwMaxWaves = 16; // d / 4 / 64
 
 template <bool BF16>
-__device__ inline void ld4(const uint8_t* base, int64_t elem, float* out) {
+using raw4_t = typename std::conditional<BF16, u32x2, u32x4>::type;
+
+template <bool BF16>
+__device__ inline raw4_t<BF16> ld4_raw(const uint8_t* base, int64_t elem) {
+  return *reinterpret_cast<const raw4_t<BF16>*>(base + elem * (BF16 ? 2 : 4));
+}
+template <bool BF16>
+__device__ inline void widen4(const raw4_t<BF16> u, float* out) {
   if constexpr (BF16) {
-    const u32x2 u = *reinterpret_cast<const u32x2*>(base + elem * 2);
     out[0] = __uint_as_float(u[0] << 16);
     out[1] = __uint_as_float(u[0] & 0xFFFF0000u);
     out[2] = __uint_as_float(u[1] << 16);
     out[3] = __uint_as_float(u[1] & 0xFFFF0000u);
   } else {
-    const floatx4 f = *reinterpret_cast<const floatx4*>(base + elem * 4);
-    out[0] = f[0];
-    out[1] = f[1];
-    out[2] = f[2];
-    out[3] = f[3];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] = __uint_as_float(u[c]);
   }
 }
 
@@ -51,127 +63,210 @@ __device__ inline void st4_grad(uint8_t* base, int64_t elem, const float* v) {
   }
 }
 
+// p[0..7]: this lane's shares of 8 tokens.  Returns the wave-wide sum of
+// token 4*b5 + 2*b4 + b3 (b = lane bits): each halving step sends the half
+// of the values that the partner keeps.
+__device__ inline float wave_sum8(float p[8], int lane) {
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+  float q[4], r[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float send = b5 ? p[k] : p[k + 4];
+    const float keep = b5 ? p[k + 4] : p[k];
+    q[k] = keep + __shfl_xor(send, 32);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float send = b4 ? q[k] : q[k + 2];
+    const float keep = b4 ? q[k + 2] : q[k];
+    r[k] = keep + __shfl_xor(send, 16);
+  }
+  float x = (b3 ? r[1] : r[0]) + __shfl_xor(b3 ? r[0] : r[1], 8);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 1);
+  return x;
+}
+
 template <bool BF16, int TAPS>
 __global__ __launch_bounds__(1024) void bwd_gate_conv_kernel(BwdArgs a) {
   constexpr int R = kBwTokens;
   constexpr int NH = TAPS - 1;
-  __shared__ floatx4 st_s[R + 2 * NH + 1];
-  __shared__ float red[16];
+  constexpr int NW = NH > 0 ? NH : 1;
+  constexpr int PD = TAPS <= 4 ? 4 : (TAPS <= 6 ? 2 : 1);  // tokens of v / G loaded ahead
+  static_assert(R % kBwBatch == 0, "");
+  __shared__ floatx4 st_s[R + 2 * NH + PD];
+  __shared__ float pdw[R][kBwMaxWaves];
+  __shared__ float dal_s[R];
   const int64_t b = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * R;
   const int d = a.d;
   const int64_t T = a.T;
   const float inv_d = 1.0f / (float)d;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
-  for (int i = threadIdx.x; i < R + 2 * NH; i += blockDim.x) {
+  for (int i = threadIdx.x; i < R + 2 * NH + PD; i += blockDim.x) {
     const int64_t u = t0 - NH + i;
     st_s[i] = (u >= 0 && u < T) ? *reinterpret_cast<const floatx4*>(a.stats + (b * T + u) * 4)
                                 : floatx4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
 
-  const int f = threadIdx.x * 4;
-  const bool act = f < d;
-  const int fc = act ? f : 0;
+  const int f = threadIdx.x * 4;  // blockDim.x * 4 == d
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int nwaves = (blockDim.x + 63) >> 6;
-  float w[4][TAPS], gqk[4];
+  const int nwaves = blockDim.x >> 6;
+  const int64_t row0 = b * T;
+  const int64_t tend = t0 + R < T ? t0 + R : T;  // tokens [t0, tend) are this block's
+  float w[4][TAPS];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < TAPS; ++i) w[c][i] = a.conv_w[(f + c) * TAPS + i];
+
+  // ---- pass A
+  float vtw[NW][4];  // gated value at u-1-i
+  float dzw[TAPS][4];  // dz at u-i
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
-    for (int i = 0; i < TAPS; ++i) w[c][i] = a.conv_w[(fc + c) * TAPS + i];
-    gqk[c] = (a.gamma_q ? a.gamma_q[fc + c] : 1.f) * (a.gamma_k ? a.gamma_k[fc + c] : 1.f);
+    for (int i = 0; i < NW; ++i) vtw[i][c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < TAPS; ++i) dzw[i][c] = 0.f;
   }
-  float vtw[NH > 0 ? NH : 1][4];  // gated value at u-1-i
-  float vw[TAPS][4], Gw[TAPS][4], dzw[TAPS][4];  // at u-i
-#pragma unroll
-  for (int i = 0; i < TAPS; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      vw[i][c] = Gw[i][c] = dzw[i][c] = 0.f;
-      if (i < NH) vtw[i][c] = 0.f;
+  const int64_t ubeg = t0 - NH;
+  // Ring of raw v / G rows: token u sits in slot (u - ubeg) % RS from its
+  // load at step u - PD until finish at step u + NH (RS > PD + NH); zero
+  // outside [0, T), and G zero before t0.
+  constexpr int RS = (PD + NH + 1 <= 8) ? 8 : 16;
+  static_assert(RS % kBwBatch == 0 && R % RS == 0, "");
+  raw4_t<BF16> rv[RS], rg[RS];
+  auto fetch = [&](int64_t u, raw4_t<BF16>& v, raw4_t<BF16>& g) __attribute__((always_inline)) {
+    v = raw4_t<BF16>{};
+    g = raw4_t<BF16>{};
+    if (u >= 0 && u < T) {
+      v = ld4_raw<BF16>(a.v, (row0 + u) * d + f);
+      if (u >= t0) g = ld4_raw<BF16>(a.dy, (row0 + u) * d + f);
     }
-  const int64_t row0 = b * T;
-  for (int64_t u = t0 - NH; u < t0 + R + NH; ++u) {
-    const bool in = u >= 0 && u < T;
-    float v[4] = {0.f, 0.f, 0.f, 0.f}, G[4] = {0.f, 0.f, 0.f, 0.f};
-    if (in && act) {
-      ld4<BF16>(a.v, (row0 + u) * d + fc, v);
-      if (u >= t0) ld4<BF16>(a.dy, (row0 + u) * d + fc, G);
-    }
-    const float al = st_s[u - (t0 - NH)][0];
-    float vt[4], dz[4] = {0.f, 0.f, 0.f, 0.f};
+  };
+#pragma unroll
+  for (int k = 0; k < PD; ++k) fetch(ubeg + k, rv[k], rg[k]);
+  float pb[kBwBatch];
+#pragma unroll
+  for (int k = 0; k < kBwBatch; ++k) pb[k] = 0.f;
+
+  // one step of pass A at u (slot k = (u - ubeg) % RS, compile-time)
+  auto step = [&](int64_t u, int k) __attribute__((always_inline)) {
+    fetch(u + PD, rv[(k + PD) % RS], rg[(k + PD) % RS]);
+    float v[4], G[4];
+    widen4<BF16>(rv[k], v);
+    widen4<BF16>(rg[k], G);
+    const float al = st_s[u - ubeg][0];
+    float vt[4], dz[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) vt[c] = al * v[c];
-    if (in && u >= t0) {
+    const bool live = u >= t0 && u < T;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float z = w[c][0] * vt[c];
+    for (int c = 0; c < 4; ++c) {
+      float z = w[c][0] * vt[c];
 #pragma unroll
-        for (int i = 1; i < TAPS; ++i) z += w[c][i] * vtw[i - 1][c];
-        const float sg = 1.0f / (1.0f + expf(-z));
-        dz[c] = G[c] * sg * (1.0f + z * (1.0f - sg));
-      }
+      for (int i = 1; i < TAPS; ++i) z += w[c][i] * vtw[i - 1][c];
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+      dz[c] = live ? G[c] * sg * (1.0f + z * (1.0f - sg)) : 0.f;
     }
 #pragma unroll
     for (int i = TAPS - 1; i > 0; --i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        vw[i][c] = vw[i - 1][c];
-        Gw[i][c] = Gw[i - 1][c];
-        dzw[i][c] = dzw[i - 1][c];
-      }
+      for (int c = 0; c < 4; ++c) dzw[i][c] = dzw[i - 1][c];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      vw[0][c] = v[c];
-      Gw[0][c] = G[c];
-      dzw[0][c] = dz[c];
-    }
+    for (int c = 0; c < 4; ++c) dzw[0][c] = dz[c];
 #pragma unroll
-    for (int i = NH - 1; i > 0; --i)
+    for (int i = NW - 1; i > 0; --i)
 #pragma unroll
       for (int c = 0; c < 4; ++c) vtw[i][c] = vtw[i - 1][c];
     if (NH > 0) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) vtw[0][c] = vt[c];
     }
-
-    const int64_t t = u - NH;  // token whose dz_{t..t+NH} are now all known
-    if (t < t0 || t >= T) continue;  // uniform over the workgroup
-    float dvt[4];
-    float pd = 0.f;
+  };
+  // token t = u - NH (slot kt) is final after step(u): dv_t out, its dalpha
+  // share into pb[pslot]
+  auto finish = [&](int64_t t, int kt, int pslot) __attribute__((always_inline)) {
+    if (t >= tend) return;  // uniform
+    float v[4], G[4];
+    widen4<BF16>(rv[kt], v);
+    widen4<BF16>(rg[kt], G);
+    const float alpha = st_s[t - ubeg][0];
+    float dv[4], pd = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float acc = Gw[NH][c];
+      float acc = G[c];
 #pragma unroll
       for (int i = 0; i < TAPS; ++i) acc += w[c][i] * dzw[NH - i][c];
-      dvt[c] = acc;
-      pd += acc * vw[NH][c];
+      pd += acc * v[c];
+      dv[c] = alpha * acc;
+    }
+    pb[pslot] = pd;
+    st4_grad<BF16>(a.dkv, (row0 + t) * 2 * d + d + f, dv);
+  };
+
+  // warm-up: u = t0-NH .. t0+NH-1 (no token final yet)
+#pragma unroll
+  for (int k = 0; k < 2 * NH; ++k) step(ubeg + k, k % RS);
+  for (int tb = 0; tb < R; tb += RS) {
+#pragma unroll
+    for (int k = 0; k < RS; ++k) {
+      // u = t0 + NH + tb + k, slot (2NH + tb + k) % RS; token t = t0 + tb + k
+      const int64_t u = t0 + NH + tb + k;
+      step(u, (2 * NH + k) % RS);
+      finish(u - NH, (NH + k) % RS, k % kBwBatch);
+      if (k % kBwBatch == kBwBatch - 1) {
+        const float s8 = wave_sum8(pb, lane);
+        if ((lane & 7) == 0) pdw[tb + (k - (kBwBatch - 1)) + ((lane >> 3) & 7)][wave] = s8;
+#pragma unroll
+        for (int q = 0; q < kBwBatch; ++q) pb[q] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < R) {
+    float s = 0.f;
+    for (int i = 0; i < nwaves; ++i) s += pdw[threadIdx.x][i];
+    dal_s[threadIdx.x] = s;
+  }
+  __syncthreads();
+
+  // ---- pass B: dk from h, k and the summed dalpha
+  float gqk[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    gqk[c] = (a.gamma_q ? a.gamma_q[f + c] : 1.f) * (a.gamma_k ? a.gamma_k[f + c] : 1.f);
+  constexpr int UB = 4;
+  for (int i0 = 0; i0 < R; i0 += UB) {
+    raw4_t<BF16> rh[UB], rk[UB];
+#pragma unroll
+    for (int q = 0; q < UB; ++q) {
+      const int64_t t = t0 + i0 + q;
+      if (t < tend) {
+        rh[q] = ld4_raw<BF16>(a.h, (row0 + t) * d + f);
+        rk[q] = ld4_raw<BF16>(a.k, (row0 + t) * d + f);
+      }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) pd += __shfl_xor(pd, o);
-    if (lane == 0) red[wave] = pd;
-    __syncthreads();
-    float dalpha = 0.f;
-    for (int i = 0; i < nwaves; ++i) dalpha += red[i];
-    __syncthreads();
-    if (!act) continue;
-    const floatx4 st = st_s[t - (t0 - NH)];
-    const float alpha = st[0], rq = st[1], rk = st[2], P = st[3];
-    const float ds = dalpha * alpha * (1.0f - alpha);
-    const float ca = ds * rq * rk * inv_sqrt_d;
-    const float cb = rk * rk * rk * ds * rq * P * inv_sqrt_d * inv_d;
-    float hv[4], kv[4], dk[4], dv[4];
-    ld4<BF16>(a.h, (row0 + t) * d + fc, hv);
-    ld4<BF16>(a.k, (row0 + t) * d + fc, kv);
+    for (int q = 0; q < UB; ++q) {
+      const int64_t t = t0 + i0 + q;
+      if (t >= tend) break;
+      const floatx4 st = st_s[t - ubeg];
+      const float alpha = st[0], rq = st[1], rkk = st[2], P = st[3];
+      const float ds = dal_s[i0 + q] * alpha * (1.0f - alpha);
+      const float ca = ds * rq * rkk * inv_sqrt_d;
+      const float cb = rkk * rkk * rkk * ds * rq * P * inv_sqrt_d * inv_d;
+      float hv[4], kv[4], dk[4];
+      widen4<BF16>(rh[q], hv);
+      widen4<BF16>(rk[q], kv);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      dk[c] = ca * gqk[c] * hv[c] - cb * kv[c];
-      dv[c] = alpha * dvt[c];
+      for (int c = 0; c < 4; ++c) dk[c] = ca * gqk[c] * hv[c] - cb * kv[c];
+      st4_grad<BF16>(a.dkv, (row0 + t) * 2 * d + f, dk);
     }
-    st4_grad<BF16>(a.dkv, (row0 + t) * 2 * d + fc, dk);
-    st4_grad<BF16>(a.dkv, (row0 + t) * 2 * d + d + fc, dv);
   }
 }
 
@@ -199,8 +294,9 @@ static hipError_t launch_bwd_taps(const BwdArgs& a, dim3 grid, int threads, hipS
 
 hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return hipSuccess;
-  const int threads = (a.d / 4 + 63) / 64 * 64;
-  if (threads > 1024) return hipErrorInvalidValue;
+  // one lane per 4 features, whole waves: d is a multiple of 256
+  if (a.d % 256 != 0 || a.d / 4 > 64 * kBwMaxWaves) return hipErrorInvalidValue;
+  const int threads = a.d / 4;
   dim3 grid((unsigned)((a.T + kBwTokens - 1) / kBwTokens), (unsigned)a.B);
   return a.io_dtype == ENGRAM_BF16 ? launch_bwd_taps<true>(a, grid, threads, s)
                                    : launch_bwd_taps<false>(a, grid, threads, s);
