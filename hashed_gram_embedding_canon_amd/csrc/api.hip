@@ -372,6 +372,7 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
   if (st != ENGRAM_OK) return st;
   if (!p || !out || B < 0 || T < 0 || T > INT32_MAX || B > 65535) return ENGRAM_E_INVALID;
   if (s.d / 4 > 1024) return ENGRAM_E_UNSUPPORTED;
+  if (s.D > 256) return ENGRAM_E_UNSUPPORTED;  // one 16-byte piece per lane of a row
   if (out->mode < ENGRAM_GRAD_SORTED_SPARSE || out->mode > ENGRAM_GRAD_ATOMIC_DENSE)
     return ENGRAM_E_INVALID;
   const int64_t N = B * T;

@@ -241,57 +241,79 @@ __global__ __launch_bounds__(256) void seg_write_kernel(const uint32_t* __restri
   }
 }
 
-// One wavefront per segment; S lane groups of D/4 lanes each take every S-th
-// element of the segment, then the groups are added in order 0..S-1.
+// Segmented reduce.  A wave holds S = 64 / (D/4) lane groups of D/4 lanes
+// (one 16-byte column piece per lane); each group sums whole segments in a
+// grid-stride walk and writes their rows.  Most segments have one element,
+// so the cost is the chain segment start -> token -> de row; a group runs two
+// segments side by side (two independent chains) and sums each segment's
+// elements in sorted order with two accumulators (a fixed order).
+constexpr int kSegBlocksMax = 4096;
 template <int MODE>
 __global__ __launch_bounds__(256) void seg_reduce_kernel(ScatterArgs a, const uint32_t* __restrict__ vals,
                                                          const uint32_t* __restrict__ seg_start,
                                                          const uint64_t* __restrict__ seg_key,
                                                          const uint32_t* __restrict__ total) {
-  __shared__ floatx4 part[4][64];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t seg = (int64_t)blockIdx.x * 4 + wave;
-  const uint32_t U = total[0];
-  if (seg >= U) return;
-  const int D4 = a.D / 4;
-  const int S = D4 <= 64 ? 64 / D4 : 1;
+  const int D4 = a.D / 4;               // <= 64 (D <= 256)
+  const int S = 64 / D4;
   const int grp = lane / D4;
   const int col = lane - grp * D4;
+  if (grp >= S) return;
+  const int64_t U = total[0];
   const int64_t NJ = a.N * a.J;
-  const int64_t beg = seg_start[seg];
-  const int64_t end = (seg + 1 < U) ? (int64_t)seg_start[seg + 1] : NJ;
-  const uint64_t key = seg_key[seg];
-  const int j = __builtin_amdgcn_readfirstlane((int)(key >> 32));
-  const int64_t row = (int64_t)(key & 0xFFFFFFFFu);
   const int64_t dm = (int64_t)a.J * a.D;
-  for (int c4 = col; c4 < D4; c4 += 64) {
-    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (grp < S) {
-      for (int64_t p = beg + grp; p < end; p += S) {
-        const int64_t tok = vals[p];
-        acc += *reinterpret_cast<const floatx4*>(a.de + tok * dm + (int64_t)j * a.D + c4 * 4);
-      }
+  const int64_t stride = (int64_t)gridDim.x * 4 * S;
+  auto bounds = [&](int64_t seg, int64_t& beg, int64_t& end, uint64_t& key) {
+    beg = seg_start[seg];
+    end = (seg + 1 < U) ? (int64_t)seg_start[seg + 1] : NJ;
+    key = seg_key[seg];
+  };
+  auto row_src = [&](uint64_t key) -> const float* {
+    return a.de + (int64_t)(key >> 32) * a.D + col * 4;
+  };
+  // the rest of a segment after its first element
+  auto tail = [&](const float* src, int64_t p, int64_t end, floatx4 acc0) -> floatx4 {
+    floatx4 acc1 = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (; p + 1 < end; p += 2) {
+      const int64_t t0 = vals[p], t1 = vals[p + 1];
+      acc0 += *reinterpret_cast<const floatx4*>(src + t0 * dm);
+      acc1 += *reinterpret_cast<const floatx4*>(src + t1 * dm);
     }
-    if (S > 1) {
-      part[wave][lane] = acc;
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      if (grp == 0) {
-        for (int g2 = 1; g2 < S; ++g2) acc += part[wave][g2 * D4 + col];
-      }
-      __builtin_amdgcn_wave_barrier();
+    if (p < end) acc0 += *reinterpret_cast<const floatx4*>(src + (int64_t)vals[p] * dm);
+    return acc0 + acc1;
+  };
+  auto emit = [&](int64_t seg, uint64_t key, floatx4 acc) {
+    const int j = (int)(key >> 32);
+    const int64_t row = (int64_t)(key & 0xFFFFFFFFu);
+    if (MODE == ENGRAM_GRAD_SORTED_SPARSE) {
+      *reinterpret_cast<floatx4*>(a.rows_out + seg * a.D + col * 4) = acc;
+      if (col == 0) a.keys_out[seg] = (int64_t)key;
+    } else {
+      floatx4* dst = reinterpret_cast<floatx4*>(a.dense[j] + row * a.D + col * 4);
+      *dst = *dst + acc;
     }
-    if (grp == 0) {
-      if (MODE == ENGRAM_GRAD_SORTED_SPARSE) {
-        *reinterpret_cast<floatx4*>(a.rows_out + seg * a.D + c4 * 4) = acc;
-      } else {
-        floatx4* dst = reinterpret_cast<floatx4*>(a.dense[j] + row * a.D + c4 * 4);
-        *dst = *dst + acc;
-      }
+  };
+  for (int64_t sa = ((int64_t)blockIdx.x * 4 + wave) * S + grp; sa < U; sa += 2 * stride) {
+    const int64_t sb = sa + stride;
+    const bool hb = sb < U;
+    int64_t ba, ea, bb = 0, eb = 0;
+    uint64_t ka, kb = 0;
+    bounds(sa, ba, ea, ka);
+    if (hb) bounds(sb, bb, eb, kb);
+    const float* srca = row_src(ka);
+    const float* srcb = row_src(kb);
+    const int64_t ta = vals[ba];
+    const int64_t tb = hb ? (int64_t)vals[bb] : 0;
+    floatx4 xa = *reinterpret_cast<const floatx4*>(srca + ta * dm);
+    floatx4 xb = hb ? *reinterpret_cast<const floatx4*>(srcb + tb * dm) : floatx4{};
+    if (ea - ba > 1) xa = tail(srca, ba + 1, ea, xa);
+    emit(sa, ka, xa);
+    if (hb) {
+      if (eb - bb > 1) xb = tail(srcb, bb + 1, eb, xb);
+      emit(sb, kb, xb);
     }
   }
-  if (MODE == ENGRAM_GRAD_SORTED_SPARSE && lane == 0) a.keys_out[seg] = (int64_t)key;
 }
 
 hipError_t launch_sorted_scatter(const ScatterArgs& a, const SortBufs& b, int32_t mode,
@@ -322,8 +344,11 @@ hipError_t launch_sorted_scatter(const ScatterArgs& a, const SortBufs& b, int32_
                      mode == ENGRAM_GRAD_SORTED_SPARSE ? a.count_out : nullptr);
   hipLaunchKernelGGL(seg_write_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.seg_count,
                      b.seg_start, b.seg_key, N, nb);
+  // grid-stride over at most N*J segments, S per wave
   const int64_t max_segs = N * J;
-  const unsigned blocks = (unsigned)((max_segs + 3) / 4);
+  const int S = 64 / (a.D / 4);
+  const int64_t want = (max_segs + 4 * S - 1) / (4 * S);
+  const unsigned blocks = (unsigned)(want < kSegBlocksMax ? want : kSegBlocksMax);
   if (mode == ENGRAM_GRAD_SORTED_SPARSE)
     hipLaunchKernelGGL(seg_reduce_kernel<ENGRAM_GRAD_SORTED_SPARSE>, dim3(blocks), dim3(256), 0, s, a,
                        b.vals[cur], b.seg_start, b.seg_key, b.total);
