@@ -20,6 +20,7 @@ ENGRAM_F32, ENGRAM_BF16 = 0, 1
 ENGRAM_MAX_ORDERS = 4
 ENGRAM_MAX_TABLES = 32
 ENGRAM_FLAG_FUSED_GATHER = 1
+ENGRAM_PLAN_REUSE = 1
 ENGRAM_GRAD_SORTED_SPARSE, ENGRAM_GRAD_SORTED_DENSE, ENGRAM_GRAD_ATOMIC_DENSE = 0, 1, 2
 ENGRAM_OP_FORWARD, ENGRAM_OP_BACKWARD = 0, 1
 
@@ -71,6 +72,7 @@ class engram_compact(ctypes.Structure):
         ("rows_dev", _vp),
         ("inverse_dev", _vp),
         ("ready_event", _vp),
+        ("flags", ctypes.c_uint32),
     ]
 
 

@@ -475,13 +475,18 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
   if (N > 0 && (!canon_map_host || !tokens_host)) return ENGRAM_E_INVALID;
   if (!plan->counts || !plan->uniq_host || !plan->inverse_host) return ENGRAM_E_INVALID;
   if (plan->capacity_rows < 0) return ENGRAM_E_INVALID;
+  if (plan->flags & ~(uint32_t)ENGRAM_PLAN_REUSE) return ENGRAM_E_INVALID;
+  const bool reuse = (plan->flags & ENGRAM_PLAN_REUSE) != 0;
+  if (reuse && (plan->total_rows < 0 || plan->total_rows > plan->capacity_rows))
+    return ENGRAM_E_INVALID;
   if (host_tables) {
     if (!plan->staging_host || !plan->rows_dev || !plan->inverse_dev) return ENGRAM_E_INVALID;
     for (int j = 0; j < J; ++j)
       if (!host_tables[j]) return ENGRAM_E_INVALID;
   }
-  for (int64_t n = 0; n < N; ++n)
-    if (tokens_host[n] < 0 || tokens_host[n] >= cfg->vocab) return ENGRAM_E_INVALID;
+  if (!reuse)
+    for (int64_t n = 0; n < N; ++n)
+      if (tokens_host[n] < 0 || tokens_host[n] >= cfg->vocab) return ENGRAM_E_INVALID;
   const HashArgs ha = make_hash_args(cfg, s);
   const int nthr = (int)std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
   auto parallel = [&](int64_t count, auto&& fn) {
@@ -495,6 +500,18 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
     for (auto& x : th) x.join();
   };
 
+  std::vector<int64_t> base(J + 1, 0);
+  if (reuse) {
+    for (int j = 0; j < J; ++j) {
+      if (plan->counts[j] < 0) return ENGRAM_E_INVALID;
+      base[j + 1] = base[j] + plan->counts[j];
+    }
+    if (base[J] != plan->total_rows) return ENGRAM_E_INVALID;
+    for (int j = 0; j < J; ++j)  // the rows must lie inside their tables
+      for (int64_t u = base[j]; u < base[j + 1]; ++u)
+        if (plan->uniq_host[u] < 0 || plan->uniq_host[u] >= cfg->table_rows[j])
+          return ENGRAM_E_INVALID;
+  } else {
   // 1. indices on the host, same hash as the device kernel
   std::vector<int32_t> idx((size_t)N * J);
   parallel(N, [&](int64_t lo, int64_t hi) {
@@ -520,7 +537,6 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
       u.erase(std::unique(u.begin(), u.end()), u.end());
     }
   });
-  std::vector<int64_t> base(J + 1, 0);
   for (int j = 0; j < J; ++j) base[j + 1] = base[j] + (int64_t)uniq[j].size();
   const int64_t total = base[J];
   if (total > plan->capacity_rows) return ENGRAM_E_INVALID;
@@ -539,26 +555,35 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
         plan->inverse_host[(size_t)n * J + j] = (int32_t)(base[j] + (it - uniq[j].begin()));
       }
   });
+  }  // !reuse
   if (!host_tables) return ENGRAM_OK;
-  // 4. gather the rows into pinned staging, then the async copies
-  const size_t rb = (size_t)s.D * s.es;
-  parallel(total, [&](int64_t lo, int64_t hi) {
-    int j = (int)(std::upper_bound(base.begin(), base.end(), lo) - base.begin()) - 1;
-    for (int64_t u = lo; u < hi; ++u) {
-      while (u >= base[j + 1]) ++j;
-      const int32_t row = plan->uniq_host[u];
-      std::memcpy((uint8_t*)plan->staging_host + (size_t)u * rb,
-                  (const uint8_t*)host_tables[j] + (size_t)row * rb, rb);
-    }
-  });
+  const int64_t total = plan->total_rows;
+  // 4. the inverse map first, then the rows chunk by chunk: gather a chunk
+  //    into pinned staging on the host threads, queue its copy, gather the next
   hipStream_t hs = (hipStream_t)side_stream;
-  if (total > 0 &&
-      hipMemcpyAsync(plan->rows_dev, plan->staging_host, (size_t)total * rb, hipMemcpyHostToDevice,
-                     hs) != hipSuccess)
-    return ENGRAM_E_HIP;
   if (N > 0 && hipMemcpyAsync(plan->inverse_dev, plan->inverse_host, (size_t)N * J * 4,
                               hipMemcpyHostToDevice, hs) != hipSuccess)
     return ENGRAM_E_HIP;
+  const size_t rb = (size_t)s.D * s.es;
+  const int64_t chunk = std::max<int64_t>(1, (int64_t)((32u << 20) / rb));  // ~32 MB of rows
+  for (int64_t c0 = 0; c0 < total; c0 += chunk) {
+    const int64_t c1 = std::min(total, c0 + chunk);
+    parallel(c1 - c0, [&](int64_t lo, int64_t hi) {
+      lo += c0;
+      hi += c0;
+      int j = (int)(std::upper_bound(base.begin(), base.end(), lo) - base.begin()) - 1;
+      for (int64_t u = lo; u < hi; ++u) {
+        while (u >= base[j + 1]) ++j;
+        const int32_t row = plan->uniq_host[u];
+        std::memcpy((uint8_t*)plan->staging_host + (size_t)u * rb,
+                    (const uint8_t*)host_tables[j] + (size_t)row * rb, rb);
+      }
+    });
+    if (hipMemcpyAsync((uint8_t*)plan->rows_dev + (size_t)c0 * rb,
+                       (const uint8_t*)plan->staging_host + (size_t)c0 * rb,
+                       (size_t)(c1 - c0) * rb, hipMemcpyHostToDevice, hs) != hipSuccess)
+      return ENGRAM_E_HIP;
+  }
   if (plan->ready_event && hipEventRecord((hipEvent_t)plan->ready_event, hs) != hipSuccess)
     return ENGRAM_E_HIP;
   return ENGRAM_OK;

@@ -132,7 +132,16 @@ typedef struct {
   int32_t* inverse_dev;   /* device [N][J]: async-copy destination of inverse_host */
   void* ready_event;      /* hipEvent_t recorded on the side stream after the copies
                              (engram_forward waits on it when non-NULL) */
+  uint32_t flags;         /* ENGRAM_PLAN_* bits, 0 for the defaults */
 } engram_compact;
+
+/* engram_compact.flags */
+enum {
+  /* counts, uniq_host, inverse_host and total_rows already hold the plan of
+   * these tokens (from an earlier call): skip hashing and sorting, only
+   * gather and copy.  Lets the indices be planned ahead of time. */
+  ENGRAM_PLAN_REUSE = 1u
+};
 
 /* Table-gradient output of engram_backward_table_grad(). */
 enum {
@@ -209,8 +218,11 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
  * compact inverse map (plan->inverse_host), and -- when host_tables is not
  * NULL -- gathers the rows from the host tables into plan->staging_host and
  * queues hipMemcpyAsync of rows and inverse map to the device buffers on
- * side_stream, then records plan->ready_event there.  Returns when the host
- * work is done; the copies run asynchronously.
+ * side_stream, then records plan->ready_event there.  The rows are gathered
+ * and queued in chunks, so the copy of one chunk runs while the next is
+ * gathered.  Returns when the host work is done; the copies run
+ * asynchronously.  With ENGRAM_PLAN_REUSE in plan->flags the plan fields are
+ * taken as given (a plan-only call made them) and only gather and copy run.
  *   canon_map_host: host [vocab]; tokens_host: host [B][T];
  *   host_tables: NULL (plan only) or host [J] pointers to [M_j][D] dtype
  *   (pinned memory makes the copy a true async DMA).

@@ -58,3 +58,45 @@ def test_compact_forward_bit_identical(torch, oracle_lib, name, B, T):
     assert np.array_equal(uniq[: plan.total_rows], u_ref)
     base = np.concatenate([[0], np.cumsum(c_ref)[:-1]]).astype(np.int32)
     assert np.array_equal(bufs["idx"].cpu().numpy(), inv_ref + base[None, :])
+
+
+def test_plan_ahead_then_reuse(torch, oracle_lib):
+    """Indices planned ahead (no host tables), then gather + copy only
+    (ENGRAM_PLAN_REUSE): same compact forward as the HBM forward."""
+    import hashed_gram_embedding_canon_amd as eg
+    wl = synth.get_workload("small").with_shape(2, 2048)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp)
+    y_ref = dp.forward()
+    N, J = dp.N, wl.J
+    cap = N * J
+    counts = np.zeros(J, np.int64)
+    uniq = np.zeros(cap, np.int32)
+    inv_h = torch.empty(N, J, dtype=torch.int32, pin_memory=True)
+    staging = torch.empty(cap * wl.dim * 2, dtype=torch.uint8, pin_memory=True)
+    rows_dev = torch.empty(cap * wl.dim * 2, dtype=torch.uint8, device="cuda")
+    inv_dev = torch.empty(N, J, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    ev.record()
+    plan = eg.engram_compact()
+    plan.capacity_rows = cap
+    plan.counts, plan.uniq_host = counts.ctypes.data, uniq.ctypes.data
+    plan.inverse_host, plan.staging_host = inv_h.data_ptr(), staging.data_ptr()
+    plan.rows_dev, plan.inverse_dev = rows_dev.data_ptr(), inv_dev.data_ptr()
+    plan.ready_event = ev.cuda_event
+    eg.engram_prefetch_plan(dp.cfg, inp.canon_map, inp.tokens, B=dp.B, T=dp.T, host_tables=None,
+                            plan=plan, side_stream=side)
+    assert plan.total_rows == int(counts.sum()) > 0
+    plan.flags = eg.ENGRAM_PLAN_REUSE
+    host_tables = [inp.table(j) for j in range(J)]
+    eg.engram_prefetch_plan(dp.cfg, inp.canon_map, inp.tokens, B=dp.B, T=dp.T,
+                            host_tables=host_tables, plan=plan, side_stream=side)
+    y = dp.forward(compact=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    # a reused plan whose rows fall outside the tables is rejected on the host
+    uniq[0] = int(inp.table_rows[0])
+    with pytest.raises(eg.EngramError):
+        eg.engram_prefetch_plan(dp.cfg, inp.canon_map, inp.tokens, B=dp.B, T=dp.T,
+                                host_tables=host_tables, plan=plan, side_stream=side)
