@@ -330,6 +330,9 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     ga.F = 2 * s.d;
     ga.K = s.d_mem;
     ga.group_m = 4;
+    // last token tiles first: the gather wrote them last, so more of their e
+    // rows are still in the Infinity Cache (measured ~1 % faster)
+    ga.reverse_m = 1;
     ga.stage_bytes = kFwdStageBytes;
     ga.d = s.d;
     ga.io_dtype = s.dtype;

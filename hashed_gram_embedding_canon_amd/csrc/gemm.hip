@@ -222,9 +222,11 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int in_g = slot - grp * per_group;
   const int tf = in_g / gm;
   const int tm_local = in_g - tf * gm;
-  const int64_t tm = (int64_t)(grp * gm + tm_local) * 8 + xcd;
+  const int64_t tm_fwd = (int64_t)(grp * gm + tm_local) * 8 + xcd;
   const int64_t tiles_m = (g.M + kBT - 1) / kBT;
-  if (tm >= tiles_m) return;
+  if (tm_fwd >= tiles_m) return;
+  // token tiles walked last to first when asked (the newest rows of B first)
+  const int64_t tm = g.reverse_m ? tiles_m - 1 - tm_fwd : tm_fwd;
   const int f0 = tf * kBF;
   const int64_t m0 = tm * kBT;
 

@@ -32,6 +32,7 @@ struct GemmArgs {
   int64_t M;
   int32_t F, K;
   int32_t group_m;     // token tiles walked per f-tile inside one XCD group
+  int32_t reverse_m;   // nonzero: token tiles in descending order
   int32_t stage_bytes; // bytes of K per LDS stage: 64 (4-deep ring) or 128 (2-deep)
   // EPI_KV
   int32_t d;           // hidden width: f < d is the key, f >= d the value
