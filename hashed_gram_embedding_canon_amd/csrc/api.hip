@@ -29,6 +29,9 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // latency (fewer cycles per tile) but runs at a lower clock under the power
 // limit and measured slower.
 constexpr int32_t kFwdStageBytes = 128;
+#ifndef ENGRAM_GEMM_PERSISTENT
+#define ENGRAM_GEMM_PERSISTENT 1
+#endif
 constexpr int32_t kBwdStageBytes = 128;
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -333,6 +336,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     // last token tiles first: the gather wrote them last, so more of their e
     // rows are still in the Infinity Cache (measured ~1 % faster)
     ga.reverse_m = 1;
+    ga.persistent = ENGRAM_GEMM_PERSISTENT;
     ga.stage_bytes = kFwdStageBytes;
     ga.d = s.d;
     ga.io_dtype = s.dtype;
@@ -449,6 +453,7 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
       ga.K = 2 * s.d;
       ga.group_m = 4;
       ga.stage_bytes = kBwdStageBytes;
+      ga.persistent = ENGRAM_GEMM_PERSISTENT;
       ga.c_out = w.de;
       Timed tm("de_gemm", hs);
       if (launch_gemm(bf ? GEMM_F16 : GEMM_F32, EPI_STORE_F32, ga, hs) != hipSuccess)

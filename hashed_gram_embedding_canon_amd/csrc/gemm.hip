@@ -26,6 +26,7 @@
 // v_mfma_f32_32x32x2f32 per 16-byte fragment.  Workgroup ids reach the 8
 // XCDs round-robin; the id -> tile map keeps the f-tiles of a small group of
 // token tiles on one XCD so they share rows and weight slabs in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -212,9 +213,13 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   int32_t* const sIdxOrRed = sIdx;
   __shared__ const uint8_t* sTab[GATHER ? kGatherMaxJ : 1];
 
-  // ---- workgroup id -> (token tile, feature tile), XCD-grouped
+  // ---- workgroup id -> (token tile, feature tile), XCD-grouped.  Slot s of
+  // XCD x (workgroups x, x+8, ...) walks the tiles of that XCD; a grid of
+  // fewer workgroups than slots makes each workgroup loop over slots
+  // s, s + gridDim/8, ... (persistent: no per-tile dispatch gap).
   const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
+  const int slot_step = gridDim.x >> 3;
+  for (int slot = blockIdx.x >> 3; slot < g.slots_per_xcd; slot += slot_step) {
   const int tiles_f = g.F / kBF;
   const int gm = g.group_m;
   const int per_group = gm * tiles_f;
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int tm_local = in_g - tf * gm;
   const int64_t tm_fwd = (int64_t)(grp * gm + tm_local) * 8 + xcd;
   const int64_t tiles_m = (g.M + kBT - 1) / kBT;
-  if (tm_fwd >= tiles_m) return;
+  if (tm_fwd >= tiles_m) continue;  // uniform over the workgroup
   // token tiles walked last to first when asked (the newest rows of B first)
   const int64_t tm = g.reverse_m ? tiles_m - 1 - tm_fwd : tm_fwd;
   const int f0 = tf * kBF;
@@ -839,15 +844,33 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       }
     }
   }
+  // the next tile reuses LDS: every wave's LDS reads of this one are done
+  // (its global stores may still be in flight)
+  ENGRAM_WAIT_VM_LDS(63);
+  ENGRAM_BARRIER();
+  }  // slot loop
 }
 
 template <int GT, int EPI, bool GATHER>
-static hipError_t launch_one(const GemmArgs& g, hipStream_t s) {
+static hipError_t launch_one(const GemmArgs& g0, hipStream_t s) {
+  GemmArgs g = g0;
   const int64_t tiles_m = (g.M + kBT - 1) / kBT;
   const int tiles_f = g.F / kBF;
   const int64_t tiles_m_x = (tiles_m + 7) / 8;
   const int64_t groups = (tiles_m_x + g.group_m - 1) / g.group_m;
-  const int64_t blocks = 8 * groups * g.group_m * tiles_f;
+  const int64_t slots = groups * g.group_m * tiles_f;  // per XCD
+  if (slots >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  g.slots_per_xcd = (int32_t)slots;
+  // persistent: one workgroup per CU (the LDS use allows no second one), 8 XCDs
+  int64_t per_xcd = slots;
+  if (g.persistent) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    per_xcd = std::min<int64_t>(slots, std::max(1, cus / 8));
+  }
+  const int64_t blocks = 8 * per_xcd;
   if (g.stage_bytes == 128)
     hipLaunchKernelGGL((gemm_kernel<GT, EPI, GATHER, 128>), dim3((unsigned)blocks), dim3(kNT), 0, s, g);
   else
