@@ -15,7 +15,7 @@
 
 namespace engram {
 
-constexpr int kGcTokens = 64;   // R
+constexpr int kGcTokens = 64;   // R (32 and 128 measured slower)
 constexpr int kMaxTaps = 8;
 
 // raw 16 bytes of VEC features (8 bf16 or 4 fp32), widened at use
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   // v rows stream through a ring of PD tokens loaded ahead (each wave keeps
   // PD 1 KB loads in flight; HBM latency, not bandwidth, bounds a shallower
   // ring at this occupancy)
-  constexpr int PD = 4;
+  constexpr int PD = 4;  // 8 measured slower (fewer waves fit)
   u32x4 ring[PD];
 #pragma unroll
   for (int u = 0; u < PD; ++u)
