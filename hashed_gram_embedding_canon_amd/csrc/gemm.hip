@@ -684,6 +684,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       }
     } else {
       // value tile: accumulators -> bf16 rows in LDS -> whole rows to v
+      // (8-byte stores straight from the accumulators measured 3 % slower)
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
         const int t = (wt * TB + b) * 32 + l32;
