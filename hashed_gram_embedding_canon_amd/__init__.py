@@ -19,6 +19,7 @@ ENGRAM_OK, ENGRAM_E_INVALID, ENGRAM_E_UNSUPPORTED, ENGRAM_E_WORKSPACE, ENGRAM_E_
 ENGRAM_F32, ENGRAM_BF16 = 0, 1
 ENGRAM_MAX_ORDERS = 4
 ENGRAM_MAX_TABLES = 32
+ENGRAM_MAX_BRANCHES = 8
 ENGRAM_FLAG_FUSED_GATHER = 1
 ENGRAM_PLAN_REUSE = 1
 ENGRAM_GRAD_SORTED_SPARSE, ENGRAM_GRAD_SORTED_DENSE, ENGRAM_GRAD_ATOMIC_DENSE = 0, 1, 2
@@ -43,6 +44,7 @@ class engram_config(ctypes.Structure):
         ("table_rows", _vp),
         ("multipliers", _vp),
         ("flags", ctypes.c_uint32),
+        ("branches", ctypes.c_int32),
     ]
 
 
@@ -163,7 +165,7 @@ class Config:
     """engram_config plus the host arrays it points at (kept alive here)."""
 
     def __init__(self, *, vocab, canon_vocab, orders, heads, dim, hidden, table_rows, multipliers,
-                 dtype=ENGRAM_BF16, conv_kernel=4, rms_eps=1e-6, pad_id=0, flags=0):
+                 dtype=ENGRAM_BF16, conv_kernel=4, rms_eps=1e-6, pad_id=0, flags=0, branches=1):
         import numpy as np
         self.table_rows = np.ascontiguousarray(table_rows, dtype=np.int64)
         self.multipliers = np.ascontiguousarray(multipliers, dtype=np.uint64)
@@ -178,7 +180,9 @@ class Config:
         c.table_rows = self.table_rows.ctypes.data
         c.multipliers = self.multipliers.ctypes.data
         c.flags = int(flags)
+        c.branches = int(branches)
         self.c = c
+        self.branches = max(1, int(branches))
         self.J = len(orders) * int(heads)
         self.d_mem = self.J * int(dim)
 

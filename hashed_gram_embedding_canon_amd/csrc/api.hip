@@ -21,6 +21,7 @@ struct Shape {
   int32_t dtype;
   int key_bits;
   uint32_t flags;
+  int M;  // branches
 };
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -54,6 +55,7 @@ engram_status check_config(const engram_config* c, Shape* s) {
   if (c->conv_kernel < 1 || c->conv_kernel > 8) return ENGRAM_E_UNSUPPORTED;
   if (!(c->rms_eps >= 0.f)) return ENGRAM_E_INVALID;
   if (c->flags & ~(uint32_t)ENGRAM_FLAG_FUSED_GATHER) return ENGRAM_E_INVALID;
+  if (c->branches < 0 || c->branches > ENGRAM_MAX_BRANCHES) return ENGRAM_E_INVALID;
   const int es = (int)dtype_size(c->dtype);
   if ((c->dim * es) % 16 != 0) return ENGRAM_E_UNSUPPORTED;
   const int d_mem = J * c->dim;
@@ -77,6 +79,7 @@ engram_status check_config(const engram_config* c, Shape* s) {
   s->dtype = c->dtype;
   s->key_bits = bits;
   s->flags = c->flags;
+  s->M = c->branches > 0 ? c->branches : 1;
   return ENGRAM_OK;
 }
 
@@ -151,7 +154,7 @@ bool fused_gather(const Shape& s, const engram_saved* sv) {
   if (sv && sv->e) return false;
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
-  ga.F = 2 * s.d;
+  ga.F = (s.M + 1) * s.d;
   ga.K = s.d_mem;
   ga.group_m = 1;
   ga.stage_bytes = kFwdStageBytes;
@@ -177,7 +180,7 @@ size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out,
   else
     w.e = nullptr;
   w.v = (sv && sv->v) ? (uint8_t*)sv->v : take((size_t)N * s.d * s.es);
-  w.partials = (float*)take((size_t)N * (s.d / kGemmBF) * 3 * 4);
+  w.partials = (float*)take((size_t)s.M * N * (s.d / kGemmBF) * 3 * 4);
   if (out) *out = w;
   return off;
 }
@@ -330,7 +333,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
       for (int j = 0; j < s.J; ++j) ga.tables[j] = g.base[j];
     }
     ga.M = N;
-    ga.F = 2 * s.d;
+    ga.F = (s.M + 1) * s.d;
     ga.K = s.d_mem;
     ga.group_m = 4;
     // last token tiles first: the gather wrote them last, so more of their e
@@ -339,6 +342,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     ga.persistent = ENGRAM_GEMM_PERSISTENT;
     ga.stage_bytes = kFwdStageBytes;
     ga.d = s.d;
+    ga.branches = s.M;
     ga.io_dtype = s.dtype;
     ga.h = (const uint8_t*)hidden;
     ga.gamma_q = p->gamma_q;
@@ -357,6 +361,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     gc.d = s.d;
     gc.taps = s.taps;
     gc.nkt = s.d / kGemmBF;
+    gc.branches = s.M;
     gc.io_dtype = s.dtype;
     gc.eps = cfg->rms_eps;
     gc.partials = w.partials;
@@ -380,6 +385,7 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
   if (!p || !out || B < 0 || T < 0 || T > INT32_MAX || B > 65535) return ENGRAM_E_INVALID;
   if (s.d / 4 > 1024) return ENGRAM_E_UNSUPPORTED;
   if (s.D > 256) return ENGRAM_E_UNSUPPORTED;  // one 16-byte piece per lane of a row
+  if (s.M > 1) return ENGRAM_E_UNSUPPORTED;    // the table-gradient backward has one branch
   if (out->mode < ENGRAM_GRAD_SORTED_SPARSE || out->mode > ENGRAM_GRAD_ATOMIC_DENSE)
     return ENGRAM_E_INVALID;
   const int64_t N = B * T;

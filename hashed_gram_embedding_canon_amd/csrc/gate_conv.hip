@@ -61,6 +61,10 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   const int64_t t0 = (int64_t)blockIdx.x * R;
   const int nh = TAPS - 1;
   const int d = a.d;
+  // branch blockIdx.z: its own partial sums, output and stats; v is shared
+  const int64_t N = a.B * a.T;
+  const float* __restrict__ partials = a.partials + blockIdx.z * N * a.nkt * 3;
+  float* const stats = a.stats ? a.stats + blockIdx.z * N * 4 : nullptr;
   const float inv_d = 1.0f / (float)d;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
 
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
     const int64_t t = t0 - nh + i;
     float al = 0.f;
     if (t >= 0 && t < a.T) {
-      const float* p = a.partials + (b * a.T + t) * a.nkt * 3;
+      const float* p = partials + (b * a.T + t) * a.nkt * 3;
       float skk = 0.f, shk = 0.f, shh = 0.f;
       for (int q = 0; q < a.nkt; ++q) {
         skk += p[3 * q];
@@ -80,8 +84,8 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
       const float rk = 1.0f / sqrtf(skk * inv_d + a.eps);
       const float s = shk * rq * rk * inv_sqrt_d;
       al = 1.0f / (1.0f + expf(-s));
-      if (a.stats && t >= t0) {
-        float* st = a.stats + (b * a.T + t) * 4;
+      if (stats && t >= t0) {
+        float* st = stats + (b * a.T + t) * 4;
         *reinterpret_cast<floatx4*>(st) = floatx4{al, rq, rk, shk};
       }
     }
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   const int64_t tbeg = t0 - nh > 0 ? t0 - nh : 0;
   const int64_t tend = (t0 + R < a.T) ? t0 + R : a.T;
   const uint8_t* __restrict__ vsrc = a.v;
-  uint8_t* __restrict__ ydst = a.y;
+  uint8_t* __restrict__ ydst = a.y + blockIdx.z * N * d * (BF16 ? 2 : 4);
   const int64_t row0 = b * a.T;
   // v rows stream through a ring of PD tokens loaded ahead (each wave keeps
   // PD 1 KB loads in flight; HBM latency, not bandwidth, bounds a shallower
@@ -156,7 +160,8 @@ hipError_t launch_gate_conv(const GateConvArgs& a, hipStream_t s) {
   const int vec = bf ? 8 : 4;
   int threads = (a.d / vec + 63) / 64 * 64;
   if (threads > 1024) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((a.T + kGcTokens - 1) / kGcTokens), (unsigned)a.B);
+  dim3 grid((unsigned)((a.T + kGcTokens - 1) / kGcTokens), (unsigned)a.B,
+            (unsigned)(a.branches > 0 ? a.branches : 1));
   switch (a.taps) {
 #define ENGRAM_TAPS_CASE(K)                                                                      \
   case K:                                                                                        \

@@ -234,6 +234,21 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int64_t tm = g.reverse_m ? tiles_m - 1 - tm_fwd : tm_fwd;
   const int f0 = tf * kBF;
   const int64_t m0 = tm * kBT;
+  // EPI_KV output features: the keys of `branches` branches (d each), then v.
+  // A feature tile lies inside one branch key or inside v (d % 256 == 0);
+  // fk is its first feature there.  h, gamma, k and the partial sums of a
+  // branch sit branch-major ([branch][M][d], [branch][d], [branch][M][d/256][3]).
+  const int nbr = g.branches > 0 ? g.branches : 1;
+  const bool key_tile = EPI == EPI_KV && f0 < nbr * g.d;
+  const int br = key_tile ? f0 / g.d : 0;
+  const int fk = EPI != EPI_KV ? 0 : (key_tile ? f0 - br * g.d : f0 - nbr * g.d);
+  constexpr int HSZ = GT == GEMM_F32 ? 4 : 2;  // bytes per element of h, k, v
+  const int64_t bstride = g.M * (int64_t)g.d;   // elements from one branch to the next
+  const uint8_t* const hB = EPI == EPI_KV ? g.h + br * bstride * HSZ : nullptr;
+  const float* const gqB = g.gamma_q ? g.gamma_q + br * g.d : nullptr;
+  const float* const gkB = g.gamma_k ? g.gamma_k + br * g.d : nullptr;
+  float* const partB = EPI == EPI_KV ? g.partials + br * g.M * (g.d / kBF) * 3 : nullptr;
+  uint8_t* const koutB = g.k_out ? g.k_out + br * bstride * HSZ : nullptr;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -328,7 +343,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // (l%32) ^ (t%32) at slot l%32 of the row.  A part is 2*NL row pairs per
   // wave, one per load slot.
   constexpr bool kHOverlap = kBf16Epi;
-  const bool hov = kHOverlap && f0 < g.d;
+  const bool hov = kHOverlap && key_tile;
   auto h_t0 = [&](int X, int p) __attribute__((always_inline)) {
     if constexpr (NS == 4)  // 32 pairs: part X = 2u + w
       return ((X & 1) << 7) | ((X >> 1) << 6) | (p << 1);
@@ -341,7 +356,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     const int64_t tc = m0 + t < g.M ? t : g.M - 1 - m0;
     return (uint32_t)((tc * g.d + c16 * 8) * 2);
   };
-  const void* const hbase = kBf16Epi ? uniform_ptr(g.h + (m0 * g.d + f0) * 2) : nullptr;
+  const void* const hbase = kBf16Epi ? uniform_ptr(hB + (m0 * g.d + fk) * 2) : nullptr;
 
   // Load slot j of a stage (j = 2i + op): piece i of operand A (op 0) or B
   // (op 1) into the stage buffer at LDS address la (A) / la + kTS (B).
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     // XOR-swizzled by (token & 31).  h is brought in and v goes out as whole
     // rows (a wave moves two 512-byte rows per instruction).
     const int d = g.d;
-    if (f0 < d) {
+    if (key_tile) {
       if (hov) {
         // the last part of h (the others went out in the last K stages)
 #pragma unroll
@@ -567,15 +582,15 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
           const int c16 = (lane & 31) ^ (t & 31);  // logical piece landing at slot lane&31
           int64_t m = m0 + t;
           m = m < g.M ? m : g.M - 1;
-          load_lds16(g.h + ((m * d + f0) + c16 * 8) * 2, lds_addr(trow(t0)));
+          load_lds16(hB + ((m * d + fk) + c16 * 8) * 2, lds_addr(trow(t0)));
         }
       }
       float* red = reinterpret_cast<float*>(sIdxOrRed);  // [2 wf][2 wt][TB][32][3]
       float* const sg = red + kRedFloats;                 // [256] gamma_q * gamma_k of the tile
       const bool has_gamma = g.gamma_q || g.gamma_k;
       if (has_gamma) {
-        const int f = f0 + tid;
-        sg[tid] = (g.gamma_q ? g.gamma_q[f] : 1.f) * (g.gamma_k ? g.gamma_k[f] : 1.f);
+        const int f = fk + tid;
+        sg[tid] = (gqB ? gqB[f] : 1.f) * (gkB ? gkB[f] : 1.f);
       }
       if (hov) {
         // parts of the first two token blocks landed (at most the last 16
@@ -629,8 +644,8 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
               }
               if constexpr (SK) {
                 if (m < g.M) {
-                  const int f = f0 + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
-                  *reinterpret_cast<u32x2*>(g.k_out + (m * d + f) * 2) =
+                  const int f = fk + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
+                  *reinterpret_cast<u32x2*>(koutB + (m * d + f) * 2) =
                       u32x2{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
                 }
               }
@@ -676,7 +691,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         if (m < g.M) {
           const float* p0 = red + (((0 + wt2) * TB + b) * 32 + l) * 3;
           const float* p1 = red + (((2 + wt2) * TB + b) * 32 + l) * 3;
-          float* out = g.partials + (m * (d / kBF) + tf) * 3;
+          float* out = partB + (m * (d / kBF) + fk / kBF) * 3;
           out[0] = p0[0] + p1[0];
           out[1] = p0[1] + p1[1];
           out[2] = p0[2] + p1[2];
@@ -711,7 +726,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         const int64_t m = m0 + t;
         if (m < g.M) {
           const u32x4 x = *reinterpret_cast<const u32x4*>(trow(t) + ((c16 ^ (t & 31)) << 4));
-          *reinterpret_cast<u32x4*>(g.v_out + (m * d + (f0 - d) + c16 * 8) * 2) = x;
+          *reinterpret_cast<u32x4*>(g.v_out + (m * d + fk + c16 * 8) * 2) = x;
         }
       }
     }
@@ -719,7 +734,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     // fp32 (small shapes): straight from the accumulators
     const int io = g.io_dtype;
     const int d = g.d;
-    if (f0 < d) {
+    if (key_tile) {
       // Key tile: per-token partial sums of the gate straight from the
       // accumulators (each lane owns one token and 64 of this wave's 128
       // features), h of the next token block loaded while this one is summed.
@@ -738,7 +753,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
             // element (m, f) of h sits at byte (m*d + f) * element size, and the
             // element size is HW bytes (4 elements = HW words)
             dst[a * 4 + q] = *reinterpret_cast<const hraw_t*>(
-                g.h + (m * d + f0 + (wf * FB + a) * 32 + q * 8 + lhalf * 4) * (int64_t)HW);
+                hB + (m * d + fk + (wf * FB + a) * 32 + q * 8 + lhalf * 4) * (int64_t)HW);
       };
       // bf16 h is prefetched one token block ahead; fp32 h (twice the
       // registers) is loaded per block
@@ -758,10 +773,10 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         for (int a = 0; a < FB; ++a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int f = f0 + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
+            const int f = fk + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
             floatx4 gg = floatx4{1.f, 1.f, 1.f, 1.f};
-            if (g.gamma_q) gg *= *reinterpret_cast<const floatx4*>(g.gamma_q + f);
-            if (g.gamma_k) gg *= *reinterpret_cast<const floatx4*>(g.gamma_k + f);
+            if (gqB) gg *= *reinterpret_cast<const floatx4*>(gqB + f);
+            if (gkB) gg *= *reinterpret_cast<const floatx4*>(gkB + f);
             const hraw_t hr = hb[b & 1][a * 4 + q];
             floatx4 hx;
             if constexpr (GT == GEMM_BF16) {
@@ -779,7 +794,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
               shk += gg[r] * hx[r] * kv[r];
               shh += hx[r] * hx[r];
             }
-            if (g.k_out && valid) store4(g.k_out, m * d + f, io, kv[0], kv[1], kv[2], kv[3]);
+            if (koutB && valid) store4(koutB, m * d + f, io, kv[0], kv[1], kv[2], kv[3]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -801,7 +816,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         if (m < g.M) {
           const float* p0 = red + (((0 + wt2) * TB + b) * 32 + l) * 3;
           const float* p1 = red + (((2 + wt2) * TB + b) * 32 + l) * 3;
-          float* out = g.partials + (m * (d / kBF) + tf) * 3;
+          float* out = partB + (m * (d / kBF) + fk / kBF) * 3;
           out[0] = p0[0] + p1[0];
           out[1] = p0[1] + p1[1];
           out[2] = p0[2] + p1[2];
@@ -818,7 +833,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
           for (int a = 0; a < FB; ++a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int f = f0 - d + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
+              const int f = fk + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
               store4(g.v_out, m * d + f, io, acc_read(acc[a][b][q * 4]),
                      acc_read(acc[a][b][q * 4 + 1]), acc_read(acc[a][b][q * 4 + 2]),
                      acc_read(acc[a][b][q * 4 + 3]));

@@ -37,13 +37,14 @@ struct GemmArgs {
   int32_t slots_per_xcd;  // set by the launcher
   int32_t stage_bytes; // bytes of K per LDS stage: 64 (4-deep ring) or 128 (2-deep)
   // EPI_KV
-  int32_t d;           // hidden width: f < d is the key, f >= d the value
+  int32_t d;           // hidden width: f < branches*d are the branch keys, the rest v
+  int32_t branches;    // keys of this many branches (0 or 1: one)
   int32_t io_dtype;    // ENGRAM_F32 / ENGRAM_BF16 of h, k_out, v_out
-  const uint8_t* h;    // [M][d]
+  const uint8_t* h;    // [branches][M][d]
   const float* gamma_q;
   const float* gamma_k;
-  float* partials;     // [M][d/BF][3]: sum k^2, sum g_q g_k h k, sum h^2
-  uint8_t* k_out;      // [M][d] or null
+  float* partials;     // [branches][M][d/BF][3]: sum k^2, sum g_q g_k h k, sum h^2
+  uint8_t* k_out;      // [branches][M][d] or null
   uint8_t* v_out;      // [M][d]
   // EPI_STORE_F32
   float* c_out;        // [M][F]
@@ -61,12 +62,13 @@ hipError_t launch_gemm(GemmType type, GemmEpilogue epi, const GemmArgs& g, hipSt
 struct GateConvArgs {
   int64_t B, T;
   int32_t d, taps, nkt, io_dtype;
+  int32_t branches;       // gates and outputs of this many branches (grid.z); v is shared
   float eps;
-  const float* partials;  // [N][nkt][3]
+  const float* partials;  // [branches][N][nkt][3]
   const uint8_t* v;       // [N][d]
   const float* conv_w;    // [d][taps]
-  uint8_t* y;             // [N][d]
-  float* stats;           // [N][4] or null
+  uint8_t* y;             // [branches][N][d]
+  float* stats;           // [branches][N][4] or null
 };
 hipError_t launch_gate_conv(const GateConvArgs& a, hipStream_t s);
 

@@ -94,24 +94,31 @@ typedef struct {
   const int64_t* table_rows;   /* host [J]: M_j, 1 <= M_j < 2^31 (prime by design) */
   const uint64_t* multipliers; /* host [J][max order]: m_{j,i} multiplies c_{t-i} */
   uint32_t flags;              /* ENGRAM_FLAG_* bits, 0 for the defaults */
+  int32_t branches;            /* M residual branches sharing the tables and W_V, each with
+                                  its own W_K, hidden state, gate and output ("DeepSeek AI
+                                  II", section "DeepSeek Engram", multi-branch integration);
+                                  0 or 1 = one branch, at most ENGRAM_MAX_BRANCHES */
 } engram_config;
+
+#define ENGRAM_MAX_BRANCHES 8
 
 /* Learned parameters (device pointers). */
 typedef struct {
   const int32_t* canon_map;               /* [vocab] raw id -> canonical id */
   const void* tables[ENGRAM_MAX_TABLES];  /* table j: [M_j][D] dtype */
-  const void* w_kv;       /* [2d][d_mem] dtype: rows 0..d-1 are W_K, rows d..2d-1 are W_V */
-  const float* gamma_q;   /* [d] RMSNorm scale of the query, NULL = all ones */
-  const float* gamma_k;   /* [d] RMSNorm scale of the key, NULL = all ones */
+  const void* w_kv;       /* [(M+1)d][d_mem] dtype: rows m*d..(m+1)*d-1 are W_K of branch m,
+                             the last d rows W_V (M = branches; [2d][d_mem] for one branch) */
+  const float* gamma_q;   /* [M][d] RMSNorm scale of each branch's query, NULL = all ones */
+  const float* gamma_k;   /* [M][d] RMSNorm scale of each branch's key, NULL = all ones */
   const float* conv_w;    /* [d][conv_kernel] fp32, tap i multiplies vt_{t-i} */
 } engram_params;
 
 /* Optional forward outputs (device).  NULL members are not written.  The
- * table-gradient backward needs idx, stats, k and v. */
+ * table-gradient backward needs idx, stats, k and v.  M = branches. */
 typedef struct {
   int32_t* idx;   /* [N][J] row indices idx_j(t) (table-local; compact-local in compact mode) */
-  float* stats;   /* [N][4]: alpha_t, rq_t, rk_t, <g_q h_t, g_k k_t> (the last without rq, rk) */
-  void* k;        /* [N][d] dtype */
+  float* stats;   /* [M][N][4]: alpha_t, rq_t, rk_t, <g_q h_t, g_k k_t> (the last without rq, rk) */
+  void* k;        /* [M][N][d] dtype */
   void* v;        /* [N][d] dtype */
   void* e;        /* [N][d_mem] dtype, the gathered memory vectors */
 } engram_saved;
@@ -182,8 +189,9 @@ engram_status engram_hash_indices(const engram_config* cfg, const int32_t* canon
  * RMSNorm-dot-sigmoid gate, gated value, causal depthwise conv + SiLU +
  * residual ("DeepSeek AI II", section "DeepSeek Engram": retrieval, then
  * context-aware gating and the short causal convolution).
- *   tokens: device [B][T] (ignored in compact mode); hidden: device [B][T][d]
- *   dtype; y: device [B][T][d] dtype output (Y only; the caller adds it to H);
+ *   tokens: device [B][T] (ignored in compact mode); hidden: device [M][B][T][d]
+ *   dtype, the hidden state of each branch (M = branches); y: device
+ *   [M][B][T][d] dtype output, each branch's Y (the caller adds it to its H);
  *   saved: NULL or buffers to keep (see engram_saved);
  *   compact: NULL, or the plan of engram_prefetch_plan(): rows are read from
  *   compact->rows_dev through compact->inverse_dev instead of params->tables;

@@ -283,3 +283,8 @@ def _widen(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     return a.astype(np.float64)
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    """bf16 bits (uint16) or fp32 values as float64, exactly."""
+    return _widen(a)

@@ -196,6 +196,22 @@ class Inputs:
         return self._get("h", lambda: normal_stream(
             seed_of(wl.cfg, S_HIDDEN), wl.B * wl.T * wl.hidden, 1.0, wl.dtype).reshape(wl.B, wl.T, wl.hidden))
 
+    def w_k_branch(self, m: int) -> np.ndarray:  # [d, d_mem] W_K of branch m (branch 0 = w_k)
+        if m == 0:
+            return self.w_k
+        wl = self.wl
+        n = wl.hidden * wl.d_mem
+        return self._get(("wk", m), lambda: normal_stream(
+            seed_of(wl.cfg, S_WK), n, wl.w_std, wl.dtype, offset=m * n).reshape(wl.hidden, wl.d_mem))
+
+    def hidden_branch(self, m: int) -> np.ndarray:  # [B, T, d] of branch m (branch 0 = hidden)
+        if m == 0:
+            return self.hidden
+        wl = self.wl
+        n = wl.B * wl.T * wl.hidden
+        return self._get(("h", m), lambda: normal_stream(
+            seed_of(wl.cfg, S_HIDDEN), n, 1.0, wl.dtype, offset=m * n).reshape(wl.B, wl.T, wl.hidden))
+
     @property
     def conv_w(self) -> np.ndarray:  # float32 [d, taps]; tap i multiplies position t-i
         wl = self.wl

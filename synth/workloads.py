@@ -28,6 +28,7 @@ class Workload:
     conv_std: float = 0.5
     rms_eps: float = 1e-6
     pad_id: int = 0
+    branches: int = 1     # M residual branches (own W_K and hidden state each)
     note: str = field(default="", compare=False)
 
     @property

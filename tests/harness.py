@@ -42,15 +42,21 @@ class DeviceProblem:
                              heads=wl.heads, dim=wl.dim, hidden=wl.hidden,
                              table_rows=inp.table_rows, multipliers=inp.multipliers,
                              dtype=self.dtype_code, conv_kernel=wl.taps, rms_eps=wl.rms_eps,
-                             pad_id=wl.pad_id, flags=flags)
+                             pad_id=wl.pad_id, flags=flags, branches=wl.branches)
         self.tokens_host = np.ascontiguousarray(inp.tokens if tokens is None else tokens, dtype=np.int32)
         self.B, self.T = self.tokens_host.shape
         self.tokens = to_dev(self.tokens_host, device)
         self.canon = to_dev(inp.canon_map, device)
         self.tables = [to_dev(inp.table(j), device) for j in range(wl.J)] if upload_tables else []
-        self.w_kv = torch.cat([to_dev(inp.w_k, device), to_dev(inp.w_v, device)], 0).contiguous()
+        M = self.M = wl.branches
+        self.w_kv = torch.cat([to_dev(inp.w_k_branch(m), device) for m in range(M)]
+                              + [to_dev(inp.w_v, device)], 0).contiguous()
         self.conv_w = to_dev(inp.conv_w, device)
-        hid = inp.hidden if tokens is None else inp.hidden[: self.B, : self.T]
+        hids = []
+        for m in range(M):
+            hid = inp.hidden_branch(m)
+            hids.append(hid if tokens is None else hid[: self.B, : self.T])
+        hid = hids[0] if M == 1 else np.stack(hids)
         self.hidden = to_dev(np.ascontiguousarray(hid), device)
         self.params = eg.make_params(canon_map=self.canon, tables=self.tables, w_kv=self.w_kv,
                                      conv_w=self.conv_w)
@@ -70,10 +76,11 @@ class DeviceProblem:
         bufs = {}
         if "idx" in want:
             bufs["idx"] = torch.empty(N, wl.J, dtype=torch.int32, device=self.device)
+        lead = (N,) if self.M == 1 else (self.M, N)
         if "stats" in want:
-            bufs["stats"] = torch.empty(N, 4, dtype=torch.float32, device=self.device)
+            bufs["stats"] = torch.empty(*lead, 4, dtype=torch.float32, device=self.device)
         if "k" in want:
-            bufs["k"] = torch.empty(N, wl.hidden, dtype=self.tdtype, device=self.device)
+            bufs["k"] = torch.empty(*lead, wl.hidden, dtype=self.tdtype, device=self.device)
         if "v" in want:
             bufs["v"] = torch.empty(N, wl.hidden, dtype=self.tdtype, device=self.device)
         if "e" in want:
@@ -84,7 +91,8 @@ class DeviceProblem:
         torch = torch_mod()
         eg = self.eg
         if y is None:
-            y = torch.empty(self.B, self.T, self.wl.hidden, dtype=self.tdtype, device=self.device)
+            lead = (self.B, self.T) if self.M == 1 else (self.M, self.B, self.T)
+            y = torch.empty(*lead, self.wl.hidden, dtype=self.tdtype, device=self.device)
         if ws is None:
             ws = self.workspace(eg.ENGRAM_OP_FORWARD)
         saved = eg.make_saved(**saved_bufs) if saved_bufs else None
@@ -125,13 +133,19 @@ class DeviceProblem:
         return res
 
 
-def oracle_problem(inp: synth.Inputs, tokens=None, hidden=None):
+def oracle_problem(inp: synth.Inputs, tokens=None, hidden=None, branch=0):
+    """The oracle's problem for one branch: its W_K and hidden state, the shared
+    tables, W_V and conv."""
     import oracle
     over = {}
     if tokens is not None:
         over["tokens"] = tokens
     if hidden is not None:
         over["h"] = hidden
+    elif branch:
+        over["h"] = inp.hidden_branch(branch)
+    if branch:
+        over["w_k"] = oracle.widen(inp.w_k_branch(branch))
     return oracle.Problem.from_inputs(inp, **over)
 
 
