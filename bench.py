@@ -30,20 +30,21 @@ def log(*a):
 
 
 def kernel_units(wl, N):
-    """Algorithmic bytes / flops per launch of each forward kernel."""
+    """Algorithmic bytes / flops per launch of each forward kernel.
+    With M branches the projection has (M+1)*d outputs and reads M hidden
+    states; gate + conv reads v and writes Y once per branch."""
     es = 2 if wl.dtype == "bf16" else 4
-    J, d, dm = wl.J, wl.hidden, wl.d_mem
+    J, d, dm, M = wl.J, wl.hidden, wl.d_mem, wl.branches
     nkt = d // 256
+    proj_bytes = N * dm * es + (M + 1) * d * dm * es + (M + 1) * N * d * es + M * N * nkt * 12
     return {
         "hash": {"bound": "hbm", "bytes": N * 4 + N * J * 4},
         "gather": {"bound": "hbm", "bytes": N * J * 4 + 2 * N * dm * es},
-        "proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * 2 * d,
-                      "bytes": N * dm * es + 2 * d * dm * es + 2 * N * d * es + N * nkt * 12},
+        "proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * (M + 1) * d, "bytes": proj_bytes},
         # the same projection reading the table rows itself (row gather fused)
-        "gather_proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * 2 * d,
-                             "bytes": N * J * 4 + N * dm * es + 2 * d * dm * es + 2 * N * d * es
-                             + N * nkt * 12},
-        "gate_conv": {"bound": "hbm", "bytes": 2 * N * d * es + N * nkt * 12},
+        "gather_proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * (M + 1) * d,
+                             "bytes": N * J * 4 + proj_bytes},
+        "gate_conv": {"bound": "hbm", "bytes": M * (2 * N * d * es + N * nkt * 12)},
     }
 
 
@@ -460,6 +461,8 @@ def main():
                     help="print HBM bytes per dispatch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                          "csv runs of the bench and of --copy-calibration")
     ap.add_argument("--calibration-bytes", type=int, default=1 << 30)
+    ap.add_argument("--branches", type=int, default=1,
+                    help="M branches sharing the tables and W_V (own W_K, hidden state, gate, Y)")
     ap.add_argument("--host-rows", type=int, default=4_880_000,
                     help="rows per host table for --workload host100b")
     args = ap.parse_args()
@@ -488,6 +491,11 @@ def main():
     from tests import harness as H
 
     wl = synth.get_workload(args.workload)
+    if args.branches != 1:
+        import dataclasses
+        wl = dataclasses.replace(wl, branches=args.branches)
+        args.no_backward = True  # the table-gradient backward has one branch
+        args.no_cpu_baseline = True  # the oracle baseline is timed on one branch
     N = wl.n_tokens
     log(f"[bench] {wl.name}: B={wl.B} T={wl.T} J={wl.J} D={wl.dim} d={wl.hidden} "
         f"table params={wl.table_params / 1e9:.2f}B; generating inputs")
@@ -496,7 +504,8 @@ def main():
     dp = H.DeviceProblem(inp, flags=eg.ENGRAM_FLAG_FUSED_GATHER if args.fused_gather else 0)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM after {time.perf_counter() - t:.1f} s")
-    y = torch.empty(wl.B, wl.T, wl.hidden, dtype=dp.tdtype, device="cuda")
+    lead = (wl.B, wl.T) if wl.branches == 1 else (wl.branches, wl.B, wl.T)
+    y = torch.empty(*lead, wl.hidden, dtype=dp.tdtype, device="cuda")
     ws = dp.workspace(eg.ENGRAM_OP_FORWARD)
     saved = None
     for _ in range(args.warmup):
@@ -579,7 +588,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "row_gather": "fused into projection" if args.fused_gather else "gathered into workspace", "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
+        "config": {"workload": wl.name, "branches": wl.branches, "row_gather": "fused into projection" if args.fused_gather else "gathered into workspace", "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
                    "rows_per_table": list(wl.rows[:1]) + ["..."], "dim": wl.dim,
                    "d_mem": wl.d_mem, "hidden": wl.hidden, "table_params": wl.table_params,
                    "zipf_s": wl.zipf_s, "vocab": wl.vocab, "canon_vocab": wl.canon_vocab},

@@ -57,14 +57,27 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   constexpr int R = kGcTokens;
   constexpr int NW = TAPS > 1 ? TAPS - 1 : 1;  // window length
   __shared__ float alpha_s[R + kMaxTaps];
+  // Workgroups go round-robin to the 8 XCDs (blockIdx.x mod 8), each with its
+  // own L2.  With several branches, blockIdx.x = (g * branches + br) * 8 + x
+  // runs branch br of token tile g * 8 + x, so the branches of one tile sit on
+  // one XCD, a few dispatches apart: v comes from HBM once, then from L2.
+  const int nbr = a.branches > 0 ? a.branches : 1;
+  int br = 0;
+  int64_t tile = blockIdx.x;
+  if (nbr > 1) {
+    const unsigned j = blockIdx.x >> 3;
+    br = (int)(j % (unsigned)nbr);
+    tile = (int64_t)(j / (unsigned)nbr) * 8 + (blockIdx.x & 7);
+    if (tile * R >= a.T) return;  // padding of the grid to whole groups
+  }
   const int64_t b = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * R;
+  const int64_t t0 = tile * R;
   const int nh = TAPS - 1;
   const int d = a.d;
-  // branch blockIdx.z: its own partial sums, output and stats; v is shared
+  // branch br: its own partial sums, output and stats; v is shared
   const int64_t N = a.B * a.T;
-  const float* __restrict__ partials = a.partials + blockIdx.z * N * a.nkt * 3;
-  float* const stats = a.stats ? a.stats + blockIdx.z * N * 4 : nullptr;
+  const float* __restrict__ partials = a.partials + br * N * a.nkt * 3;
+  float* const stats = a.stats ? a.stats + br * N * 4 : nullptr;
   const float inv_d = 1.0f / (float)d;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
 
@@ -110,7 +123,7 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   const int64_t tbeg = t0 - nh > 0 ? t0 - nh : 0;
   const int64_t tend = (t0 + R < a.T) ? t0 + R : a.T;
   const uint8_t* __restrict__ vsrc = a.v;
-  uint8_t* __restrict__ ydst = a.y + blockIdx.z * N * d * (BF16 ? 2 : 4);
+  uint8_t* __restrict__ ydst = a.y + br * N * d * (BF16 ? 2 : 4);
   const int64_t row0 = b * a.T;
   // v rows stream through a ring of PD tokens loaded ahead (each wave keeps
   // PD 1 KB loads in flight; HBM latency, not bandwidth, bounds a shallower
@@ -160,8 +173,10 @@ hipError_t launch_gate_conv(const GateConvArgs& a, hipStream_t s) {
   const int vec = bf ? 8 : 4;
   int threads = (a.d / vec + 63) / 64 * 64;
   if (threads > 1024) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((a.T + kGcTokens - 1) / kGcTokens), (unsigned)a.B,
-            (unsigned)(a.branches > 0 ? a.branches : 1));
+  const int64_t nbr = a.branches > 0 ? a.branches : 1;
+  const int64_t tiles = (a.T + kGcTokens - 1) / kGcTokens;
+  const int64_t gx = nbr > 1 ? (tiles + 7) / 8 * 8 * nbr : tiles;
+  dim3 grid((unsigned)gx, (unsigned)a.B);
   switch (a.taps) {
 #define ENGRAM_TAPS_CASE(K)                                                                      \
   case K:                                                                                        \

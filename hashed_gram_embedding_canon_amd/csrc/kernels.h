@@ -62,7 +62,7 @@ hipError_t launch_gemm(GemmType type, GemmEpilogue epi, const GemmArgs& g, hipSt
 struct GateConvArgs {
   int64_t B, T;
   int32_t d, taps, nkt, io_dtype;
-  int32_t branches;       // gates and outputs of this many branches (grid.z); v is shared
+  int32_t branches;       // gates and outputs of this many branches; v is shared
   float eps;
   const float* partials;  // [branches][N][nkt][3]
   const uint8_t* v;       // [N][d]
