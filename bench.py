@@ -32,7 +32,7 @@ def log(*a):
 def kernel_units(wl, N):
     """Algorithmic bytes / flops per launch of each forward kernel.
     With M branches the projection has (M+1)*d outputs and reads M hidden
-    states; gate + conv reads v and writes Y once per branch."""
+    states; gate + conv reads v once and writes one Y per branch."""
     es = 2 if wl.dtype == "bf16" else 4
     J, d, dm, M = wl.J, wl.hidden, wl.d_mem, wl.branches
     nkt = d // 256
@@ -44,7 +44,8 @@ def kernel_units(wl, N):
         # the same projection reading the table rows itself (row gather fused)
         "gather_proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * (M + 1) * d,
                              "bytes": N * J * 4 + proj_bytes},
-        "gate_conv": {"bound": "hbm", "bytes": M * (2 * N * d * es + N * nkt * 12)},
+        # v is read once for all branches; each branch writes its own Y
+        "gate_conv": {"bound": "hbm", "bytes": (M + 1) * N * d * es + M * N * nkt * 12},
     }
 
 

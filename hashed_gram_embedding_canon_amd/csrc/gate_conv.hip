@@ -8,9 +8,9 @@
 // features (a lane holds VEC neighbouring features).  The gate of each token
 // comes from the per-feature-tile partial sums that the projection epilogue
 // left behind (sum k^2, sum g_q g_k h k, sum h^2), so k and h are never read
-// here.  The conv walks the tokens in order with the last taps-1 gated values
-// in registers, so v is read once (plus a taps-1 token halo per workgroup)
-// and Y is written once: an HBM-streaming kernel.
+// here.  The conv walks the tokens in order with the last taps-1 values of v
+// in registers, so v is read once for all branches (plus a taps-1 token halo
+// per workgroup) and each branch's Y is written once: an HBM-streaming kernel.
 #include "kernels.h"
 
 namespace engram {
@@ -56,37 +56,27 @@ template <int VEC, bool BF16, int TAPS>
 __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   constexpr int R = kGcTokens;
   constexpr int NW = TAPS > 1 ? TAPS - 1 : 1;  // window length
-  __shared__ float alpha_s[R + kMaxTaps];
-  // Workgroups go round-robin to the 8 XCDs (blockIdx.x mod 8), each with its
-  // own L2.  With several branches, blockIdx.x = (g * branches + br) * 8 + x
-  // runs branch br of token tile g * 8 + x, so the branches of one tile sit on
-  // one XCD, a few dispatches apart: v comes from HBM once, then from L2.
+  constexpr int RH = R + kMaxTaps;             // gates kept per branch
+  // gates of every branch for this tile and its taps-1 token halo
+  __shared__ float alpha_s[ENGRAM_MAX_BRANCHES * RH];
   const int nbr = a.branches > 0 ? a.branches : 1;
-  int br = 0;
-  int64_t tile = blockIdx.x;
-  if (nbr > 1) {
-    const unsigned j = blockIdx.x >> 3;
-    br = (int)(j % (unsigned)nbr);
-    tile = (int64_t)(j / (unsigned)nbr) * 8 + (blockIdx.x & 7);
-    if (tile * R >= a.T) return;  // padding of the grid to whole groups
-  }
   const int64_t b = blockIdx.y;
-  const int64_t t0 = tile * R;
+  const int64_t t0 = (int64_t)blockIdx.x * R;
   const int nh = TAPS - 1;
   const int d = a.d;
-  // branch br: its own partial sums, output and stats; v is shared
   const int64_t N = a.B * a.T;
-  const float* __restrict__ partials = a.partials + br * N * a.nkt * 3;
-  float* const stats = a.stats ? a.stats + br * N * 4 : nullptr;
   const float inv_d = 1.0f / (float)d;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
 
-  // ---- gate of tokens t0-nh .. t0+R-1 (zero before the sequence start)
-  for (int i = threadIdx.x; i < R + nh; i += blockDim.x) {
+  // ---- gate of tokens t0-nh .. t0+R-1 of each branch (zero before the
+  // sequence start); branch m has its own partial sums and stats
+  for (int e = threadIdx.x; e < nbr * (R + nh); e += blockDim.x) {
+    const int m = e / (R + nh);
+    const int i = e - m * (R + nh);
     const int64_t t = t0 - nh + i;
     float al = 0.f;
     if (t >= 0 && t < a.T) {
-      const float* p = partials + (b * a.T + t) * a.nkt * 3;
+      const float* p = a.partials + (m * N + b * a.T + t) * a.nkt * 3;
       float skk = 0.f, shk = 0.f, shh = 0.f;
       for (int q = 0; q < a.nkt; ++q) {
         skk += p[3 * q];
@@ -97,16 +87,19 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
       const float rk = 1.0f / sqrtf(skk * inv_d + a.eps);
       const float s = shk * rq * rk * inv_sqrt_d;
       al = 1.0f / (1.0f + expf(-s));
-      if (stats && t >= t0) {
-        float* st = stats + (b * a.T + t) * 4;
+      if (a.stats && t >= t0) {
+        float* st = a.stats + (m * N + b * a.T + t) * 4;
         *reinterpret_cast<floatx4*>(st) = floatx4{al, rq, rk, shk};
       }
     }
-    alpha_s[i] = al;
+    alpha_s[m * RH + i] = al;
   }
   __syncthreads();
 
-  // ---- causal conv over the gated values, VEC features per lane
+  // ---- causal conv, VEC features per lane.  The branches share v and the
+  // conv weights, so one pass over v serves all of them: the lane keeps the
+  // last taps-1 raw v values, and branch m's conv input at t-i is
+  // alpha_m(t-i) v(t-i), i.e. z_m = sum_i alpha_m(t-i) (w_i v(t-i)).
   const int f = threadIdx.x * VEC;
   if (f >= d) return;
   float w[VEC][TAPS];
@@ -114,7 +107,7 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   for (int c = 0; c < VEC; ++c)
 #pragma unroll
     for (int i = 0; i < TAPS; ++i) w[c][i] = a.conv_w[(f + c) * TAPS + i];
-  float win[NW][VEC];  // win[i] = gated value at t-1-i
+  float win[NW][VEC];  // win[i] = raw v at t-1-i
 #pragma unroll
   for (int i = 0; i < NW; ++i)
 #pragma unroll
@@ -123,7 +116,7 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   const int64_t tbeg = t0 - nh > 0 ? t0 - nh : 0;
   const int64_t tend = (t0 + R < a.T) ? t0 + R : a.T;
   const uint8_t* __restrict__ vsrc = a.v;
-  uint8_t* __restrict__ ydst = a.y + br * N * d * (BF16 ? 2 : 4);
+  const int64_t ystride = N * d * (BF16 ? 2 : 4);  // bytes between branch outputs
   const int64_t row0 = b * a.T;
   // v rows stream through a ring of PD tokens loaded ahead (each wave keeps
   // PD 1 KB loads in flight; HBM latency, not bandwidth, bounds a shallower
@@ -141,20 +134,30 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
         float cur[VEC];
         widen<VEC, BF16>(ring[u], cur);
         if (t + PD < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + t + PD) * d + f);
-        const float al = alpha_s[t - (t0 - nh)];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) cur[c] *= al;
         if (t >= t0) {
-          float out[VEC];
+          // weighted taps, shared by the branches
+          float p[TAPS][VEC];
 #pragma unroll
           for (int c = 0; c < VEC; ++c) {
-            float z = w[c][0] * cur[c];
+            p[0][c] = w[c][0] * cur[c];
 #pragma unroll
-            for (int i = 1; i < TAPS; ++i) z += w[c][i] * win[i - 1][c];
-            // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
-            out[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) + cur[c];
+            for (int i = 1; i < TAPS; ++i) p[i][c] = w[c][i] * win[i - 1][c];
           }
-          store_vec<VEC, BF16>(ydst, (row0 + t) * d + f, out);
+          const int li = (int)(t - (t0 - nh));
+          uint8_t* ydst = a.y;
+          for (int m = 0; m < nbr; ++m, ydst += ystride) {
+            const float* al = alpha_s + m * RH + li;  // al[-i] = alpha_m(t-i)
+            float out[VEC];
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+              float z = al[0] * p[0][c];
+#pragma unroll
+              for (int i = 1; i < TAPS; ++i) z += al[-i] * p[i][c];
+              // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
+              out[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) + al[0] * cur[c];
+            }
+            store_vec<VEC, BF16>(ydst, (row0 + t) * d + f, out);
+          }
         }
 #pragma unroll
         for (int i = NW - 1; i > 0; --i)
@@ -173,10 +176,8 @@ hipError_t launch_gate_conv(const GateConvArgs& a, hipStream_t s) {
   const int vec = bf ? 8 : 4;
   int threads = (a.d / vec + 63) / 64 * 64;
   if (threads > 1024) return hipErrorInvalidValue;
-  const int64_t nbr = a.branches > 0 ? a.branches : 1;
-  const int64_t tiles = (a.T + kGcTokens - 1) / kGcTokens;
-  const int64_t gx = nbr > 1 ? (tiles + 7) / 8 * 8 * nbr : tiles;
-  dim3 grid((unsigned)gx, (unsigned)a.B);
+  if (a.branches > ENGRAM_MAX_BRANCHES) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((a.T + kGcTokens - 1) / kGcTokens), (unsigned)a.B);
   switch (a.taps) {
 #define ENGRAM_TAPS_CASE(K)                                                                      \
   case K:                                                                                        \
