@@ -77,6 +77,7 @@ def _load():
     lib.oracle_conv.argtypes = [P, i64, vp, vp, vp]
     lib.oracle_forward.argtypes = [P, i64, vp, vp, vp, vp, vp, vp]
     lib.oracle_backward_de.argtypes = [P, vp, i64, vp, vp]
+    lib.oracle_backward_params.argtypes = [P, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_table_grad_rows.argtypes = [P, vp, vp, i64, vp, vp, vp]
     lib.oracle_table_grad_dense.argtypes = [P, vp, vp]
     lib.oracle_prefetch_plan.argtypes = [i64, i32, vp, vp, vp, vp]
@@ -244,6 +245,26 @@ class Problem:
         pos = self.all_positions() if pos is None else np.ascontiguousarray(pos, dtype=np.int64)
         out = np.empty((pos.size, self.d_mem), np.float64)
         _load().oracle_backward_de(self.ref, _ptr(dy), pos.size, _ptr(pos), _ptr(out))
+        return out
+
+    def backward_params(self, dy: np.ndarray, pos=None,
+                        want=("w_k", "w_v", "conv_w", "gamma_q", "gamma_k", "h")) -> dict:
+        """Parameter and hidden-state gradients of L = sum <G, Y> (float64).
+
+        w_k, w_v [d, d_mem], conv_w [d, taps], gamma_q, gamma_k [d]: summed
+        over the positions `pos` (default: all, the full gradients); h
+        [npos, d]: per position, the gate's part of dL/dh_t."""
+        dy = np.ascontiguousarray(dy)
+        assert dy.shape == (self.B, self.T, self.hidden) and _dt(dy) == _dt(self.h)
+        pos = self.all_positions() if pos is None else np.ascontiguousarray(pos, dtype=np.int64)
+        d, dm = self.hidden, self.d_mem
+        shapes = {"w_k": (d, dm), "w_v": (d, dm), "conv_w": (d, self.taps), "gamma_q": (d,),
+                  "gamma_k": (d,), "h": (pos.size, d)}
+        out = {k: np.empty(shapes[k], np.float64) for k in want}
+        _load().oracle_backward_params(self.ref, _ptr(dy), pos.size, _ptr(pos), _ptr(out.get("w_k")),
+                                       _ptr(out.get("w_v")), _ptr(out.get("conv_w")),
+                                       _ptr(out.get("gamma_q")), _ptr(out.get("gamma_k")),
+                                       _ptr(out.get("h")))
         return out
 
     def table_grad_rows(self, dy: np.ndarray, idx_all: np.ndarray, rows_j, rows_r):

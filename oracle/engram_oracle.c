@@ -290,16 +290,91 @@ int oracle_forward(const oracle_problem* p, int64_t npos, const int64_t* pos, do
 }
 
 /*
- * Backward to the memory vector: de_t = dL/de_t for L = sum_t <G_t, Y_t>,
- * G = dy (dtype of the problem, [B][T][d]).  Derived by the chain rule from
- * the forward above (the pages print no backward):
+ * Backward at one token t of sequence b for L = sum_t <G_t, Y_t>, G = dy
+ * (dtype of the problem, [B][T][d]).  Derived by the chain rule from the
+ * forward above (the pages print no backward):
  *   dz_u   = G_u * sig(z_u) * (1 + z_u (1 - sig(z_u)))            u = t..t+taps-1
  *   dvt_t  = G_t + sum_i w[:,i] * dz_{t+i}
  *   dalpha = <dvt_t, v_t>,  dv_t = alpha_t dvt_t
  *   ds     = dalpha * alpha (1 - alpha)
  *   dk^    = ds * q / sqrt(d)                  (q = g_q h rq)
  *   g      = g_k * dk^,  dk = rk g - rk^3 k <g,k> / d
- *   de_t   = W_K^T dk + W_V^T dv
+ * st[0 .. 2 taps-2] receive the forward at t-taps+1 .. t+taps-1 (st[taps-1]
+ * is t itself), dz[i*d + c] the conv-input gradient at t+i; dk, dv [d] and
+ * *ds_out are written.
+ */
+typedef struct {
+  double* dz;   /* [taps][d] */
+  double* z;    /* [d] */
+  double* dvt;  /* [d] */
+  double* g;    /* [d] */
+} bwd_scratch;
+
+static void bwd_alloc(const oracle_problem* p, bwd_scratch* w) {
+  int d = p->hidden;
+  w->dz = (double*)malloc(sizeof(double) * d * p->taps);
+  w->z = (double*)malloc(sizeof(double) * d);
+  w->dvt = (double*)malloc(sizeof(double) * d);
+  w->g = (double*)malloc(sizeof(double) * d);
+}
+
+static void bwd_free(bwd_scratch* w) { free(w->dz); free(w->z); free(w->dvt); free(w->g); }
+
+static void token_backward(const oracle_problem* p, const void* dy, int64_t b, int64_t t,
+                           tok_state* st, bwd_scratch* w, double* dk, double* dv, double* ds_out) {
+  int d = p->hidden;
+  int taps = p->taps;
+  int W = 2 * taps - 1; /* positions t-taps+1 .. t+taps-1 */
+  double* dz = w->dz;
+  double* z = w->z;
+  double* dvt = w->dvt;
+  double* g = w->g;
+  for (int s = 0; s < W; ++s) {
+    int64_t u = t - (taps - 1) + s;
+    if (u < p->T) token_forward(p, b, u, &st[s]);
+  }
+  /* dz at u = t + i, i < taps */
+  for (int i = 0; i < taps; ++i) {
+    int64_t u = t + i;
+    if (u >= p->T) {
+      memset(dz + (int64_t)i * d, 0, sizeof(double) * d);
+      continue;
+    }
+    double* win[16];
+    for (int a = 0; a < taps; ++a) win[a] = st[(taps - 1) + i - a].vt;
+    conv_out(p, win, z, NULL);
+    for (int c = 0; c < d; ++c) {
+      double G = load_val(dy, p->act_dtype, (b * p->T + u) * d + c);
+      double sg = sigmoid(z[c]);
+      dz[(int64_t)i * d + c] = G * sg * (1.0 + z[c] * (1.0 - sg));
+    }
+  }
+  tok_state* s0 = &st[taps - 1];
+  double dalpha = 0.0;
+  for (int c = 0; c < d; ++c) {
+    double acc = load_val(dy, p->act_dtype, (b * p->T + t) * d + c);
+    for (int i = 0; i < taps; ++i) acc += p->conv_w[(int64_t)c * taps + i] * dz[(int64_t)i * d + c];
+    dvt[c] = acc;
+    dalpha += acc * s0->v[c];
+  }
+  for (int c = 0; c < d; ++c) dv[c] = s0->alpha * dvt[c];
+  double ds = dalpha * s0->alpha * (1.0 - s0->alpha);
+  double gk_dot = 0.0;
+  for (int c = 0; c < d; ++c) {
+    double gq = p->gamma_q ? p->gamma_q[c] : 1.0;
+    double gk = p->gamma_k ? p->gamma_k[c] : 1.0;
+    double dkhat = ds * gq * s0->h[c] * s0->rq / sqrt((double)d);
+    g[c] = gk * dkhat;
+    gk_dot += g[c] * s0->k[c];
+  }
+  double rk = s0->rk;
+  for (int c = 0; c < d; ++c) dk[c] = rk * g[c] - rk * rk * rk * s0->k[c] * gk_dot / d;
+  *ds_out = ds;
+}
+
+/*
+ * Backward to the memory vector at the positions pos[q] = b*T + t:
+ *   de_t = W_K^T dk_t + W_V^T dv_t        (dk, dv from token_backward)
  * Output de [npos][d_mem].
  */
 int oracle_backward_de(const oracle_problem* p, const void* dy, int64_t npos, const int64_t* pos,
@@ -307,61 +382,20 @@ int oracle_backward_de(const oracle_problem* p, const void* dy, int64_t npos, co
   int d = p->hidden;
   int taps = p->taps;
   int64_t dm = d_mem(p);
-  int W = 2 * taps - 1; /* positions t-taps+1 .. t+taps-1 */
+  int W = 2 * taps - 1;
 #pragma omp parallel
   {
     tok_state st[32];
     for (int i = 0; i < W; ++i) tok_alloc(p, &st[i]);
-    double* dz = (double*)malloc(sizeof(double) * d * taps);
-    double* z = (double*)malloc(sizeof(double) * d);
-    double* dvt = (double*)malloc(sizeof(double) * d);
+    bwd_scratch ws;
+    bwd_alloc(p, &ws);
     double* dk = (double*)malloc(sizeof(double) * d);
     double* dv = (double*)malloc(sizeof(double) * d);
-    double* g = (double*)malloc(sizeof(double) * d);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t q = 0; q < npos; ++q) {
       int64_t b = pos[q] / p->T, t = pos[q] % p->T;
-      /* st[w] holds position t - (taps-1) + w */
-      for (int w = 0; w < W; ++w) {
-        int64_t u = t - (taps - 1) + w;
-        if (u < p->T) token_forward(p, b, u, &st[w]);
-      }
-      /* dz at u = t + i, i < taps */
-      for (int i = 0; i < taps; ++i) {
-        int64_t u = t + i;
-        if (u >= p->T) {
-          memset(dz + (int64_t)i * d, 0, sizeof(double) * d);
-          continue;
-        }
-        double* win[16];
-        for (int a = 0; a < taps; ++a) win[a] = st[(taps - 1) + i - a].vt;
-        conv_out(p, win, z, NULL);
-        for (int c = 0; c < d; ++c) {
-          double G = load_val(dy, p->act_dtype, (b * p->T + u) * d + c);
-          double sg = sigmoid(z[c]);
-          dz[(int64_t)i * d + c] = G * sg * (1.0 + z[c] * (1.0 - sg));
-        }
-      }
-      tok_state* s0 = &st[taps - 1];
-      double dalpha = 0.0;
-      for (int c = 0; c < d; ++c) {
-        double acc = load_val(dy, p->act_dtype, (b * p->T + t) * d + c);
-        for (int i = 0; i < taps; ++i) acc += p->conv_w[(int64_t)c * taps + i] * dz[(int64_t)i * d + c];
-        dvt[c] = acc;
-        dalpha += acc * s0->v[c];
-      }
-      for (int c = 0; c < d; ++c) dv[c] = s0->alpha * dvt[c];
-      double ds = dalpha * s0->alpha * (1.0 - s0->alpha);
-      double gk_dot = 0.0;
-      for (int c = 0; c < d; ++c) {
-        double gq = p->gamma_q ? p->gamma_q[c] : 1.0;
-        double gk = p->gamma_k ? p->gamma_k[c] : 1.0;
-        double dkhat = ds * gq * s0->h[c] * s0->rq / sqrt((double)d);
-        g[c] = gk * dkhat;
-        gk_dot += g[c] * s0->k[c];
-      }
-      double rk = s0->rk;
-      for (int c = 0; c < d; ++c) dk[c] = rk * g[c] - rk * rk * rk * s0->k[c] * gk_dot / d;
+      double ds;
+      token_backward(p, dy, b, t, st, &ws, dk, dv, &ds);
       double* de = de_out + q * dm;
       for (int64_t i = 0; i < dm; ++i) {
         double acc = 0.0;
@@ -372,8 +406,108 @@ int oracle_backward_de(const oracle_problem* p, const void* dy, int64_t npos, co
       }
     }
     for (int i = 0; i < W; ++i) tok_free(&st[i]);
-    free(dz); free(z); free(dvt); free(dk); free(dv); free(g);
+    bwd_free(&ws);
+    free(dk); free(dv);
   }
+  return 0;
+}
+
+/*
+ * Gradients of the module's own parameters and of the hidden state, for the
+ * same L, by the chain rule through the same forward:
+ *   dW_K[c][i]  = sum_t dk_t[c] e_t[i],   dW_V[c][i] = sum_t dv_t[c] e_t[i]
+ *                 (k_t = W_K e_t, v_t = W_V e_t)
+ *   dconv[c][i] = sum_t dz_t[c] vt_{t-i}[c]      (z_t = sum_i w[c][i] vt_{t-i})
+ *   with q = g_q h rq, k^ = g_k k rk, s = <q, k^>/sqrt(d):
+ *   dq = ds k^ / sqrt(d),  dk^ = ds q / sqrt(d)
+ *   dgamma_q[c] = sum_t dq[c] h_t[c] rq_t,   dgamma_k[c] = sum_t dk^[c] k_t[c] rk_t
+ *   dh_t = rq f - rq^3 h_t <f, h_t> / d,  f = g_q dq     (RMSNorm backward;
+ *          the gate's part only: the caller's residual H + Y adds G itself)
+ * The sums run over the positions pos[0..npos) (all positions give the full
+ * gradients; where G vanishes on t..t+taps-1 a position adds nothing).
+ * Outputs, each may be NULL: dw_k, dw_v [d][d_mem], dconv [d][taps],
+ * dgamma_q, dgamma_k [d] (sums), dh [npos][d] (per position).
+ */
+int oracle_backward_params(const oracle_problem* p, const void* dy, int64_t npos, const int64_t* pos,
+                           double* dw_k, double* dw_v, double* dconv, double* dgamma_q,
+                           double* dgamma_k, double* dh) {
+  int d = p->hidden;
+  int taps = p->taps;
+  int64_t dm = d_mem(p);
+  int W = 2 * taps - 1;
+  const int64_t CH = 256; /* positions per chunk: computed in parallel, summed in order */
+  /* per position of a chunk: dk, dv, e, dz (x) vt window, dq h rq, dk^ k rk */
+  int64_t per = 2 * d + dm + (int64_t)d * taps + 2 * d;
+  double* buf = (double*)malloc(sizeof(double) * CH * per);
+  if (dw_k) memset(dw_k, 0, sizeof(double) * d * dm);
+  if (dw_v) memset(dw_v, 0, sizeof(double) * d * dm);
+  if (dconv) memset(dconv, 0, sizeof(double) * d * taps);
+  if (dgamma_q) memset(dgamma_q, 0, sizeof(double) * d);
+  if (dgamma_k) memset(dgamma_k, 0, sizeof(double) * d);
+  for (int64_t q0 = 0; q0 < npos; q0 += CH) {
+    int64_t nq = npos - q0 < CH ? npos - q0 : CH;
+#pragma omp parallel
+    {
+      tok_state st[32];
+      for (int i = 0; i < W; ++i) tok_alloc(p, &st[i]);
+      bwd_scratch ws;
+      bwd_alloc(p, &ws);
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t a = 0; a < nq; ++a) {
+        int64_t b = pos[q0 + a] / p->T, t = pos[q0 + a] % p->T;
+        double* o = buf + a * per;
+        double *dk = o, *dv = o + d, *e = o + 2 * d, *cz = e + dm, *gqs = cz + (int64_t)d * taps,
+               *gks = gqs + d;
+        double ds;
+        token_backward(p, dy, b, t, st, &ws, dk, dv, &ds);
+        tok_state* s0 = &st[taps - 1];
+        memcpy(e, s0->e, sizeof(double) * dm);
+        for (int c = 0; c < d; ++c)
+          for (int i = 0; i < taps; ++i) /* dz_t at index 0 of the scratch; vt_{t-i} = st[taps-1-i] */
+            cz[(int64_t)c * taps + i] = ws.dz[c] * st[taps - 1 - i].vt[c];
+        double sd = sqrt((double)d);
+        double fh = 0.0;
+        for (int c = 0; c < d; ++c) {
+          double gq = p->gamma_q ? p->gamma_q[c] : 1.0;
+          double gk = p->gamma_k ? p->gamma_k[c] : 1.0;
+          double qv = gq * s0->h[c] * s0->rq;
+          double kv = gk * s0->k[c] * s0->rk;
+          double dq = ds * kv / sd;
+          double dkh = ds * qv / sd;
+          gqs[c] = dq * s0->h[c] * s0->rq;
+          gks[c] = dkh * s0->k[c] * s0->rk;
+          fh += gq * dq * s0->h[c];
+        }
+        if (dh) {
+          double rq = s0->rq;
+          for (int c = 0; c < d; ++c) {
+            double gq = p->gamma_q ? p->gamma_q[c] : 1.0;
+            double gk = p->gamma_k ? p->gamma_k[c] : 1.0;
+            double f = gq * ds * (gk * s0->k[c] * s0->rk) / sd;
+            dh[(q0 + a) * d + c] = rq * f - rq * rq * rq * s0->h[c] * fh / d;
+          }
+        }
+      }
+      for (int i = 0; i < W; ++i) tok_free(&st[i]);
+      bwd_free(&ws);
+    }
+    for (int64_t a = 0; a < nq; ++a) {
+      const double* o = buf + a * per;
+      const double *dk = o, *dv = o + d, *e = o + 2 * d, *cz = e + dm, *gqs = cz + (int64_t)d * taps,
+                   *gks = gqs + d;
+      for (int c = 0; c < d; ++c) {
+        if (dw_k)
+          for (int64_t i = 0; i < dm; ++i) dw_k[(int64_t)c * dm + i] += dk[c] * e[i];
+        if (dw_v)
+          for (int64_t i = 0; i < dm; ++i) dw_v[(int64_t)c * dm + i] += dv[c] * e[i];
+        if (dconv)
+          for (int i = 0; i < taps; ++i) dconv[(int64_t)c * taps + i] += cz[(int64_t)c * taps + i];
+        if (dgamma_q) dgamma_q[c] += gqs[c];
+        if (dgamma_k) dgamma_k[c] += gks[c];
+      }
+    }
+  }
+  free(buf);
   return 0;
 }
 
