@@ -23,7 +23,7 @@ ENGRAM_MAX_BRANCHES = 8
 ENGRAM_FLAG_FUSED_GATHER = 1
 ENGRAM_PLAN_REUSE = 1
 ENGRAM_GRAD_SORTED_SPARSE, ENGRAM_GRAD_SORTED_DENSE, ENGRAM_GRAD_ATOMIC_DENSE = 0, 1, 2
-ENGRAM_OP_FORWARD, ENGRAM_OP_BACKWARD = 0, 1
+ENGRAM_OP_FORWARD, ENGRAM_OP_BACKWARD, ENGRAM_OP_BACKWARD_PARAMS = 0, 1, 2
 
 _vp = ctypes.c_void_p
 
@@ -88,6 +88,16 @@ class engram_table_grad(ctypes.Structure):
     ]
 
 
+class engram_param_grad(ctypes.Structure):
+    _fields_ = [
+        ("w_kv", _vp),
+        ("conv_w", _vp),
+        ("gamma_q", _vp),
+        ("gamma_k", _vp),
+        ("hidden", _vp),
+    ]
+
+
 class EngramError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {engram_status_string(status)} (status {status})")
@@ -95,7 +105,8 @@ class EngramError(RuntimeError):
 
 
 EXPORTS = ("engram_workspace_size", "engram_status_string", "engram_hash_indices", "engram_forward",
-           "engram_backward_table_grad", "engram_prefetch_plan", "engram_profile_enable",
+           "engram_backward_table_grad", "engram_backward", "engram_prefetch_plan",
+           "engram_profile_enable",
            "engram_profile_reset", "engram_profile_read")
 
 _lib = None
@@ -111,9 +122,9 @@ def lib():
                            "(hashed_gram_embedding_canon_amd/build.py)")
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-    C, P, S, K, G = (ctypes.POINTER(engram_config), ctypes.POINTER(engram_params),
-                     ctypes.POINTER(engram_saved), ctypes.POINTER(engram_compact),
-                     ctypes.POINTER(engram_table_grad))
+    C, P, S, K, G, PG = (ctypes.POINTER(engram_config), ctypes.POINTER(engram_params),
+                         ctypes.POINTER(engram_saved), ctypes.POINTER(engram_compact),
+                         ctypes.POINTER(engram_table_grad), ctypes.POINTER(engram_param_grad))
     L.engram_workspace_size.argtypes = [C, i64, i64, i32]
     L.engram_workspace_size.restype = sz
     L.engram_status_string.argtypes = [ctypes.c_int]
@@ -121,6 +132,7 @@ def lib():
     L.engram_hash_indices.argtypes = [C, _vp, _vp, i64, i64, _vp, _vp]
     L.engram_forward.argtypes = [C, P, _vp, _vp, i64, i64, _vp, S, K, _vp, sz, _vp]
     L.engram_backward_table_grad.argtypes = [C, P, _vp, _vp, i64, i64, S, G, _vp, sz, _vp]
+    L.engram_backward.argtypes = [C, P, _vp, _vp, i64, i64, S, G, PG, _vp, sz, _vp]
     L.engram_prefetch_plan.argtypes = [C, _vp, _vp, i64, i64, _vp, K, _vp]
     L.engram_profile_enable.argtypes = [i32]
     L.engram_profile_enable.restype = None
@@ -129,7 +141,7 @@ def lib():
     L.engram_profile_read.argtypes = [ctypes.c_char_p, sz, _vp, _vp, i32]
     L.engram_profile_read.restype = i32
     for name in ("engram_hash_indices", "engram_forward", "engram_backward_table_grad",
-                 "engram_prefetch_plan"):
+                 "engram_backward", "engram_prefetch_plan"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -243,6 +255,27 @@ def engram_backward_table_grad(cfg: Config, params: engram_params, hidden, dy, *
                                             B, T, ctypes.byref(saved) if saved is not None else None,
                                             ctypes.byref(out), _ptr(workspace), ws_bytes,
                                             _stream(stream)), "engram_backward_table_grad")
+
+
+def make_param_grad(*, w_kv=None, conv_w=None, gamma_q=None, gamma_k=None,
+                    hidden=None) -> engram_param_grad:
+    g = engram_param_grad()
+    g.w_kv, g.conv_w, g.gamma_q, g.gamma_k, g.hidden = (_ptr(w_kv), _ptr(conv_w), _ptr(gamma_q),
+                                                        _ptr(gamma_k), _ptr(hidden))
+    return g
+
+
+def engram_backward(cfg: Config, params: engram_params, hidden, dy, *, B: int, T: int,
+                    saved: engram_saved, table_out: engram_table_grad | None = None,
+                    param_out: engram_param_grad | None = None, workspace=None,
+                    ws_bytes: int | None = None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().engram_backward(cfg.ref, ctypes.byref(params), _ptr(hidden), _ptr(dy), B, T,
+                                 ctypes.byref(saved) if saved is not None else None,
+                                 ctypes.byref(table_out) if table_out is not None else None,
+                                 ctypes.byref(param_out) if param_out is not None else None,
+                                 _ptr(workspace), ws_bytes, _stream(stream)), "engram_backward")
 
 
 def engram_prefetch_plan(cfg: Config, canon_map_host, tokens_host, *, B: int, T: int,

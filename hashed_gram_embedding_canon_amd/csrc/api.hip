@@ -186,13 +186,25 @@ size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out,
 }
 
 struct BwdWs {
-  uint8_t* dkv;
+  uint8_t* dkv;    // [round_up(N, 32)][2d]: the weight-gradient GEMM reads whole 32-token stages
   uint8_t* wt;
   float* de;
   uint8_t* sort;
+  // parameter gradients
+  uint8_t* e;      // [N][d_mem] dtype, rows gathered again (when e was not saved)
+  float* dw_part;  // [splits][2d][d_mem] (splits > 1)
+  float* pacc;     // [nblk][d][taps+1]
+  float* ptmp;     // bwd_param_tmp_floats
+  int32_t splits;
 };
 
-size_t backward_ws(const Shape& s, int64_t N, BwdWs* out, uint8_t* base) {
+int64_t round32(int64_t n) { return (n + 31) / 32 * 32; }
+
+// table: de GEMM and scatter buffers; params: the parameter-gradient buffers
+// (e only when need_e)
+size_t backward_ws(const Shape& s, int64_t B, int64_t T, BwdWs* out, uint8_t* base,
+                   bool table = true, bool params = false, bool need_e = true) {
+  const int64_t N = B * T;
   const int eg = s.dtype == ENGRAM_BF16 ? 2 : 4;  // fp16 or fp32 GEMM operands
   size_t off = 0;
   auto take = [&](size_t bytes) -> uint8_t* {
@@ -201,10 +213,20 @@ size_t backward_ws(const Shape& s, int64_t N, BwdWs* out, uint8_t* base) {
     return p;
   };
   BwdWs w{};
-  w.dkv = take((size_t)N * 2 * s.d * eg);
-  w.wt = take((size_t)s.d_mem * 2 * s.d * eg);
-  w.de = (float*)take((size_t)N * s.d_mem * 4);
-  w.sort = take(sort_workspace_bytes(N, s.J));
+  w.dkv = take((size_t)round32(N) * 2 * s.d * eg);
+  if (table) {
+    w.wt = take((size_t)s.d_mem * 2 * s.d * eg);
+    w.de = (float*)take((size_t)N * s.d_mem * 4);
+    w.sort = take(sort_workspace_bytes(N, s.J));
+  }
+  if (params) {
+    if (need_e) w.e = take((size_t)N * s.d_mem * s.es);
+    w.splits = tn_splits(N, 2 * s.d, s.d_mem);
+    if (w.splits > 1) w.dw_part = (float*)take((size_t)w.splits * 2 * s.d * s.d_mem * 4);
+    const int64_t nb = std::max<int64_t>(1, bwd_blocks(B, T));
+    w.pacc = (float*)take((size_t)nb * s.d * (s.taps + 1) * 4);
+    w.ptmp = (float*)take((size_t)std::max<int64_t>(1, bwd_param_tmp_floats(nb, s.d, s.taps)) * 4);
+  }
   if (out) *out = w;
   return off;
 }
@@ -218,7 +240,8 @@ size_t engram_workspace_size(const engram_config* cfg, int64_t B, int64_t T, int
   if (check_config(cfg, &s) != ENGRAM_OK || B < 0 || T < 0) return 0;
   const int64_t N = B * T;
   if (op == ENGRAM_OP_FORWARD) return forward_ws(s, N, nullptr, nullptr, nullptr, true);
-  if (op == ENGRAM_OP_BACKWARD) return backward_ws(s, N, nullptr, nullptr);
+  if (op == ENGRAM_OP_BACKWARD) return backward_ws(s, B, T, nullptr, nullptr);
+  if (op == ENGRAM_OP_BACKWARD_PARAMS) return backward_ws(s, B, T, nullptr, nullptr, true, true, true);
   return 0;
 }
 
@@ -375,26 +398,37 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
   return ENGRAM_OK;
 }
 
-engram_status engram_backward_table_grad(const engram_config* cfg, const engram_params* p,
-                                         const void* hidden, const void* dy, int64_t B, int64_t T,
-                                         const engram_saved* saved, engram_table_grad* out,
-                                         void* workspace, size_t ws_bytes, void* stream) {
+engram_status engram_backward(const engram_config* cfg, const engram_params* p,
+                              const void* hidden, const void* dy, int64_t B, int64_t T,
+                              const engram_saved* saved, engram_table_grad* out,
+                              engram_param_grad* pg, void* workspace, size_t ws_bytes,
+                              void* stream) {
   Shape s;
   engram_status st = check_config(cfg, &s);
   if (st != ENGRAM_OK) return st;
-  if (!p || !out || B < 0 || T < 0 || T > INT32_MAX || B > 65535) return ENGRAM_E_INVALID;
+  if (!p || (!out && !pg) || B < 0 || T < 0 || T > INT32_MAX || B > 65535) return ENGRAM_E_INVALID;
   if (s.d / 4 > 1024) return ENGRAM_E_UNSUPPORTED;
   if (s.D > 256) return ENGRAM_E_UNSUPPORTED;  // one 16-byte piece per lane of a row
-  if (s.M > 1) return ENGRAM_E_UNSUPPORTED;    // the table-gradient backward has one branch
-  if (out->mode < ENGRAM_GRAD_SORTED_SPARSE || out->mode > ENGRAM_GRAD_ATOMIC_DENSE)
-    return ENGRAM_E_INVALID;
+  if (s.M > 1) return ENGRAM_E_UNSUPPORTED;    // the backward has one branch
   const int64_t N = B * T;
   if ((uint64_t)N * (uint64_t)s.J >= (uint64_t(1) << 31)) return ENGRAM_E_UNSUPPORTED;
-  if (out->mode == ENGRAM_GRAD_SORTED_SPARSE) {
-    if (!out->keys || !out->rows || !out->count || !aligned16(out->rows)) return ENGRAM_E_INVALID;
-  } else {
-    for (int j = 0; j < s.J; ++j)
-      if (!out->dense[j] || !aligned16(out->dense[j])) return ENGRAM_E_INVALID;
+  if (out) {
+    if (out->mode < ENGRAM_GRAD_SORTED_SPARSE || out->mode > ENGRAM_GRAD_ATOMIC_DENSE)
+      return ENGRAM_E_INVALID;
+    if (out->mode == ENGRAM_GRAD_SORTED_SPARSE) {
+      if (!out->keys || !out->rows || !out->count || !aligned16(out->rows)) return ENGRAM_E_INVALID;
+    } else {
+      for (int j = 0; j < s.J; ++j)
+        if (!out->dense[j] || !aligned16(out->dense[j])) return ENGRAM_E_INVALID;
+    }
+  }
+  const bool want_w = pg && pg->w_kv;
+  const bool want_sums = pg && (pg->conv_w || pg->gamma_q || pg->gamma_k);
+  const bool need_e = want_w && !(saved && saved->e);
+  if (pg) {
+    if (s.d_mem % 256 != 0) return ENGRAM_E_UNSUPPORTED;  // whole 256-wide dW tiles
+    if (pg->hidden && !aligned16(pg->hidden)) return ENGRAM_E_INVALID;
+    if (want_w && !aligned16(pg->w_kv)) return ENGRAM_E_INVALID;
   }
   if (N > 0) {
     if (!hidden || !dy || !saved || !saved->idx || !saved->stats || !saved->k || !saved->v)
@@ -403,14 +437,117 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
     if (!aligned16(hidden) || !aligned16(dy) || !aligned16(saved->k) || !aligned16(saved->v) ||
         !aligned16(saved->stats) || !aligned16(p->w_kv))
       return ENGRAM_E_INVALID;
+    if (want_w && saved->e && !aligned16(saved->e)) return ENGRAM_E_INVALID;
+    if (need_e)
+      for (int j = 0; j < s.J; ++j)
+        if (!p->tables[j] || !aligned16(p->tables[j])) return ENGRAM_E_INVALID;
   }
-  const size_t need = backward_ws(s, N, nullptr, nullptr);
+  const size_t need = backward_ws(s, B, T, nullptr, nullptr, out != nullptr, pg != nullptr, need_e);
   if (!workspace || ws_bytes < need || !aligned16(workspace)) return ENGRAM_E_WORKSPACE;
   BwdWs w;
-  backward_ws(s, N, &w, (uint8_t*)workspace);
+  backward_ws(s, B, T, &w, (uint8_t*)workspace, out != nullptr, pg != nullptr, need_e);
   hipStream_t hs = (hipStream_t)stream;
   const bool bf = s.dtype == ENGRAM_BF16;
 
+  if (N > 0) {
+    BwdArgs ba;
+    std::memset(&ba, 0, sizeof(ba));
+    ba.B = B;
+    ba.T = T;
+    ba.d = s.d;
+    ba.taps = s.taps;
+    ba.io_dtype = s.dtype;
+    ba.dy = (const uint8_t*)dy;
+    ba.v = (const uint8_t*)saved->v;
+    ba.k = (const uint8_t*)saved->k;
+    ba.h = (const uint8_t*)hidden;
+    ba.stats = saved->stats;
+    ba.conv_w = p->conv_w;
+    ba.gamma_q = p->gamma_q;
+    ba.gamma_k = p->gamma_k;
+    ba.dkv = w.dkv;
+    if (pg) {
+      ba.pacc = want_sums ? w.pacc : nullptr;
+      ba.dh = (uint8_t*)pg->hidden;
+      ba.pad_rows = want_w ? (int32_t)(round32(N) - N) : 0;
+    }
+    Timed tm("bwd_gate_conv", hs);
+    if (launch_bwd_gate_conv(ba, hs) != hipSuccess) return ENGRAM_E_HIP;
+  }
+  if (out && N > 0) {
+    {
+      Timed tm("transpose_w", hs);
+      if (launch_transpose_w((const uint8_t*)p->w_kv, w.wt, 2 * s.d, s.d_mem, s.dtype, hs) !=
+          hipSuccess)
+        return ENGRAM_E_HIP;
+    }
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.A = w.wt;
+    ga.B = w.dkv;
+    ga.M = N;
+    ga.F = s.d_mem;
+    ga.K = 2 * s.d;
+    ga.group_m = 4;
+    ga.stage_bytes = kBwdStageBytes;
+    ga.persistent = ENGRAM_GEMM_PERSISTENT;
+    ga.c_out = w.de;
+    Timed tm("de_gemm", hs);
+    if (launch_gemm(bf ? GEMM_F16 : GEMM_F32, EPI_STORE_F32, ga, hs) != hipSuccess)
+      return ENGRAM_E_HIP;
+  }
+  if (pg) {
+    if (want_sums) {
+      if (N > 0) {
+        Timed tm("bwd_param_sums", hs);
+        if (launch_bwd_param_sums(w.pacc, w.ptmp, bwd_blocks(B, T), s.d, s.taps, p->gamma_q,
+                                  p->gamma_k, pg->conv_w, pg->gamma_q, pg->gamma_k,
+                                  hs) != hipSuccess)
+          return ENGRAM_E_HIP;
+      } else {
+        // no tokens: the sums are zero
+        if (pg->conv_w && launch_zero_f32(pg->conv_w, (int64_t)s.d * s.taps, hs) != hipSuccess)
+          return ENGRAM_E_HIP;
+        if (pg->gamma_q && launch_zero_f32(pg->gamma_q, s.d, hs) != hipSuccess)
+          return ENGRAM_E_HIP;
+        if (pg->gamma_k && launch_zero_f32(pg->gamma_k, s.d, hs) != hipSuccess)
+          return ENGRAM_E_HIP;
+      }
+    }
+    if (want_w) {
+      const uint8_t* e = need_e ? w.e : (const uint8_t*)(saved ? saved->e : nullptr);
+      if (need_e && N > 0) {
+        GatherArgs g;
+        std::memset(&g, 0, sizeof(g));
+        g.J = s.J;
+        g.row_chunks = s.D * s.es / 16;
+        for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
+        Timed tm("gather", hs);
+        if (launch_gather(saved->idx, w.e, N, g, hs) != hipSuccess) return ENGRAM_E_HIP;
+      }
+      if (N == 0) {
+        if (launch_zero_f32(pg->w_kv, (int64_t)2 * s.d * s.d_mem, hs) != hipSuccess)
+          return ENGRAM_E_HIP;
+      } else {
+        GemmTnArgs ta;
+        std::memset(&ta, 0, sizeof(ta));
+        ta.x = w.dkv;
+        ta.y = e;
+        ta.ldx = 2 * s.d;
+        ta.ldy = s.d_mem;
+        ta.K = N;
+        ta.m = 2 * s.d;
+        ta.n = s.d_mem;
+        ta.splits = w.splits;
+        ta.kchunk = ((N + 31) / 32 + w.splits - 1) / w.splits * 32;
+        ta.out = w.dw_part;
+        Timed tm("dw_gemm", hs);
+        if (launch_gemm_tn(bf ? GEMM_F16 : GEMM_F32, ta, pg->w_kv, hs) != hipSuccess)
+          return ENGRAM_E_HIP;
+      }
+    }
+  }
+  if (!out) return ENGRAM_OK;
   ScatterArgs sa;
   std::memset(&sa, 0, sizeof(sa));
   sa.N = N;
@@ -423,49 +560,6 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
   sa.keys_out = out->keys;
   sa.rows_out = out->rows;
   sa.count_out = out->count;
-  if (N > 0) {
-    {
-      BwdArgs ba;
-      ba.B = B;
-      ba.T = T;
-      ba.d = s.d;
-      ba.taps = s.taps;
-      ba.io_dtype = s.dtype;
-      ba.dy = (const uint8_t*)dy;
-      ba.v = (const uint8_t*)saved->v;
-      ba.k = (const uint8_t*)saved->k;
-      ba.h = (const uint8_t*)hidden;
-      ba.stats = saved->stats;
-      ba.conv_w = p->conv_w;
-      ba.gamma_q = p->gamma_q;
-      ba.gamma_k = p->gamma_k;
-      ba.dkv = w.dkv;
-      Timed tm("bwd_gate_conv", hs);
-      if (launch_bwd_gate_conv(ba, hs) != hipSuccess) return ENGRAM_E_HIP;
-    }
-    {
-      Timed tm("transpose_w", hs);
-      if (launch_transpose_w((const uint8_t*)p->w_kv, w.wt, 2 * s.d, s.d_mem, s.dtype, hs) !=
-          hipSuccess)
-        return ENGRAM_E_HIP;
-    }
-    {
-      GemmArgs ga;
-      std::memset(&ga, 0, sizeof(ga));
-      ga.A = w.wt;
-      ga.B = w.dkv;
-      ga.M = N;
-      ga.F = s.d_mem;
-      ga.K = 2 * s.d;
-      ga.group_m = 4;
-      ga.stage_bytes = kBwdStageBytes;
-      ga.persistent = ENGRAM_GEMM_PERSISTENT;
-      ga.c_out = w.de;
-      Timed tm("de_gemm", hs);
-      if (launch_gemm(bf ? GEMM_F16 : GEMM_F32, EPI_STORE_F32, ga, hs) != hipSuccess)
-        return ENGRAM_E_HIP;
-    }
-  }
   if (out->mode == ENGRAM_GRAD_ATOMIC_DENSE) {
     Timed tm("atomic_scatter", hs);
     return hip_status(launch_atomic_scatter(sa, hs));
@@ -474,6 +568,14 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
   carve_sort(w.sort, N, s.J, &sb);
   Timed tm("sorted_scatter", hs);
   return hip_status(launch_sorted_scatter(sa, sb, out->mode, hs));
+}
+
+engram_status engram_backward_table_grad(const engram_config* cfg, const engram_params* p,
+                                         const void* hidden, const void* dy, int64_t B, int64_t T,
+                                         const engram_saved* saved, engram_table_grad* out,
+                                         void* workspace, size_t ws_bytes, void* stream) {
+  if (!out) return ENGRAM_E_INVALID;
+  return engram_backward(cfg, p, hidden, dy, B, T, saved, out, nullptr, workspace, ws_bytes, stream);
 }
 
 engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* canon_map_host,

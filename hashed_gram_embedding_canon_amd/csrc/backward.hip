@@ -21,6 +21,12 @@
 //   B: dalpha_t from the per-wave sums; dk_t from h_t and k_t, whose loads
 //      do not depend on each other.
 // dk and dv leave as fp16 (bf16 io) or fp32 (fp32 io): the de GEMM operands.
+// With PARAMS the same passes also give what the module's own parameters
+// need: pass A sums dz_t vt_{t-i} per tap over the workgroup's tokens (the
+// conv weights' gradient), pass B writes the gate's part of dh_t,
+//   dh_t = ca g_q g_k k_t - cq h_t,  cq = rq^3 ds rk P / (sqrt(d) d)
+// (the query's RMSNorm backward, the mirror of dk), and sums
+// ca h_t k_t, of which the RMSNorm scales' gradients are g_k and g_q times.
 #include <type_traits>
 
 #include "kernels.h"
@@ -63,6 +69,16 @@ __device__ inline void st4_grad(uint8_t* base, int64_t elem, const float* v) {
   }
 }
 
+// bf16 (round to nearest even) or fp32 store of 4 values in the io dtype
+template <bool BF16>
+__device__ inline void st4_io(uint8_t* base, int64_t elem, const float* v) {
+  if constexpr (BF16) {
+    *reinterpret_cast<u32x2*>(base + elem * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else {
+    *reinterpret_cast<floatx4*>(base + elem * 4) = floatx4{v[0], v[1], v[2], v[3]};
+  }
+}
+
 // p[0..7]: this lane's shares of 8 tokens.  Returns the wave-wide sum of
 // token 4*b5 + 2*b4 + b3 (b = lane bits): each halving step sends the half
 // of the values that the partner keeps.
@@ -88,8 +104,11 @@ __device__ inline float wave_sum8(float p[8], int lane) {
   return x;
 }
 
-template <bool BF16, int TAPS>
-__global__ __launch_bounds__(1024) void bwd_gate_conv_kernel(BwdArgs a) {
+// MAXT: the largest block it is launched with.  One workgroup of d/4 lanes
+// fits a CU at d = 2560 whatever the register count up to 168, and the
+// parameter sums need more than the 128 that 1024 threads leave.
+template <bool BF16, int TAPS, bool PARAMS, int MAXT>
+__global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   constexpr int R = kBwTokens;
   constexpr int NH = TAPS - 1;
   constexpr int NW = NH > 0 ? NH : 1;
@@ -153,6 +172,18 @@ __global__ __launch_bounds__(1024) void bwd_gate_conv_kernel(BwdArgs a) {
   float pb[kBwBatch];
 #pragma unroll
   for (int k = 0; k < kBwBatch; ++k) pb[k] = 0.f;
+  // PARAMS: sum over this block's tokens of dz_u vt_{u-i} (tap i); written
+  // out after pass A
+  float dcw[PARAMS ? 4 : 1][PARAMS ? TAPS : 1];
+  if constexpr (PARAMS) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < TAPS; ++i) dcw[c][i] = 0.f;
+  }
+  float* const pdst = PARAMS && a.pacc ? a.pacc + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) *
+                                                      d * (TAPS + 1) + (int64_t)f * (TAPS + 1)
+                                       : nullptr;
 
   // one step of pass A at u (slot k = (u - ubeg) % RS, compile-time)
   auto step = [&](int64_t u, int k) __attribute__((always_inline)) {
@@ -172,6 +203,17 @@ __global__ __launch_bounds__(1024) void bwd_gate_conv_kernel(BwdArgs a) {
       for (int i = 1; i < TAPS; ++i) z += w[c][i] * vtw[i - 1][c];
       const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
       dz[c] = live ? G[c] * sg * (1.0f + z * (1.0f - sg)) : 0.f;
+    }
+    if constexpr (PARAMS) {
+      // u's own tokens only: u in [tend, tend + NH) belongs to the next block
+      if (u < tend) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          dcw[c][0] += dz[c] * vt[c];
+#pragma unroll
+          for (int i = 1; i < TAPS; ++i) dcw[c][i] += dz[c] * vtw[i - 1][c];
+        }
+      }
     }
 #pragma unroll
     for (int i = TAPS - 1; i > 0; --i)
@@ -227,6 +269,14 @@ __global__ __launch_bounds__(1024) void bwd_gate_conv_kernel(BwdArgs a) {
       }
     }
   }
+  if constexpr (PARAMS) {
+    if (pdst) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < TAPS; ++i) pdst[c * (TAPS + 1) + i] = dcw[c][i];
+    }
+  }
   __syncthreads();
   if (threadIdx.x < R) {
     float s = 0.f;
@@ -240,6 +290,11 @@ __global__ __launch_bounds__(1024) void bwd_gate_conv_kernel(BwdArgs a) {
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     gqk[c] = (a.gamma_q ? a.gamma_q[f + c] : 1.f) * (a.gamma_k ? a.gamma_k[f + c] : 1.f);
+  float sgs[PARAMS ? 4 : 1];  // PARAMS: sum over tokens of ca h k
+  if constexpr (PARAMS) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sgs[c] = 0.f;
+  }
   constexpr int UB = 4;
   for (int i0 = 0; i0 < R; i0 += UB) {
     raw4_t<BF16> rh[UB], rk[UB];
@@ -266,16 +321,42 @@ __global__ __launch_bounds__(1024) void bwd_gate_conv_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) dk[c] = ca * gqk[c] * hv[c] - cb * kv[c];
       st4_grad<BF16>(a.dkv, (row0 + t) * 2 * d + f, dk);
+      if constexpr (PARAMS) {
+        const float cq = rq * rq * rq * ds * rkk * P * inv_sqrt_d * inv_d;
+        float dh[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          dh[c] = ca * gqk[c] * kv[c] - cq * hv[c];
+          sgs[c] += ca * hv[c] * kv[c];
+        }
+        if (a.dh) st4_io<BF16>(a.dh, (row0 + t) * d + f, dh);
+      }
+    }
+  }
+  if constexpr (PARAMS) {
+    if (pdst) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pdst[c * (TAPS + 1) + TAPS] = sgs[c];
+    }
+    // zero rows after the last token, for the weight-gradient GEMM's last stage
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+      const float z4[4] = {0.f, 0.f, 0.f, 0.f};
+      const int64_t N = a.B * T;
+      for (int r = 0; r < a.pad_rows; ++r) {
+        st4_grad<BF16>(a.dkv, (N + r) * 2 * d + f, z4);
+        st4_grad<BF16>(a.dkv, (N + r) * 2 * d + d + f, z4);
+      }
     }
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool PARAMS, int MAXT>
 static hipError_t launch_bwd_taps(const BwdArgs& a, dim3 grid, int threads, hipStream_t s) {
   switch (a.taps) {
-#define ENGRAM_TAPS_CASE(K)                                                               \
-  case K:                                                                                 \
-    hipLaunchKernelGGL((bwd_gate_conv_kernel<BF16, K>), grid, dim3(threads), 0, s, a); \
+#define ENGRAM_TAPS_CASE(K)                                                                   \
+  case K:                                                                                     \
+    hipLaunchKernelGGL((bwd_gate_conv_kernel<BF16, K, PARAMS, MAXT>), grid, dim3(threads), 0, \
+                       s, a);                                                                 \
     break;
     ENGRAM_TAPS_CASE(1)
     ENGRAM_TAPS_CASE(2)
@@ -298,8 +379,94 @@ hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s) {
   if (a.d % 256 != 0 || a.d / 4 > 64 * kBwMaxWaves) return hipErrorInvalidValue;
   const int threads = a.d / 4;
   dim3 grid((unsigned)((a.T + kBwTokens - 1) / kBwTokens), (unsigned)a.B);
-  return a.io_dtype == ENGRAM_BF16 ? launch_bwd_taps<true>(a, grid, threads, s)
-                                   : launch_bwd_taps<false>(a, grid, threads, s);
+  const bool params = a.pacc || a.dh || a.pad_rows > 0;
+  if (a.pad_rows < 0 || a.pad_rows > 64) return hipErrorInvalidValue;
+  const bool narrow = threads <= 768;
+  if (a.io_dtype == ENGRAM_BF16) {
+    if (!params) return launch_bwd_taps<true, false, 1024>(a, grid, threads, s);
+    return narrow ? launch_bwd_taps<true, true, 768>(a, grid, threads, s)
+                  : launch_bwd_taps<true, true, 1024>(a, grid, threads, s);
+  }
+  if (!params) return launch_bwd_taps<false, false, 1024>(a, grid, threads, s);
+  return narrow ? launch_bwd_taps<false, true, 768>(a, grid, threads, s)
+                : launch_bwd_taps<false, true, 1024>(a, grid, threads, s);
+}
+
+int64_t bwd_blocks(int64_t B, int64_t T) { return B * ((T + kBwTokens - 1) / kBwTokens); }
+
+// ------------------------------------------------------------- parameter sums
+// dst[c][e] = sum of src rows c*64 .. c*64+63 (< rows) in column e, in order
+__global__ __launch_bounds__(256) void colsum64_kernel(const float* __restrict__ src,
+                                                       float* __restrict__ dst, int64_t rows,
+                                                       int64_t cols) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int64_t r1 = r0 + 64 < rows ? r0 + 64 : rows;
+  float acc = 0.f;
+  for (int64_t r = r0; r < r1; ++r) acc += src[r * cols + e];
+  dst[(int64_t)blockIdx.y * cols + e] = acc;
+}
+
+// sums [d][taps+1] -> dconv [d][taps], dgq = g_k S, dgk = g_q S
+__global__ __launch_bounds__(256) void param_finish_kernel(const float* __restrict__ sums, int32_t d,
+                                                           int32_t taps, const float* gamma_q,
+                                                           const float* gamma_k, float* dconv,
+                                                           float* dgq, float* dgk) {
+  const int f = blockIdx.x * 256 + threadIdx.x;
+  if (f >= d) return;
+  const float* sf = sums + (int64_t)f * (taps + 1);
+  if (dconv)
+    for (int i = 0; i < taps; ++i) dconv[(int64_t)f * taps + i] = sf[i];
+  const float S = sf[taps];
+  if (dgq) dgq[f] = (gamma_k ? gamma_k[f] : 1.f) * S;
+  if (dgk) dgk[f] = (gamma_q ? gamma_q[f] : 1.f) * S;
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+int64_t bwd_param_tmp_floats(int64_t nblk, int32_t d, int32_t taps) {
+  const int64_t cols = (int64_t)d * (taps + 1);
+  int64_t rows = nblk, total = 0;
+  while (rows > 1) {
+    rows = (rows + 63) / 64;
+    total += rows * cols;
+  }
+  return total;
+}
+
+hipError_t launch_bwd_param_sums(const float* pacc, float* tmp, int64_t nblk, int32_t d,
+                                 int32_t taps, const float* gamma_q, const float* gamma_k,
+                                 float* dconv, float* dgq, float* dgk, hipStream_t s) {
+  if (nblk <= 0) return hipErrorInvalidValue;
+  const int64_t cols = (int64_t)d * (taps + 1);
+  // passes of 64-row sums, each into a fresh region of tmp, until one row is left
+  const float* src = pacc;
+  float* dst = tmp;
+  int64_t rows = nblk;
+  while (rows > 1) {
+    const int64_t groups = (rows + 63) / 64;
+    if (groups > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(colsum64_kernel, dim3((unsigned)((cols + 255) / 256), (unsigned)groups),
+                       dim3(256), 0, s, src, dst, rows, cols);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    src = dst;
+    dst += groups * cols;
+    rows = groups;
+  }
+  hipLaunchKernelGGL(param_finish_kernel, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, s, src,
+                     d, taps, gamma_q, gamma_k, dconv, dgq, dgk);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------- W transpose

@@ -85,8 +85,37 @@ struct BwdArgs {
   const float* gamma_q;
   const float* gamma_k;
   uint8_t* dkv;           // [N][2d] fp16 (bf16 io) or fp32 (f32 io)
+  // parameter gradients (null = not wanted)
+  float* pacc;            // [nblk][d][taps+1]: per workgroup, sum_t dz_t vt_{t-i} per tap and
+                          // sum_t (ds rq rk / sqrt d) h_t k_t (the RMSNorm scales' shared sum)
+  uint8_t* dh;            // [N][d] io dtype: the gate's part of dL/dh
+  int32_t pad_rows;       // zero rows N .. N+pad_rows-1 of dkv are written too
 };
 hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s);
+int64_t bwd_blocks(int64_t B, int64_t T);  // workgroups of the backward, rows of pacc
+// pacc -> dconv [d][taps] and the RMSNorm scale gradients dgq = g_k S, dgk =
+// g_q S (each output may be null); tmp holds bwd_param_tmp_floats() floats
+int64_t bwd_param_tmp_floats(int64_t nblk, int32_t d, int32_t taps);
+hipError_t launch_bwd_param_sums(const float* pacc, float* tmp, int64_t nblk, int32_t d,
+                                 int32_t taps, const float* gamma_q, const float* gamma_k,
+                                 float* dconv, float* dgq, float* dgk, hipStream_t s);
+
+// Weight gradients dW[i][j] = sum_t X[t][i] Y[t][j] over token-major operands.
+struct GemmTnArgs {
+  const uint8_t* x;  // [round_up(K, 32)][ldx] fp16 (GEMM_F16) or fp32; rows >= K are zero
+  const uint8_t* y;  // [K][ldy] bf16 (GEMM_F16, widened in registers) or fp32
+  int64_t ldx, ldy;  // row strides in elements
+  int64_t K;         // tokens
+  int32_t m, n;      // output rows (columns of X) and columns (of Y), multiples of 256
+  int32_t splits;    // token chunks of kchunk tokens (the last may be short or empty)
+  int64_t kchunk;    // a multiple of 32
+  float* out;        // [splits][m][n] fp32 slices (unused with one split)
+};
+int tn_splits(int64_t K, int32_t m, int32_t n);
+// p[0..n) = 0 (a kernel, so that it can sit in a captured graph)
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+// dst [m][n] fp32 = the sum of the splits' slices, in order
+hipError_t launch_gemm_tn(GemmType type, const GemmTnArgs& g, float* dst, hipStream_t s);
 
 // W_kv [2d][d_mem] (io dtype) -> Wt [d_mem][2d] (fp16 for bf16 io, fp32 for f32 io)
 hipError_t launch_transpose_w(const uint8_t* w, uint8_t* wt, int32_t rows, int32_t cols,

@@ -165,7 +165,27 @@ typedef struct {
   float* dense[ENGRAM_MAX_TABLES]; /* DENSE: device [M_j][D] fp32, gradients are ADDED (caller zeroes) */
 } engram_table_grad;
 
-enum { ENGRAM_OP_FORWARD = 0, ENGRAM_OP_BACKWARD = 1 };
+/*
+ * Gradients of the module's own parameters and of the hidden state, output of
+ * engram_backward().  Every member may be NULL (not computed).  Outputs are
+ * overwritten, not added to.  Chain rule through the forward of "DeepSeek AI
+ * II", section "DeepSeek Engram" (the pages print no backward).
+ */
+typedef struct {
+  float* w_kv;     /* [2d][d_mem] fp32: dL/dW_KV = sum_t [dk_t; dv_t] e_t^T, rows as in
+                      params->w_kv (the key rows, then the value rows) */
+  float* conv_w;   /* [d][conv_kernel] fp32: sum_t dz_t[c] vt_{t-i}[c] */
+  float* gamma_q;  /* [d] fp32: dL/dg_q (of params->gamma_q, or of all-ones scales when NULL) */
+  float* gamma_k;  /* [d] fp32: dL/dg_k */
+  void* hidden;    /* [B][T][d] dtype: the gate's part of dL/dh_t through the query's RMSNorm
+                      (the residual H + Y adds G itself, which is the caller's) */
+} engram_param_grad;
+
+enum {
+  ENGRAM_OP_FORWARD = 0,
+  ENGRAM_OP_BACKWARD = 1,         /* engram_backward with table gradients only */
+  ENGRAM_OP_BACKWARD_PARAMS = 2   /* engram_backward with parameter gradients too */
+};
 
 /* Bytes of device workspace the operation needs for B x T tokens (0 on bad config). */
 size_t engram_workspace_size(const engram_config* cfg, int64_t B, int64_t T, int32_t op);
@@ -216,6 +236,27 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
                                          const void* hidden, const void* dy, int64_t B, int64_t T,
                                          const engram_saved* saved, engram_table_grad* out,
                                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Training backward: the table gradients of engram_backward_table_grad() and
+ * the gradients of the projections, the conv taps, the RMSNorm scales and
+ * the hidden state (see engram_param_grad), from one pass through the conv
+ * and the gate.  table_out or param_out may be NULL (not computed), not both.
+ *   saved: idx, stats, k, v as for the table gradients; saved->e, when given,
+ *   is read for dW_KV, otherwise the rows are gathered again from
+ *   params->tables through saved->idx (which must then be table-local: a
+ *   forward over device tables, not a compact plan);
+ *   workspace: >= engram_workspace_size(cfg, B, T, ENGRAM_OP_BACKWARD_PARAMS)
+ *   when param_out is given, else ENGRAM_OP_BACKWARD.
+ * dW_KV takes its operands in fp16 (bf16 io) like the de contraction and sums
+ * in fp32 over token chunks, the chunks in a fixed order (deterministic).
+ * One branch only (branches 0 or 1), d a multiple of 256, d_mem of 256.
+ */
+engram_status engram_backward(const engram_config* cfg, const engram_params* params,
+                              const void* hidden, const void* dy, int64_t B, int64_t T,
+                              const engram_saved* saved, engram_table_grad* table_out,
+                              engram_param_grad* param_out, void* workspace, size_t ws_bytes,
+                              void* stream);
 
 /*
  * Prefetch plan for tables held in host memory ("DeepSeek AI II",

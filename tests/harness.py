@@ -133,6 +133,25 @@ class DeviceProblem:
         return res
 
 
+    def backward_params(self, saved_bufs, dy, want=("w_kv", "conv_w", "gamma_q", "gamma_k", "hidden"),
+                        ws=None):
+        """engram_backward with parameter gradients only -> dict of tensors."""
+        torch = torch_mod()
+        eg, wl = self.eg, self.wl
+        d = wl.hidden
+        shapes = {"w_kv": ((2 * d, wl.d_mem), torch.float32), "conv_w": ((d, wl.taps), torch.float32),
+                  "gamma_q": ((d,), torch.float32), "gamma_k": ((d,), torch.float32),
+                  "hidden": ((self.B, self.T, d), self.tdtype)}
+        res = {k: torch.full(shapes[k][0], float("nan"), dtype=shapes[k][1], device=self.device)
+               for k in want}
+        pg = eg.make_param_grad(**res)
+        if ws is None:
+            ws = self.workspace(eg.ENGRAM_OP_BACKWARD_PARAMS)
+        eg.engram_backward(self.cfg, self.params, self.hidden, dy, B=self.B, T=self.T,
+                           saved=eg.make_saved(**saved_bufs), param_out=pg, workspace=ws)
+        return res
+
+
 def oracle_problem(inp: synth.Inputs, tokens=None, hidden=None, branch=0):
     """The oracle's problem for one branch: its W_K and hidden state, the shared
     tables, W_V and conv."""

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(eg):
     names = _declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     L = ctypes.CDLL(eg.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -60,6 +60,8 @@ def test_workspace_sizes(eg):
     f = eg.engram_workspace_size(cfg, 2, 100, eg.ENGRAM_OP_FORWARD)
     b = eg.engram_workspace_size(cfg, 2, 100, eg.ENGRAM_OP_BACKWARD)
     assert f > 200 * 256 * 4 and b > f  # e alone is N*d_mem*4 bytes
+    bp = eg.engram_workspace_size(cfg, 2, 100, eg.ENGRAM_OP_BACKWARD_PARAMS)
+    assert bp > b  # the rows gathered again, dW slices and per-block sums on top
     assert eg.engram_workspace_size(cfg, 2, 100, 7) == 0
     assert eg.engram_workspace_size(_cfg(eg, hidden=200), 2, 100, 0) == 0
     assert eg.engram_workspace_size(cfg, -1, 100, 0) == 0
@@ -116,6 +118,19 @@ def test_backward_and_hash_validation(eg):
     out.mode = eg.ENGRAM_GRAD_ATOMIC_DENSE  # dense pointers missing
     assert L.engram_backward_table_grad(cfg.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, ctypes.byref(sv),
                                         ctypes.byref(out), FAKE, 1 << 40, None) == eg.ENGRAM_E_INVALID
+    # engram_backward: at least one output; parameter grads need d_mem % 256 == 0
+    out.mode = eg.ENGRAM_GRAD_SORTED_SPARSE
+    assert L.engram_backward(cfg.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, ctypes.byref(sv), None,
+                             None, FAKE, 1 << 40, None) == eg.ENGRAM_E_INVALID
+    pg = eg.make_param_grad(w_kv=FAKE, conv_w=FAKE)
+    assert L.engram_backward(cfg.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, ctypes.byref(sv), None,
+                             ctypes.byref(pg), FAKE, 16, None) == eg.ENGRAM_E_WORKSPACE
+    pg_bad = eg.make_param_grad(w_kv=FAKE + 4)
+    assert L.engram_backward(cfg.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, ctypes.byref(sv), None,
+                             ctypes.byref(pg_bad), FAKE, 1 << 40, None) == eg.ENGRAM_E_INVALID
+    odd = _cfg(eg, dim=40)  # d_mem = 320
+    assert L.engram_backward(odd.ref, ctypes.byref(p), FAKE, FAKE, 2, 8, ctypes.byref(sv), None,
+                             ctypes.byref(pg), FAKE, 1 << 40, None) == eg.ENGRAM_E_UNSUPPORTED
     assert L.engram_hash_indices(cfg.ref, None, FAKE, 2, 8, FAKE, None) == eg.ENGRAM_E_INVALID
     assert L.engram_hash_indices(cfg.ref, FAKE, FAKE, 0, 8, FAKE, None) == eg.ENGRAM_OK
 
