@@ -224,9 +224,31 @@ def backward_units(wl, N):
     }
 
 
+def training_units(wl, N):
+    """The training backward's extra kernels (parameter and hidden-state
+    gradients) on top of backward_units."""
+    es = 2 if wl.dtype == "bf16" else 4
+    eg_ = 2 if wl.dtype == "bf16" else 4
+    J, d, dm, taps = wl.J, wl.hidden, wl.d_mem, wl.taps
+    nblk = wl.B * ((wl.T + 63) // 64)
+    u = backward_units(wl, N)
+    # dh written and the per-workgroup conv / RMSNorm-scale sums
+    u["bwd_gate_conv"] = {"bound": "hbm", "bytes": u["bwd_gate_conv"]["bytes"] + N * d * es
+                          + nblk * d * (taps + 1) * 4}
+    # rows gathered again: indices + rows in, e out
+    u["gather"] = {"bound": "hbm", "bytes": N * J * 4 + 2 * N * dm * es}
+    # dW = [dk|dv]^T e: both token-major operands once, dW once
+    u["dw_gemm"] = {"bound": "mfma", "flops": 2 * N * 2 * d * dm,
+                    "bytes": N * 2 * d * eg_ + N * dm * es + 2 * d * dm * 4}
+    u["bwd_param_sums"] = {"bound": "hbm", "bytes": nblk * d * (taps + 1) * 4}
+    return u
+
+
 def bench_backward(dp, inp, steps: int) -> dict:
-    """Table-gradient backward of the same workload: sorted segmented reduce
-    (sparse rows) and the dense-atomic variant, per-kernel times and rates."""
+    """Backward of the same workload: the table gradients by sorted segmented
+    reduce (sparse rows) and by the dense-atomic variant, and the training
+    backward (sorted table gradients plus dW_KV, conv taps, RMSNorm scales and
+    dh, e gathered again); per-kernel times and rates."""
     import torch
 
     import hashed_gram_embedding_canon_amd as eg
@@ -235,12 +257,18 @@ def bench_backward(dp, inp, steps: int) -> dict:
     saved = dp.alloc_saved(("idx", "stats", "k", "v"))
     dp.forward(saved)
     dy = H.to_dev(inp.dy)
-    ws = dp.workspace(eg.ENGRAM_OP_BACKWARD)
-    units = backward_units(wl, N)
+    ws = dp.workspace(eg.ENGRAM_OP_BACKWARD_PARAMS)
     res = {}
     for mode, label in ((eg.ENGRAM_GRAD_SORTED_SPARSE, "sorted_sparse"),
-                        (eg.ENGRAM_GRAD_ATOMIC_DENSE, "atomic_dense")):
+                        (eg.ENGRAM_GRAD_ATOMIC_DENSE, "atomic_dense"),
+                        (eg.ENGRAM_GRAD_SORTED_SPARSE, "training")):
+        training = label == "training"
+        units = training_units(wl, N) if training else backward_units(wl, N)
         out = dp.backward(saved, dy, mode, ws=ws)  # warm-up; allocates the outputs
+        pgrads, pg = None, None
+        if training:
+            pgrads = dp.backward_params(saved, dy, ws=ws)
+            pg = eg.make_param_grad(**pgrads)
         torch.cuda.synchronize()
         tg = eg.engram_table_grad()
         tg.mode = mode
@@ -265,8 +293,12 @@ def bench_backward(dp, inp, steps: int) -> dict:
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         for _ in range(steps):
-            eg.engram_backward_table_grad(dp.cfg, dp.params, dp.hidden, dy, B=dp.B, T=dp.T,
-                                          saved=sv, out=tg, workspace=ws)
+            if training:
+                eg.engram_backward(dp.cfg, dp.params, dp.hidden, dy, B=dp.B, T=dp.T, saved=sv,
+                                   table_out=tg, param_out=pg, workspace=ws)
+            else:
+                eg.engram_backward_table_grad(dp.cfg, dp.params, dp.hidden, dy, B=dp.B, T=dp.T,
+                                              saved=sv, out=tg, workspace=ws)
         t1.record()
         torch.cuda.synchronize()
         eg.engram_profile_enable(False)
@@ -291,8 +323,11 @@ def bench_backward(dp, inp, steps: int) -> dict:
         if zero_ms is not None:
             entry["zero_dense_ms_excluded"] = round(zero_ms, 3)
             entry["note"] = "accumulates into the caller's dense fp32 tables without zeroing them"
+        if training:
+            entry["note"] = ("table gradients (sorted) + dW_KV, conv taps, RMSNorm scales, dh; "
+                             "e gathered again from the tables")
         res[label] = entry
-        del out
+        del out, pgrads
         torch.cuda.empty_cache()
     return res
 
@@ -599,7 +634,7 @@ def main():
         "kernels": kernels,
     }
     if not args.no_backward:
-        log(f"[bench] table-gradient backward, {args.backward_steps} steps per mode")
+        log(f"[bench] backward (table gradients; training), {args.backward_steps} steps per mode")
         out["backward"] = bench_backward(dp, inp, args.backward_steps)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on host cores for ~{args.cpu_seconds:.0f} s")

@@ -186,7 +186,7 @@ size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out,
 }
 
 struct BwdWs {
-  uint8_t* dkv;    // [round_up(N, 32)][2d]: the weight-gradient GEMM reads whole 32-token stages
+  uint8_t* dkv;    // [round_up(N, 64)][2d]: the weight-gradient GEMM reads whole stages
   uint8_t* wt;
   float* de;
   uint8_t* sort;
@@ -198,7 +198,7 @@ struct BwdWs {
   int32_t splits;
 };
 
-int64_t round32(int64_t n) { return (n + 31) / 32 * 32; }
+int64_t round_pad(int64_t n) { return (n + kTnPadTokens - 1) / kTnPadTokens * kTnPadTokens; }
 
 // table: de GEMM and scatter buffers; params: the parameter-gradient buffers
 // (e only when need_e)
@@ -213,7 +213,7 @@ size_t backward_ws(const Shape& s, int64_t B, int64_t T, BwdWs* out, uint8_t* ba
     return p;
   };
   BwdWs w{};
-  w.dkv = take((size_t)round32(N) * 2 * s.d * eg);
+  w.dkv = take((size_t)round_pad(N) * 2 * s.d * eg);
   if (table) {
     w.wt = take((size_t)s.d_mem * 2 * s.d * eg);
     w.de = (float*)take((size_t)N * s.d_mem * 4);
@@ -469,7 +469,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
     if (pg) {
       ba.pacc = want_sums ? w.pacc : nullptr;
       ba.dh = (uint8_t*)pg->hidden;
-      ba.pad_rows = want_w ? (int32_t)(round32(N) - N) : 0;
+      ba.pad_rows = want_w ? (int32_t)(round_pad(N) - N) : 0;
     }
     Timed tm("bwd_gate_conv", hs);
     if (launch_bwd_gate_conv(ba, hs) != hipSuccess) return ENGRAM_E_HIP;
@@ -539,7 +539,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
         ta.m = 2 * s.d;
         ta.n = s.d_mem;
         ta.splits = w.splits;
-        ta.kchunk = ((N + 31) / 32 + w.splits - 1) / w.splits * 32;
+        ta.kchunk = ((N + kTnPadTokens - 1) / kTnPadTokens + w.splits - 1) / w.splits * kTnPadTokens;
         ta.out = w.dw_part;
         Timed tm("dw_gemm", hs);
         if (launch_gemm_tn(bf ? GEMM_F16 : GEMM_F32, ta, pg->w_kv, hs) != hipSuccess)

@@ -23,27 +23,40 @@
 
 namespace engram {
 
+// Stage shapes: KS tokens per stage in a ring of NS stages; both operands of
+// all stages fill 128 KB of LDS.
+#ifndef ENGRAM_TN_KS
+#define ENGRAM_TN_KS 32
+#endif
+#ifndef ENGRAM_TN_NS
+#define ENGRAM_TN_NS 4
+#endif
 template <int GT>
 struct TnShape;
 template <>
 struct TnShape<GEMM_F16> {
   static constexpr int ES = 2;   // bytes per element in LDS (fp16 X, bf16 Y)
-  static constexpr int KS = 32;  // tokens per stage
+  static constexpr int KS = ENGRAM_TN_KS;  // tokens per stage
+  static constexpr int NS = ENGRAM_TN_NS;  // stages in the ring
   static constexpr int KK = 16;  // tokens per MFMA step (8 per lane half)
 };
 template <>
 struct TnShape<GEMM_F32> {
   static constexpr int ES = 4;
   static constexpr int KS = 16;
+  static constexpr int NS = 4;
   static constexpr int KK = 8;   // 4 per lane half, four 32x32x2 MFMAs
 };
-constexpr int kTnStages = 4;
-constexpr int kTnOperand = 16384;  // bytes of one operand in one stage: KS rows x 256 x ES
+static_assert(TnShape<GEMM_F16>::KS <= kTnPadTokens && kTnPadTokens % TnShape<GEMM_F16>::KS == 0, "");
 
 // 16-byte piece p of LDS row r sits at piece p ^ tn_swz(r).  A transposing
-// read covers 4 consecutive rows; with this map the 4 x 64 bytes that a half
-// wave reads fall on distinct banks.
-__device__ inline int tn_swz(int r) { return (r & 3) << 2; }
+// read covers 4 consecutive rows x 32 bytes per 16 lanes; XOR with 2(r & 3)
+// spreads them over 8 distinct pieces (measured 2 % faster than 4(r & 3),
+// which separates the 64-byte spans of a half wave instead).
+#ifndef ENGRAM_TN_SWZ
+#define ENGRAM_TN_SWZ 1
+#endif
+__device__ inline int tn_swz(int r) { return (r & 3) << ENGRAM_TN_SWZ; }
 
 typedef __fp16 half4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) half4_t lds_half4;
@@ -66,11 +79,11 @@ __device__ inline uint32_t bf16x2_to_f16x2(uint32_t u) {
 template <int GT>
 __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
   using S = TnShape<GT>;
-  constexpr int ES = S::ES, KS = S::KS, KK = S::KK;
-  constexpr int RB = 256 * ES;             // bytes of a token row in LDS
-  constexpr int NS = kTnStages;
-  constexpr int NL = kTnOperand / (256 * 16);  // loads per operand, thread and stage (4)
-  static_assert(KS * RB == kTnOperand, "");
+  constexpr int ES = S::ES, KS = S::KS, KK = S::KK, NS = S::NS;
+  constexpr int RB = 256 * ES;              // bytes of a token row in LDS
+  constexpr int kTnOperand = KS * RB;       // bytes of one operand in one stage
+  constexpr int NL = kTnOperand / (256 * 16);  // loads per operand, thread and stage
+  static_assert(NS * 2 * kTnOperand == 131072, "");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * 2 * kTnOperand];
 
   // ---- work item: XCD-major so that the items one XCD runs at a time share
@@ -99,8 +112,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
 
   // ---- loads: wave-wide load q of an operand fills bytes [L*1024, L*1024+1024)
   // of the stage (L = wave*NL + q): token row r, slot s, logical piece s^swz(r)
-  uint32_t voffX[NL], voffY[NL];
+  uint32_t voffX[NL];
   int rowL[NL], pieceL[NL];
+  const int ldyb = (int)(g.ldy * ES);  // bytes per Y row (< 2^26, checked at launch)
 #pragma unroll
   for (int q = 0; q < NL; ++q) {
     const int byte = (wave * NL + q) * 1024 + lane * 16;
@@ -109,7 +123,6 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
     rowL[q] = r;
     pieceL[q] = p;
     voffX[q] = (uint32_t)(r * g.ldx * ES + p * 16);
-    voffY[q] = (uint32_t)(r * g.ldy * ES + p * 16);
   }
   const uint32_t lds0 = lds_addr(ring);
   // Stage st into ring slot sl.  Rows of X at and beyond K are zero in
@@ -123,18 +136,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
     const uint8_t* by = g.y + (k0 * g.ldy + j0) * ES;
     const uint32_t mx = lds0 + sl * 2 * kTnOperand + wave * NL * 1024;
     const uint32_t my = mx + kTnOperand;
-    const bool tail = k0 + KS > g.K;  // uniform
+    // last row of Y in this stage (KS-1 except in the stage holding row K-1)
+    const int last = (int)(g.K - 1 - k0 < KS - 1 ? g.K - 1 - k0 : KS - 1);
 #pragma unroll
     for (int q = 0; q < NL; ++q) load_lds16_s(voffX[q], bx, mx + q * 1024);
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      uint32_t vo = voffY[q];
-      if (tail) {
-        const int64_t last = g.K - 1 - k0;
-        const int64_t r = rowL[q] < last ? rowL[q] : last;
-        vo = (uint32_t)(r * g.ldy * ES + pieceL[q] * 16);
-      }
-      load_lds16_s(vo, by, my + q * 1024);
+      const int r = rowL[q] < last ? rowL[q] : last;
+      load_lds16_s((uint32_t)(r * ldyb + pieceL[q] * 16), by, my + q * 1024);
     }
   };
 
@@ -146,8 +155,9 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
 
   const lds_u8* lbase = (const lds_u8*)(const __attribute__((address_space(3))) void*)ring;
   // Fragment of 32 columns (block blk of this wave's 128) at MFMA step ss of
-  // the operand tile at byte `tb`: 8 K values of column cb + l32 per lane.
-  auto frag = [&](uint32_t tb, int cb, int ss, bool widen) __attribute__((always_inline)) {
+  // the operand tile at byte `tb`: 8 K values of column cb + l32 per lane,
+  // as stored (Y still in bf16).
+  auto frag = [&](uint32_t tb, int cb, int ss) __attribute__((always_inline)) {
     u32x4 f;
     if constexpr (GT == GEMM_F16) {
       const int j = lane & 15;
@@ -157,10 +167,6 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
       const u32x2 lo = read_tr16(lbase, tb + r0 * RB + ((pc ^ tn_swz(r0)) * 16) + in);
       const u32x2 hi = read_tr16(lbase, tb + (r0 + 4) * RB + ((pc ^ tn_swz(r0 + 4)) * 16) + in);
       f = u32x4{lo.x, lo.y, hi.x, hi.y};
-      if (widen) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) f[c] = bf16x2_to_f16x2(f[c]);
-      }
     } else {
       const int col = cb + l32;
       const uint32_t pc = (uint32_t)(col * 4) / 16, in = (uint32_t)(col * 4) % 16;
@@ -173,29 +179,60 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
     return f;
   };
 
+  // Ring protocol.  Stage kt's loads were issued NS-1 stages ahead.  The
+  // wait and barrier for stage kt+1 come before the last MFMA step of stage
+  // kt, so that stage kt+1's first fragments are read while that step's
+  // MFMAs run; within a stage, step s+1's fragments are read during step s.
+  // Waiting for this wave's LDS reads at each barrier makes the slot that
+  // the next issue overwrites free in every wave.
+  constexpr int SP = KS / KK;  // MFMA steps per stage
+  static_assert(SP % 2 == 0, "a stage starts in fragment buffer 0");
+  u32x4 af[2][4], bf[2][4];
+  auto read_step = [&](int slot, int ss, u32x4* a4, u32x4* b4) __attribute__((always_inline)) {
+    const uint32_t tx = (uint32_t)(slot * 2 * kTnOperand);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) a4[a] = frag(tx, wf * 128 + a * 32, ss);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) b4[b] = frag(tx + kTnOperand, wt * 128 + b * 32, ss);
+  };
+  // bf16 Y is widened to fp16 a fragment at a time, each feeding 4 MFMAs, so
+  // the conversions overlap the matrix pipe instead of preceding it
+  auto mfma_step = [&](const u32x4* a4, const u32x4* b4) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      u32x4 y = b4[b];
+      if constexpr (GT == GEMM_F16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] = bf16x2_to_f16x2(y[c]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) Mma<GT>::run(a4[a], y, acc[a][b]);
+    }
+  };
   if (nst > 0) {
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(s, s);
+    ENGRAM_WAIT_VM((NS - 2) * 2 * NL);
+    ENGRAM_BARRIER();
+    read_step(0, 0, af[0], bf[0]);
     for (int kt = 0; kt < nst; ++kt) {
-      ENGRAM_WAIT_VM((NS - 2) * 2 * NL);  // this wave's loads of stage kt are in LDS
-      ENGRAM_BARRIER();                   // everyone's are, and slot (kt-1)%NS is free
-      issue(kt + NS - 1, (kt + NS - 1) % NS);
-      const uint32_t tx = (uint32_t)((kt % NS) * 2 * kTnOperand);
-      const uint32_t ty = tx + kTnOperand;
+      issue(kt + NS - 1, (kt + NS - 1) % NS);  // the slot stage kt-1 used
+      const int slot = kt % NS;
 #pragma unroll
-      for (int ss = 0; ss < KS / KK; ++ss) {
-        u32x4 af[4], bf[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) af[a] = frag(tx, wf * 128 + a * 32, ss, false);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) bf[b] = frag(ty, wt * 128 + b * 32, ss, true);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) Mma<GT>::run(af[a], bf[b], acc[a][b]);
+      for (int ss = 0; ss < SP; ++ss) {
+        const int cur = ss & 1, nxt = cur ^ 1;  // SP is even: stage k starts in buffer 0
+        if (ss + 1 < SP) {
+          read_step(slot, ss + 1, af[nxt], bf[nxt]);
+        } else {
+          __builtin_amdgcn_sched_barrier(0);  // the previous step's MFMAs stay ahead of the wait
+          ENGRAM_WAIT_VM_LDS((NS - 2) * 2 * NL);  // stage kt+1 in LDS, this wave's reads done
+          ENGRAM_BARRIER();
+          if (kt + 1 < nst) read_step((kt + 1) % NS, 0, af[nxt], bf[nxt]);
+        }
+        mfma_step(af[cur], bf[cur]);
       }
     }
-    ENGRAM_WAIT_VM(0);  // the dummy loads of the last iterations
+    ENGRAM_WAIT_VM(0);  // the loads of stages past the end
   }
 
   // ---- epilogue: lane owns column j0 + wt*128 + b*32 + l32 and rows
@@ -229,10 +266,10 @@ __global__ __launch_bounds__(256) void tn_reduce_kernel(const float* __restrict_
 
 int tn_splits(int64_t K, int32_t m, int32_t n) {
   // enough items for 256 CUs with little idle time in the last round, each
-  // split at least 8 stages of 32 tokens
+  // split at least 4 chunks of kTnPadTokens tokens
   const int64_t tiles = (int64_t)(m / 256) * (n / 256);
-  const int64_t k32 = (K + 31) / 32;
-  int smax = (int)std::min<int64_t>(32, std::max<int64_t>(1, k32 / 8));
+  const int64_t kc = (K + kTnPadTokens - 1) / kTnPadTokens;
+  int smax = (int)std::min<int64_t>(32, std::max<int64_t>(1, kc / 4));
   for (int s = 1; s <= smax; ++s) {
     const int64_t items = tiles * s;
     const int64_t rounds = (items + 255) / 256;
@@ -246,9 +283,11 @@ hipError_t launch_gemm_tn(GemmType type, const GemmTnArgs& g0, float* dst, hipSt
   if (g.m % 256 || g.n % 256 || g.m <= 0 || g.n <= 0 || g.K < 0 || g.splits < 1)
     return hipErrorInvalidValue;
   if (type != GEMM_F16 && type != GEMM_F32) return hipErrorInvalidValue;
-  // 32-bit per-lane offsets inside a stage
+  // 32-bit per-lane offsets inside a stage; chunks of whole stages
   const int es = type == GEMM_F16 ? 2 : 4;
-  if ((int64_t)32 * std::max(g.ldx, g.ldy) * es >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if ((int64_t)kTnPadTokens * std::max(g.ldx, g.ldy) * es >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  if (g.kchunk % kTnPadTokens != 0) return hipErrorInvalidValue;
   if (g.splits == 1) g.out = dst;
   const int64_t items = (int64_t)(g.m / 256) * (g.n / 256) * g.splits;
   const int64_t blocks = (items + 7) / 8 * 8;

@@ -101,14 +101,15 @@ hipError_t launch_bwd_param_sums(const float* pacc, float* tmp, int64_t nblk, in
                                  float* dconv, float* dgq, float* dgk, hipStream_t s);
 
 // Weight gradients dW[i][j] = sum_t X[t][i] Y[t][j] over token-major operands.
+constexpr int kTnPadTokens = 64;  // X rows are padded to, and chunks are, multiples of this
 struct GemmTnArgs {
-  const uint8_t* x;  // [round_up(K, 32)][ldx] fp16 (GEMM_F16) or fp32; rows >= K are zero
+  const uint8_t* x;  // [round_up(K, 64)][ldx] fp16 (GEMM_F16) or fp32; rows >= K are zero
   const uint8_t* y;  // [K][ldy] bf16 (GEMM_F16, widened in registers) or fp32
   int64_t ldx, ldy;  // row strides in elements
   int64_t K;         // tokens
   int32_t m, n;      // output rows (columns of X) and columns (of Y), multiples of 256
   int32_t splits;    // token chunks of kchunk tokens (the last may be short or empty)
-  int64_t kchunk;    // a multiple of 32
+  int64_t kchunk;    // a multiple of kTnPadTokens
   float* out;        // [splits][m][n] fp32 slices (unused with one split)
 };
 int tn_splits(int64_t K, int32_t m, int32_t n);
