@@ -82,7 +82,14 @@ def kernel_key(name: str) -> str:
         if epi == "1":
             return "de_gemm"
         return "gather_proj_gemm" if gather == "true" else "proj_gemm"
-    for key in ("bwd_gate_conv", "gate_conv", "gather", "hash", "transpose_w", "atomic_scatter"):
+    if "gemm_tn_kernel" in base or "tn_reduce_kernel" in base:
+        return "dw_gemm"
+    if "colsum64_kernel" in base or "param_finish_kernel" in base:
+        return "bwd_param_sums"
+    if "bwd_gate_conv_kernel<" in base:
+        targs = base.split("<", 1)[1].rstrip(">").replace(" ", "").split(",")
+        return "bwd_gate_conv_params" if targs[2] == "true" else "bwd_gate_conv"
+    for key in ("gate_conv", "gather", "hash", "transpose_w", "atomic_scatter"):
         if f"{key}_kernel" in base:
             return key
     for key in ("sort_", "seg_"):
@@ -108,7 +115,8 @@ def csrc_digest() -> str:
 
 
 # bench names made of several dispatches per call: the kernel that runs once per call
-GROUP_LEADER = {"sorted_scatter": "sort_init_kernel"}
+GROUP_LEADER = {"sorted_scatter": "sort_init_kernel", "dw_gemm": "gemm_tn_kernel",
+                "bwd_param_sums": "param_finish_kernel"}
 
 
 def _pmc_per_kernel(csv_dir: str, counter: str) -> dict:
@@ -135,7 +143,8 @@ def _pmc_per_kernel(csv_dir: str, counter: str) -> dict:
 
 def summarize_trace(trace_dir: str) -> str:
     """Per-kernel durations of a rocprofv3 --kernel-trace run (bench kernels
-    only; several dispatches of one bench name in a row count as one call)."""
+    only; the dispatches in a row of one multi-dispatch bench name count as
+    one call)."""
     import csv
     import glob
     import statistics
@@ -154,15 +163,15 @@ def summarize_trace(trace_dir: str) -> str:
             continue
         ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         names.setdefault(k, set()).add(r["Kernel_Name"].split("(")[0])
-        if k == prev_key and k in GROUP_LEADER and GROUP_LEADER[k] not in r["Kernel_Name"]:
+        if k == prev_key and k in GROUP_LEADER:
             cur[-1] += ns
         else:
             cur = calls.setdefault(k, [])
             cur.append(ns)
         prev_key = k
-    lines = [f"{'kernel':<16} {'calls':>5} {'mean_us':>9} {'median_us':>10} {'min_us':>9} {'max_us':>9}  kernels"]
+    lines = [f"{'kernel':<21} {'calls':>5} {'mean_us':>9} {'median_us':>10} {'min_us':>9} {'max_us':>9}  kernels"]
     for k, v in sorted(calls.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"{k:<16} {len(v):>5} {statistics.mean(v) / 1e3:>9.2f} {statistics.median(v) / 1e3:>10.2f} "
+        lines.append(f"{k:<21} {len(v):>5} {statistics.mean(v) / 1e3:>9.2f} {statistics.median(v) / 1e3:>10.2f} "
                      f"{min(v) / 1e3:>9.2f} {max(v) / 1e3:>9.2f}  {'; '.join(sorted(names[k]))}")
     return "\n".join(lines)
 
@@ -179,12 +188,12 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
     out = [f"source {csrc_digest()}",
            f"copy_calibration bytes {copy_bytes} fetch_kib {cf:.1f} write_kib {cw:.1f} "
            f"fetch_scale {f_scale:.4f} write_scale {w_scale:.4f}",
-           f"{'kernel':<18} {'fetch_kib':>14} {'write_kib':>14} {'traffic_bytes':>16}"]
+           f"{'kernel':<21} {'fetch_kib':>14} {'write_kib':>14} {'traffic_bytes':>16}"]
     for k in sorted(set(fetch) & set(write)):
         if k == "copy":
             continue
         t = fetch[k] * 1024.0 * f_scale + write[k] * 1024.0 * w_scale
-        out.append(f"{k:<18} {fetch[k]:>14.1f} {write[k]:>14.1f} {t:>16.0f}")
+        out.append(f"{k:<21} {fetch[k]:>14.1f} {write[k]:>14.1f} {t:>16.0f}")
     return "\n".join(out)
 
 
@@ -233,8 +242,8 @@ def training_units(wl, N):
     nblk = wl.B * ((wl.T + 63) // 64)
     u = backward_units(wl, N)
     # dh written and the per-workgroup conv / RMSNorm-scale sums
-    u["bwd_gate_conv"] = {"bound": "hbm", "bytes": u["bwd_gate_conv"]["bytes"] + N * d * es
-                          + nblk * d * (taps + 1) * 4}
+    u["bwd_gate_conv_params"] = {"bound": "hbm", "bytes": u["bwd_gate_conv"]["bytes"] + N * d * es
+                                 + nblk * d * (taps + 1) * 4}
     # rows gathered again: indices + rows in, e out
     u["gather"] = {"bound": "hbm", "bytes": N * J * 4 + 2 * N * dm * es}
     # dW = [dk|dv]^T e: both token-major operands once, dW once

@@ -471,7 +471,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
       ba.dh = (uint8_t*)pg->hidden;
       ba.pad_rows = want_w ? (int32_t)(round_pad(N) - N) : 0;
     }
-    Timed tm("bwd_gate_conv", hs);
+    Timed tm(pg ? "bwd_gate_conv_params" : "bwd_gate_conv", hs);
     if (launch_bwd_gate_conv(ba, hs) != hipSuccess) return ENGRAM_E_HIP;
   }
   if (out && N > 0) {
