@@ -445,6 +445,8 @@ def bench_host(args):
         sweep.append({"gemms": k, "gemms_forward_ms": round(t_only, 3), "with_prefetch_ms": round(t_ovl, 3),
                       "exposed_copy_ms": round(max(0.0, t_ovl - t_only), 3),
                       "tokens_per_s": round(N / (t_ovl * 1e-3), 1)})
+    ring = bench_ring(args, wl, inp, dp, host_tables, staging, inv_h, inv_dev, side, ev, y, ws,
+                      lambda: torch.matmul(xa, wg, out=yg), timed)
     # the compact forward is bit-identical to the one reading the tables in HBM
     out = {
         "metric": "host-table Engram forward: tokens/s and exposed copy time",
@@ -457,10 +459,83 @@ def bench_host(args):
         "compact_forward_ms": round(fwd_ms, 3), "standin_gemm_ms": round(gemm_ms, 3),
         "tokens_per_s_forward_only": round(N / (fwd_ms * 1e-3), 1),
         "sweep": sweep,
+        "row_ring": ring,
         "note": f"table rows reduced from ~48.8M to ~{args.host_rows} per table to fit host memory; "
                 "the rows copied per forward depend on the token stream, not the table size",
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_ring(args, wl, inp, dp, host_tables, staging, inv_h, inv_dev, side, ev, y, ws, gemm,
+               timed) -> dict:
+    """Successive batches of one token stream, each planned ahead and then
+    gathered + copied behind two stand-in GEMMs, without and with the HBM row
+    ring (rows an earlier batch copied are not copied again)."""
+    import numpy as np
+    import torch
+
+    import hashed_gram_embedding_canon_amd as eg
+    import synth
+    N, J = wl.n_tokens, wl.J
+    es = 2 if wl.dtype == "bf16" else 4
+    rb = wl.dim * es
+    cap = N * J
+    R = args.ring_factor * cap
+    rows_dev = torch.empty(R * rb, dtype=torch.uint8, device="cuda")
+    ring_pos = np.full(int(inp.table_rows.sum()), -1, np.int64)
+    counts = np.zeros(J, np.int64)
+    uniq = np.zeros(cap, np.int32)
+    res = {"ring_rows": R, "ring_GiB": round(R * rb / 2**30, 2), "batches": args.ring_batches,
+           "standin_gemms": 2}
+    for mode in ("no_ring", "ring"):
+        plan = eg.engram_compact()
+        plan.capacity_rows = cap
+        plan.counts, plan.uniq_host = counts.ctypes.data, uniq.ctypes.data
+        plan.inverse_host, plan.staging_host = inv_h.data_ptr(), staging.data_ptr()
+        plan.rows_dev, plan.inverse_dev = rows_dev.data_ptr(), inv_dev.data_ptr()
+        plan.ready_event = ev.cuda_event
+        if mode == "ring":
+            ring_pos.fill(-1)
+            plan.ring_rows, plan.ring_pos, plan.ring_head = R, ring_pos.ctypes.data, 0
+        per = []
+        for k in range(args.ring_batches):
+            tok = synth.zipf_tokens(synth.seed_of(wl.cfg, synth.S_TOKENS), N, wl.vocab, wl.zipf_s,
+                                    offset=k * N).reshape(wl.B, wl.T)
+            plan.flags = 0
+            eg.engram_prefetch_plan(dp.cfg, inp.canon_map, tok, B=wl.B, T=wl.T, host_tables=None,
+                                    plan=plan)
+            plan.flags = eg.ENGRAM_PLAN_REUSE
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0 = torch.cuda.Event(enable_timing=True)
+            a0.record()
+            gemm()
+            gemm()
+            s0.record(side)
+            eg.engram_prefetch_plan(dp.cfg, inp.canon_map, tok, B=wl.B, T=wl.T,
+                                    host_tables=host_tables, plan=plan, side_stream=side)
+            dp.forward(compact=plan, ws=ws, y=y)
+            a1.record()
+            torch.cuda.synchronize()
+            t_ovl = a0.elapsed_time(a1)
+            copy_ms = s0.elapsed_time(ev)
+
+            def only():
+                gemm()
+                gemm()
+                dp.forward(compact=plan, ws=ws, y=y)
+            t_only = timed(only)
+            copied = int(plan.total_rows)  # with the ring, the plan keeps its misses only
+            hits = int(plan.ring_hits) if mode == "ring" else 0
+            per.append({"distinct_rows": copied + hits, "copied_rows": copied,
+                        "copy_ms": round(copy_ms, 3), "exposed_copy_ms": round(max(0.0, t_ovl - t_only), 3)})
+        later = per[1:] if len(per) > 1 else per
+        res[mode] = {"per_batch": per,
+                     "mean_copied_rows_after_first": round(float(np.mean([p["copied_rows"] for p in later])), 1),
+                     "mean_exposed_copy_ms_after_first": round(float(np.mean([p["exposed_copy_ms"] for p in later])), 3)}
+    res["copied_rows_reduction"] = round(1.0 - res["ring"]["mean_copied_rows_after_first"]
+                                         / res["no_ring"]["mean_copied_rows_after_first"], 4)
+    return res
 
 
 def copy_calibration(nbytes: int):
@@ -508,6 +583,10 @@ def main():
     ap.add_argument("--calibration-bytes", type=int, default=1 << 30)
     ap.add_argument("--branches", type=int, default=1,
                     help="M branches sharing the tables and W_V (own W_K, hidden state, gate, Y)")
+    ap.add_argument("--ring-batches", type=int, default=8,
+                    help="successive batches for the row-ring measurement of --workload host100b")
+    ap.add_argument("--ring-factor", type=int, default=16,
+                    help="HBM row ring size in units of one batch's capacity (N*J rows)")
     ap.add_argument("--host-rows", type=int, default=4_880_000,
                     help="rows per host table for --workload host100b")
     args = ap.parse_args()

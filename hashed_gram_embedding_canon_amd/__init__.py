@@ -75,6 +75,10 @@ class engram_compact(ctypes.Structure):
         ("inverse_dev", _vp),
         ("ready_event", _vp),
         ("flags", ctypes.c_uint32),
+        ("ring_rows", ctypes.c_int64),
+        ("ring_pos", _vp),
+        ("ring_head", ctypes.c_int64),
+        ("ring_hits", ctypes.c_int64),
     ]
 
 

@@ -600,6 +600,10 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
     for (int j = 0; j < J; ++j)
       if (!host_tables[j]) return ENGRAM_E_INVALID;
   }
+  const bool ring = plan->ring_rows != 0;
+  if (ring && (plan->ring_rows < 2 * plan->capacity_rows || plan->ring_rows < 1 ||
+               plan->ring_rows >= (int64_t(1) << 31) || !plan->ring_pos || plan->ring_head < 0))
+    return ENGRAM_E_INVALID;
   if (!reuse)
     for (int64_t n = 0; n < N; ++n)
       if (tokens_host[n] < 0 || tokens_host[n] >= cfg->vocab) return ENGRAM_E_INVALID;
@@ -671,9 +675,78 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
         plan->inverse_host[(size_t)n * J + j] = (int32_t)(base[j] + (it - uniq[j].begin()));
       }
   });
+  // 4. with the ring: rows an earlier call left in the ring are not copied
+  //    again.  The inverse map gets its final ring rows, the misses get ring
+  //    positions from ring_head on, and the plan keeps the misses only
+  //    (counts, uniq_host, total_rows), so the copying call moves just those.
+  if (ring) {
+    // A row in the ring is usable when neither this call's appends nor the
+    // next call's (each at most capacity_rows) reach its slot.
+    const int64_t R = plan->ring_rows, head = plan->ring_head;
+    const int64_t oldest = head + 2 * plan->capacity_rows - R;
+    std::vector<int64_t> toff(J + 1, 0);
+    for (int j = 0; j < J; ++j) toff[j + 1] = toff[j] + cfg->table_rows[j];
+    std::vector<int32_t> dev((size_t)total);   // ring row of each distinct row
+    std::vector<uint8_t> hit((size_t)total);
+    std::vector<int64_t> miss_base(J + 1, 0);
+    // ring_pos is read at ascending but scattered rows (one cache line
+    // each), so both sweeps prefetch kPf rows ahead to keep many in flight
+    constexpr int64_t kPf = 32;
+    parallel(J, [&](int64_t lo, int64_t hi) {
+      for (int64_t j = lo; j < hi; ++j) {
+        const int64_t* rp = plan->ring_pos + toff[j];
+        const int32_t* uj = uniq[j].data();
+        const int64_t n = (int64_t)uniq[j].size();
+        for (int64_t i = 0; i < n; ++i) {
+          if (i + kPf < n) __builtin_prefetch(rp + uj[i + kPf], 1);
+          const int64_t P = rp[uj[i]];
+          const bool h = P >= 0 && P >= oldest && P < head;
+          hit[base[j] + i] = h;
+          if (h) dev[base[j] + i] = (int32_t)(P % R);
+        }
+      }
+    });
+    for (int j = 0; j < J; ++j) {
+      int64_t m = 0;
+      for (int64_t u = base[j]; u < base[j + 1]; ++u) m += !hit[u];
+      miss_base[j + 1] = miss_base[j] + m;
+    }
+    parallel(J, [&](int64_t lo, int64_t hi) {
+      for (int64_t j = lo; j < hi; ++j) {
+        int64_t* rp = plan->ring_pos + toff[j];
+        const int32_t* uj = uniq[j].data();
+        const int64_t n = (int64_t)uniq[j].size();
+        int64_t m = miss_base[j];
+        for (int64_t i = 0; i < n; ++i) {
+          if (i + kPf < n) __builtin_prefetch(rp + uj[i + kPf], 1);
+          if (hit[base[j] + i]) continue;
+          const int64_t P = head + m;
+          rp[uj[i]] = P;
+          dev[base[j] + i] = (int32_t)(P % R);
+          plan->uniq_host[m++] = uj[i];  // misses only, table after table
+        }
+        plan->counts[j] = miss_base[j + 1] - miss_base[j];
+      }
+    });
+    parallel(N, [&](int64_t lo, int64_t hi) {
+      for (int64_t n = lo; n < hi; ++n)
+        for (int j = 0; j < J; ++j) {
+          int32_t& x = plan->inverse_host[(size_t)n * J + j];
+          x = dev[(size_t)x];
+        }
+    });
+    plan->total_rows = miss_base[J];
+    plan->ring_head = head + miss_base[J];
+    plan->ring_hits = total - miss_base[J];
+    for (int j = 0; j <= J; ++j) base[j] = miss_base[j];
+  }
   }  // !reuse
   if (!host_tables) return ENGRAM_OK;
-  const int64_t total = plan->total_rows;
+  // Rows to copy: the plan's rows; with the ring they are the misses and go
+  // to the ring positions the planning reserved, ending at ring_head.
+  const int64_t ncopy = plan->total_rows;
+  const int64_t dst0 = ring ? plan->ring_head - ncopy : 0;
+  if (ring && dst0 < 0) return ENGRAM_E_INVALID;
   // 4. the inverse map first, then the rows chunk by chunk: gather a chunk
   //    into pinned staging on the host threads, queue its copy, gather the next
   hipStream_t hs = (hipStream_t)side_stream;
@@ -682,8 +755,24 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
     return ENGRAM_E_HIP;
   const size_t rb = (size_t)s.D * s.es;
   const int64_t chunk = std::max<int64_t>(1, (int64_t)((32u << 20) / rb));  // ~32 MB of rows
-  for (int64_t c0 = 0; c0 < total; c0 += chunk) {
-    const int64_t c1 = std::min(total, c0 + chunk);
+  // staged rows [a, b) to ring (or buffer) rows from dst0 + a, split at the ring's end
+  auto copy_rows = [&](int64_t a, int64_t b) -> bool {
+    while (a < b) {
+      int64_t d = dst0 + a, n = b - a;
+      if (ring) {
+        d %= plan->ring_rows;
+        n = std::min(n, plan->ring_rows - d);
+      }
+      if (hipMemcpyAsync((uint8_t*)plan->rows_dev + (size_t)d * rb,
+                         (const uint8_t*)plan->staging_host + (size_t)a * rb, (size_t)n * rb,
+                         hipMemcpyHostToDevice, hs) != hipSuccess)
+        return false;
+      a += n;
+    }
+    return true;
+  };
+  for (int64_t c0 = 0; c0 < ncopy; c0 += chunk) {
+    const int64_t c1 = std::min(ncopy, c0 + chunk);
     parallel(c1 - c0, [&](int64_t lo, int64_t hi) {
       lo += c0;
       hi += c0;
@@ -695,10 +784,7 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
                     (const uint8_t*)host_tables[j] + (size_t)row * rb, rb);
       }
     });
-    if (hipMemcpyAsync((uint8_t*)plan->rows_dev + (size_t)c0 * rb,
-                       (const uint8_t*)plan->staging_host + (size_t)c0 * rb,
-                       (size_t)(c1 - c0) * rb, hipMemcpyHostToDevice, hs) != hipSuccess)
-      return ENGRAM_E_HIP;
+    if (!copy_rows(c0, c1)) return ENGRAM_E_HIP;
   }
   if (plan->ready_event && hipEventRecord((hipEvent_t)plan->ready_event, hs) != hipSuccess)
     return ENGRAM_E_HIP;

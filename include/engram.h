@@ -140,6 +140,23 @@ typedef struct {
   void* ready_event;      /* hipEvent_t recorded on the side stream after the copies
                              (engram_forward waits on it when non-NULL) */
   uint32_t flags;         /* ENGRAM_PLAN_* bits, 0 for the defaults */
+  /* HBM row ring: a cache of the rows earlier calls copied ("DeepSeek AI II",
+   * system-efficiency part: Zipf-distributed N-gram use lets the frequent
+   * rows sit in a faster tier).  ring_rows = 0: off (rows_dev holds this
+   * call's rows only).  Otherwise rows_dev holds ring_rows rows used as a
+   * ring.  Planning (a call without ENGRAM_PLAN_REUSE) points the inverse
+   * map at rows an earlier call left in the ring, when no copy of this plan
+   * or of the next one can overwrite them, reserves ring positions from
+   * ring_head on for the rest, and leaves only those in counts, uniq_host
+   * and total_rows; the copying call moves just them.  Each plan must be
+   * copied before the next one is made.  One forward may read the ring while
+   * the next plan copies; a third must wait for that forward. */
+  int64_t ring_rows;      /* R >= 2 * capacity_rows, < 2^31; rows_dev holds R rows */
+  int64_t* ring_pos;      /* host [sum_j M_j]: ring position (a count of appended rows) where
+                             each table row was last copied, -1 = none; the caller sets all
+                             to -1 before the first call and keeps it with the ring */
+  int64_t ring_head;      /* in/out: rows appended to the ring so far */
+  int64_t ring_hits;      /* out: distinct rows of the last planning call found in the ring */
 } engram_compact;
 
 /* engram_compact.flags */
@@ -269,8 +286,9 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* par
  * queues hipMemcpyAsync of rows and inverse map to the device buffers on
  * side_stream, then records plan->ready_event there.  The rows are gathered
  * and queued in chunks, so the copy of one chunk runs while the next is
- * gathered.  Returns when the host work is done; the copies run
- * asynchronously.  With ENGRAM_PLAN_REUSE in plan->flags the plan fields are
+ * gathered.  With plan->ring_rows > 0 only the rows missing from the ring
+ * are gathered and copied (see engram_compact).  Returns when the host work
+ * is done; the copies run asynchronously.  With ENGRAM_PLAN_REUSE in plan->flags the plan fields are
  * taken as given (a plan-only call made them) and only gather and copy run.
  *   canon_map_host: host [vocab]; tokens_host: host [B][T];
  *   host_tables: NULL (plan only) or host [J] pointers to [M_j][D] dtype

@@ -92,12 +92,14 @@ def normal_stream(seed: int, n: int, stdev: float, dtype: str, offset: int = 0,
     return out
 
 
-def zipf_tokens(seed: int, n: int, vocab: int, s: float) -> np.ndarray:
+def zipf_tokens(seed: int, n: int, vocab: int, s: float, offset: int = 0) -> np.ndarray:
+    """Elements offset .. offset+n-1 of the token stream (later batches of one
+    stream continue it)."""
     lib = _load()
     cdf = np.empty(vocab, np.float64)
     lib.synth_zipf_cdf(vocab, s, cdf.ctypes.data)
     out = np.empty(n, np.int32)
-    lib.synth_zipf(seed, 0, n, vocab, cdf.ctypes.data, out.ctypes.data)
+    lib.synth_zipf(seed, offset, n, vocab, cdf.ctypes.data, out.ctypes.data)
     return out
 
 

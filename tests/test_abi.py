@@ -203,6 +203,30 @@ def test_host_plan_adversarial_multipliers(eg, oracle_lib):
                 j += 1
 
 
+def test_row_ring_validation(eg):
+    """The HBM row ring is checked on the host before any copy is queued."""
+    cfg = _cfg(eg)
+    N, J = 2 * 8, cfg.J
+    tokens = np.ones((2, 8), np.int32)
+    canon = np.zeros(cfg.c.vocab, np.int32)
+    cap = N * J
+    counts = np.zeros(J, np.int64)
+    uniq = np.zeros(cap, np.int32)
+    inv = np.zeros((N, J), np.int32)
+    pos = np.full(10, -1, np.int64)
+    plan = eg.engram_compact()
+    plan.capacity_rows = cap
+    plan.counts, plan.uniq_host, plan.inverse_host = counts.ctypes.data, uniq.ctypes.data, inv.ctypes.data
+    plan.staging_host = plan.rows_dev = plan.inverse_dev = FAKE
+    tabs = (ctypes.c_void_p * J)(*([FAKE] * J))
+    L = eg.lib()
+    for R, p, head in ((2 * cap - 1, pos, 0), (2 * cap, None, 0), (2 * cap, pos, -1), (1 << 31, pos, 0)):
+        plan.ring_rows, plan.ring_head = R, head
+        plan.ring_pos = None if p is None else p.ctypes.data
+        assert L.engram_prefetch_plan(cfg.ref, canon.ctypes.data, tokens.ctypes.data, 2, 8, tabs,
+                                      ctypes.byref(plan), None) == eg.ENGRAM_E_INVALID
+
+
 def test_profile_api_without_launches(eg):
     eg.engram_profile_enable(True)
     eg.engram_profile_reset()

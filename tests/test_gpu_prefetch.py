@@ -100,3 +100,74 @@ def test_plan_ahead_then_reuse(torch, oracle_lib):
     with pytest.raises(eg.EngramError):
         eg.engram_prefetch_plan(dp.cfg, inp.canon_map, inp.tokens, B=dp.B, T=dp.T,
                                 host_tables=host_tables, plan=plan, side_stream=side)
+
+
+@pytest.mark.parametrize("name,B,T,batches,ahead", [("tiny", 2, 300, 6, False), ("tiny", 2, 300, 6, True),
+                                                    ("small", 2, 2048, 4, True)])
+def test_row_ring_across_batches(torch, name, B, T, batches, ahead):
+    """HBM row ring over successive batches of one token stream, planned in
+    the copying call or ahead of it: the compact forward stays bit-identical
+    to the HBM forward, every inverse entry points at a ring row holding its
+    table row, rows found in the ring are not copied again, and the ring
+    wraps."""
+    import hashed_gram_embedding_canon_amd as eg
+    wl = synth.get_workload(name).with_shape(B, T)
+    print(f"[row ring {name}] B={B} T={T} batches={batches}", flush=True)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp)
+    N, J = dp.N, wl.J
+    cap = N * J
+    R = 2 * cap + cap // 2
+    es = 2 if wl.dtype == "bf16" else 4
+    rb = wl.dim * es
+    counts = np.zeros(J, np.int64)
+    uniq = np.zeros(cap, np.int32)
+    inv_h = torch.empty(N, J, dtype=torch.int32, pin_memory=True)
+    staging = torch.empty(cap * rb, dtype=torch.uint8, pin_memory=True)
+    ring = torch.zeros(R * rb, dtype=torch.uint8, device="cuda")
+    inv_dev = torch.empty(N, J, dtype=torch.int32, device="cuda")
+    ring_pos = np.full(int(inp.table_rows.sum()), -1, np.int64)
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    ev.record()
+    plan = eg.engram_compact()
+    plan.capacity_rows = cap
+    plan.counts, plan.uniq_host = counts.ctypes.data, uniq.ctypes.data
+    plan.inverse_host, plan.staging_host = inv_h.data_ptr(), staging.data_ptr()
+    plan.rows_dev, plan.inverse_dev = ring.data_ptr(), inv_dev.data_ptr()
+    plan.ready_event = ev.cuda_event
+    plan.ring_rows, plan.ring_pos, plan.ring_head = R, ring_pos.ctypes.data, 0
+    host_tables = [inp.table(j) for j in range(J)]
+    tables_u8 = [np.ascontiguousarray(t).view(np.uint8).reshape(t.shape[0], rb) for t in host_tables]
+    hits_total = 0
+    for k in range(batches):
+        tok = synth.zipf_tokens(synth.seed_of(wl.cfg, synth.S_TOKENS), N, wl.vocab, wl.zipf_s,
+                                offset=k * N).reshape(B, T)
+        dp.tokens_host = tok
+        dp.tokens = H.to_dev(tok)
+        y_ref = dp.forward()
+        head0 = plan.ring_head
+        plan.flags = 0
+        if ahead:
+            eg.engram_prefetch_plan(dp.cfg, inp.canon_map, tok, B=B, T=T, host_tables=None, plan=plan)
+            plan.flags = eg.ENGRAM_PLAN_REUSE
+        eg.engram_prefetch_plan(dp.cfg, inp.canon_map, tok, B=B, T=T, host_tables=host_tables,
+                                plan=plan, side_stream=side)
+        y = dp.forward(compact=plan)
+        idx = dp.hash()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), k
+        assert plan.ring_head - head0 == plan.total_rows  # the misses, all copied
+        hits_total += plan.ring_hits if k else 0
+        if k == 0:
+            assert plan.ring_hits == 0
+        # ring row of every (token, table) holds that table row, byte for byte
+        ringh = ring.cpu().numpy().reshape(R, rb)
+        inv = inv_dev.cpu().numpy()
+        idxh = idx.cpu().numpy()
+        for j in range(J):
+            assert np.array_equal(ringh[inv[:, j]], tables_u8[j][idxh[:, j]]), (k, j)
+        print(f"  batch {k}: {plan.total_rows} rows copied, {plan.ring_hits} found in the ring, "
+              f"head {plan.ring_head}", flush=True)
+    assert hits_total > 0
+    assert plan.ring_head > R  # wrapped
