@@ -23,7 +23,8 @@ ENGRAM_MAX_BRANCHES = 8
 ENGRAM_FLAG_FUSED_GATHER = 1
 ENGRAM_PLAN_REUSE = 1
 ENGRAM_GRAD_SORTED_SPARSE, ENGRAM_GRAD_SORTED_DENSE, ENGRAM_GRAD_ATOMIC_DENSE = 0, 1, 2
-ENGRAM_OP_FORWARD, ENGRAM_OP_BACKWARD, ENGRAM_OP_BACKWARD_PARAMS = 0, 1, 2
+ENGRAM_OP_FORWARD, ENGRAM_OP_BACKWARD, ENGRAM_OP_BACKWARD_PARAMS, ENGRAM_OP_SHARD = 0, 1, 2, 3
+ENGRAM_SHARD_MAX_GPUS = 64
 
 _vp = ctypes.c_void_p
 
@@ -110,6 +111,7 @@ class EngramError(RuntimeError):
 
 EXPORTS = ("engram_workspace_size", "engram_status_string", "engram_hash_indices", "engram_forward",
            "engram_backward_table_grad", "engram_backward", "engram_prefetch_plan",
+           "engram_shard_requests", "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce",
            "engram_profile_enable",
            "engram_profile_reset", "engram_profile_read")
 
@@ -138,6 +140,10 @@ def lib():
     L.engram_backward_table_grad.argtypes = [C, P, _vp, _vp, i64, i64, S, G, _vp, sz, _vp]
     L.engram_backward.argtypes = [C, P, _vp, _vp, i64, i64, S, G, PG, _vp, sz, _vp]
     L.engram_prefetch_plan.argtypes = [C, _vp, _vp, i64, i64, _vp, K, _vp]
+    L.engram_shard_requests.argtypes = [C, i32, _vp, i64, _vp, _vp, _vp, _vp, sz, _vp]
+    L.engram_shard_serve.argtypes = [C, i32, _vp, _vp, i64, _vp, _vp]
+    L.engram_shard_grads.argtypes = [C, i32, _vp, _vp, _vp, i64, _vp, _vp, _vp, _vp, sz, _vp]
+    L.engram_shard_reduce.argtypes = [C, i32, _vp, _vp, _vp, _vp, i32, _vp]
     L.engram_profile_enable.argtypes = [i32]
     L.engram_profile_enable.restype = None
     L.engram_profile_reset.argtypes = []
@@ -145,7 +151,8 @@ def lib():
     L.engram_profile_read.argtypes = [ctypes.c_char_p, sz, _vp, _vp, i32]
     L.engram_profile_read.restype = i32
     for name in ("engram_hash_indices", "engram_forward", "engram_backward_table_grad",
-                 "engram_backward", "engram_prefetch_plan"):
+                 "engram_backward", "engram_prefetch_plan", "engram_shard_requests",
+                 "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -280,6 +287,41 @@ def engram_backward(cfg: Config, params: engram_params, hidden, dy, *, B: int, T
                                  ctypes.byref(table_out) if table_out is not None else None,
                                  ctypes.byref(param_out) if param_out is not None else None,
                                  _ptr(workspace), ws_bytes, _stream(stream)), "engram_backward")
+
+
+def _ws_bytes(workspace, ws_bytes):
+    if ws_bytes is None:
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return ws_bytes
+
+
+def engram_shard_requests(cfg: Config, G: int, idx, N: int, send_ids, send_counts, inverse, *,
+                          workspace=None, ws_bytes: int | None = None, stream=None):
+    _check(lib().engram_shard_requests(cfg.ref, G, _ptr(idx), N, _ptr(send_ids), _ptr(send_counts),
+                                       _ptr(inverse), _ptr(workspace), _ws_bytes(workspace, ws_bytes),
+                                       _stream(stream)), "engram_shard_requests")
+
+
+def engram_shard_serve(cfg: Config, G: int, shard_tables, ids, n: int, rows_out, *, stream=None):
+    tabs = (ctypes.c_void_p * len(shard_tables))(*[_ptr(t) for t in shard_tables])
+    _check(lib().engram_shard_serve(cfg.ref, G, ctypes.cast(tabs, ctypes.c_void_p), _ptr(ids), n,
+                                    _ptr(rows_out), _stream(stream)), "engram_shard_serve")
+
+
+def engram_shard_grads(cfg: Config, G: int, keys, rows, count, capacity: int, send_ids, send_rows,
+                       send_counts, *, workspace=None, ws_bytes: int | None = None, stream=None):
+    _check(lib().engram_shard_grads(cfg.ref, G, _ptr(keys), _ptr(rows), _ptr(count), capacity,
+                                    _ptr(send_ids), _ptr(send_rows), _ptr(send_counts),
+                                    _ptr(workspace), _ws_bytes(workspace, ws_bytes), _stream(stream)),
+           "engram_shard_grads")
+
+
+def engram_shard_reduce(cfg: Config, G: int, shard_grads, ids, rows, counts_host, *, stream=None):
+    grads = (ctypes.c_void_p * len(shard_grads))(*[_ptr(t) for t in shard_grads])
+    counts = (ctypes.c_int64 * len(counts_host))(*[int(c) for c in counts_host])
+    _check(lib().engram_shard_reduce(cfg.ref, G, ctypes.cast(grads, ctypes.c_void_p), _ptr(ids),
+                                     _ptr(rows), ctypes.cast(counts, ctypes.c_void_p), len(counts_host),
+                                     _stream(stream)), "engram_shard_reduce")
 
 
 def engram_prefetch_plan(cfg: Config, canon_map_host, tokens_host, *, B: int, T: int,

@@ -231,6 +231,38 @@ size_t backward_ws(const Shape& s, int64_t B, int64_t T, BwdWs* out, uint8_t* ba
   return off;
 }
 
+// sharded exchange: sort buffers, send positions and the per-(table, owner) bounds
+size_t shard_ws(const Shape& s, int64_t N, uint8_t* base, SortBufs* sb, int32_t** send_pos,
+                int64_t** first, int64_t** dest_base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> uint8_t* {
+    uint8_t* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  uint8_t* sort = take(sort_workspace_bytes(N, s.J));
+  uint8_t* sp = take((size_t)N * s.J * 4);
+  uint8_t* fi = take(((size_t)s.J * ENGRAM_SHARD_MAX_GPUS + 1) * 8);
+  uint8_t* db = take((size_t)s.J * ENGRAM_SHARD_MAX_GPUS * 8);
+  if (base) {
+    if (sb) carve_sort(sort, N, s.J, sb);
+    if (send_pos) *send_pos = (int32_t*)sp;
+    *first = (int64_t*)fi;
+    *dest_base = (int64_t*)db;
+  }
+  return off;
+}
+
+// S_j = ceil(M_j / G); UNSUPPORTED when a shard needs 27 bits or more
+engram_status shard_rows(const engram_config* cfg, const Shape& s, int32_t G, ShardRows* sr) {
+  if (G < 1 || G > ENGRAM_SHARD_MAX_GPUS || s.J * G > 1024) return ENGRAM_E_INVALID;
+  for (int j = 0; j < s.J; ++j) {
+    sr->rows[j] = (cfg->table_rows[j] + G - 1) / G;
+    if (sr->rows[j] >= (int64_t(1) << 27)) return ENGRAM_E_UNSUPPORTED;
+  }
+  return ENGRAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -242,6 +274,11 @@ size_t engram_workspace_size(const engram_config* cfg, int64_t B, int64_t T, int
   if (op == ENGRAM_OP_FORWARD) return forward_ws(s, N, nullptr, nullptr, nullptr, true);
   if (op == ENGRAM_OP_BACKWARD) return backward_ws(s, B, T, nullptr, nullptr);
   if (op == ENGRAM_OP_BACKWARD_PARAMS) return backward_ws(s, B, T, nullptr, nullptr, true, true, true);
+  if (op == ENGRAM_OP_SHARD) {
+    int64_t* f = nullptr;
+    int64_t* d = nullptr;
+    return shard_ws(s, N, nullptr, nullptr, nullptr, &f, &d);
+  }
   return 0;
 }
 
@@ -788,6 +825,132 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
   }
   if (plan->ready_event && hipEventRecord((hipEvent_t)plan->ready_event, hs) != hipSuccess)
     return ENGRAM_E_HIP;
+  return ENGRAM_OK;
+}
+
+engram_status engram_shard_requests(const engram_config* cfg, int32_t G, const int32_t* idx,
+                                    int64_t N, uint32_t* send_ids, int64_t* send_counts,
+                                    int32_t* inverse, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  Shape s;
+  engram_status st = check_config(cfg, &s);
+  if (st != ENGRAM_OK) return st;
+  ShardRows sr;
+  if ((st = shard_rows(cfg, s, G, &sr)) != ENGRAM_OK) return st;
+  if (N < 0 || (uint64_t)N * (uint64_t)s.J >= (uint64_t(1) << 31)) return ENGRAM_E_INVALID;
+  if (!send_counts || (N > 0 && (!idx || !send_ids || !inverse))) return ENGRAM_E_INVALID;
+  const size_t need = shard_ws(s, N, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return ENGRAM_E_WORKSPACE;
+  SortBufs sb;
+  ShardPackArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  shard_ws(s, N, (uint8_t*)workspace, &sb, &pa.send_pos, &pa.first, &pa.dest_base);
+  hipStream_t hs = (hipStream_t)stream;
+  {
+    Timed tm("shard_dedup", hs);
+    if (launch_dedup(idx, N, s.J, s.key_bits, sb, inverse, hs) != hipSuccess) return ENGRAM_E_HIP;
+  }
+  pa.keys = sb.seg_key;
+  pa.count_u32 = sb.total;
+  pa.capacity = N * s.J;
+  pa.J = s.J;
+  pa.G = G;
+  pa.shard_rows = sr;
+  pa.send_counts = send_counts;
+  pa.send_ids = send_ids;
+  pa.inverse = inverse;
+  pa.n_inverse = N * s.J;
+  Timed tm("shard_pack", hs);
+  return hip_status(launch_shard_pack(pa, hs));
+}
+
+engram_status engram_shard_serve(const engram_config* cfg, int32_t G,
+                                 const void* const* shard_tables, const uint32_t* ids, int64_t n,
+                                 void* rows_out, void* stream) {
+  Shape s;
+  engram_status st = check_config(cfg, &s);
+  if (st != ENGRAM_OK) return st;
+  ShardRows sr;
+  if ((st = shard_rows(cfg, s, G, &sr)) != ENGRAM_OK) return st;
+  if (n < 0 || !shard_tables) return ENGRAM_E_INVALID;
+  if (n == 0) return ENGRAM_OK;
+  if (!ids || !rows_out || !aligned16(rows_out)) return ENGRAM_E_INVALID;
+  ShardTables t;
+  std::memset(&t, 0, sizeof(t));
+  for (int j = 0; j < s.J; ++j) {
+    if (!shard_tables[j] || !aligned16(shard_tables[j])) return ENGRAM_E_INVALID;
+    t.base[j] = (const uint8_t*)shard_tables[j];
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  Timed tm("shard_serve", hs);
+  return hip_status(launch_shard_serve(t, ids, n, (uint8_t*)rows_out, s.D * s.es, hs));
+}
+
+engram_status engram_shard_grads(const engram_config* cfg, int32_t G, const int64_t* keys,
+                                 const float* rows, const int64_t* count, int64_t capacity,
+                                 uint32_t* send_ids, float* send_rows, int64_t* send_counts,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  Shape s;
+  engram_status st = check_config(cfg, &s);
+  if (st != ENGRAM_OK) return st;
+  ShardRows sr;
+  if ((st = shard_rows(cfg, s, G, &sr)) != ENGRAM_OK) return st;
+  if (capacity < 0 || capacity >= (int64_t(1) << 31) || !count || !send_counts)
+    return ENGRAM_E_INVALID;
+  if (capacity > 0 && (!keys || !rows || !send_ids || !send_rows || !aligned16(rows) ||
+                       !aligned16(send_rows)))
+    return ENGRAM_E_INVALID;
+  const size_t need = shard_ws(s, 1, nullptr, nullptr, nullptr, nullptr, nullptr);
+  if (!workspace || ws_bytes < need || !aligned16(workspace)) return ENGRAM_E_WORKSPACE;
+  ShardPackArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  shard_ws(s, 1, (uint8_t*)workspace, nullptr, nullptr, &pa.first, &pa.dest_base);
+  pa.keys = (const uint64_t*)keys;
+  pa.count_i64 = count;
+  pa.capacity = capacity;
+  pa.J = s.J;
+  pa.G = G;
+  pa.shard_rows = sr;
+  pa.send_counts = send_counts;
+  pa.send_ids = send_ids;
+  pa.rows = rows;
+  pa.send_rows = send_rows;
+  pa.pieces = s.D / 4;
+  hipStream_t hs = (hipStream_t)stream;
+  Timed tm("shard_grad_pack", hs);
+  return hip_status(launch_shard_pack(pa, hs));
+}
+
+engram_status engram_shard_reduce(const engram_config* cfg, int32_t G, float* const* shard_grads,
+                                  const uint32_t* ids, const float* rows,
+                                  const int64_t* counts_host, int32_t nblocks, void* stream) {
+  Shape s;
+  engram_status st = check_config(cfg, &s);
+  if (st != ENGRAM_OK) return st;
+  ShardRows sr;
+  if ((st = shard_rows(cfg, s, G, &sr)) != ENGRAM_OK) return st;
+  if (nblocks < 0 || (nblocks > 0 && !counts_host) || !shard_grads) return ENGRAM_E_INVALID;
+  int64_t total = 0;
+  for (int b = 0; b < nblocks; ++b) {
+    if (counts_host[b] < 0) return ENGRAM_E_INVALID;
+    total += counts_host[b];
+  }
+  if (total == 0) return ENGRAM_OK;
+  if (!ids || !rows || !aligned16(rows)) return ENGRAM_E_INVALID;
+  ShardGrads g;
+  std::memset(&g, 0, sizeof(g));
+  for (int j = 0; j < s.J; ++j) {
+    if (!shard_grads[j] || !aligned16(shard_grads[j])) return ENGRAM_E_INVALID;
+    g.base[j] = shard_grads[j];
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  Timed tm("shard_reduce", hs);
+  int64_t off = 0;
+  for (int b = 0; b < nblocks; ++b) {
+    if (launch_shard_grad_add(g, ids + off, rows + off * s.D, counts_host[b], s.D, hs) != hipSuccess)
+      return ENGRAM_E_HIP;
+    off += counts_host[b];
+  }
   return ENGRAM_OK;
 }
 

@@ -100,6 +100,43 @@ hipError_t launch_bwd_param_sums(const float* pacc, float* tmp, int64_t nblk, in
                                  int32_t taps, const float* gamma_q, const float* gamma_k,
                                  float* dconv, float* dgq, float* dgk, hipStream_t s);
 
+// ---------------------------------------------------------------- sharded exchange
+struct ShardRows {
+  int64_t rows[ENGRAM_MAX_TABLES];  // S_j = ceil(M_j / G): rows each GPU owns of table j
+};
+struct ShardTables {
+  const uint8_t* base[ENGRAM_MAX_TABLES];  // this GPU's [S_j][D] shard of each table
+};
+struct ShardGrads {
+  float* base[ENGRAM_MAX_TABLES];  // this GPU's [S_j][D] fp32 gradient of each shard
+};
+// Group sorted distinct keys ((j << 32) | row) by owner: send_ids (and with
+// rows, the D-float rows) in send order, send_counts [G], send_pos [count]
+// (send position of key s) and, with inverse, inverse[i] = send_pos[inverse[i]].
+struct ShardPackArgs {
+  const uint64_t* keys;
+  const uint32_t* count_u32;  // device count of keys (one of the two)
+  const int64_t* count_i64;
+  int64_t capacity;           // upper bound of the count
+  int32_t J, G;
+  ShardRows shard_rows;
+  int64_t* first;             // [J*G + 1] scratch
+  int64_t* dest_base;         // [G*J] scratch
+  int64_t* send_counts;       // [G] out
+  uint32_t* send_ids;         // [capacity] out
+  int32_t* send_pos;          // [capacity] out (may be null without inverse)
+  const float* rows;          // [capacity][D] or null
+  float* send_rows;           // [capacity][D] out with rows
+  int32_t pieces;             // D / 4 with rows
+  int32_t* inverse;           // [n_inverse] in/out or null
+  int64_t n_inverse;
+};
+hipError_t launch_shard_pack(const ShardPackArgs& a, hipStream_t s);
+hipError_t launch_shard_serve(const ShardTables& st, const uint32_t* ids, int64_t n, uint8_t* rows_out,
+                              int32_t row_bytes, hipStream_t s);
+hipError_t launch_shard_grad_add(const ShardGrads& sg, const uint32_t* ids, const float* rows,
+                                 int64_t n, int32_t dim, hipStream_t s);
+
 // Weight gradients dW[i][j] = sum_t X[t][i] Y[t][j] over token-major operands.
 constexpr int kTnPadTokens = 64;  // X rows are padded to, and chunks are, multiples of this
 struct GemmTnArgs {
@@ -148,5 +185,10 @@ void carve_sort(uint8_t* base, int64_t N, int32_t J, SortBufs* b);
 hipError_t launch_sorted_scatter(const ScatterArgs& a, const SortBufs& b, int32_t mode,
                                  hipStream_t s);
 hipError_t launch_atomic_scatter(const ScatterArgs& a, hipStream_t s);
+// Distinct (table, row) keys of idx [N][J]: b.seg_key[0 .. b.total[0]) in
+// table-major ascending order, and inverse[n][j] = position of idx[n][j]'s
+// key among them.
+hipError_t launch_dedup(const int32_t* idx, int64_t N, int32_t J, int32_t key_bits,
+                        const SortBufs& b, int32_t* inverse, hipStream_t s);
 
 }  // namespace engram

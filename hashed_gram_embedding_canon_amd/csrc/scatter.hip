@@ -241,6 +241,40 @@ __global__ __launch_bounds__(256) void seg_write_kernel(const uint32_t* __restri
   }
 }
 
+// inverse[n][j] = index of (j, idx[n][j]) among all segment heads: the
+// position of token n's row in the distinct keys seg_key.  The segment of
+// sorted position p is the number of heads at or before p, minus one.
+__global__ __launch_bounds__(256) void seg_inverse_kernel(const uint32_t* __restrict__ keys,
+                                                          const uint32_t* __restrict__ vals,
+                                                          const uint32_t* __restrict__ seg_count,
+                                                          int32_t* __restrict__ inverse, int64_t N,
+                                                          int nb, int J) {
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t base_s;
+  const int j = blockIdx.y;
+  const int blk = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const uint64_t le_mask = ~0ull >> (63 - lane);
+  if (threadIdx.x == 0) base_s = seg_count[j * nb + blk];
+  __syncthreads();
+  const uint32_t* k = keys + j * N;
+  const uint32_t* v = vals + j * N;
+  for (int r = 0; r < kSortItems; ++r) {
+    const int64_t p = (int64_t)blk * kSortTile + r * 256 + threadIdx.x;
+    const bool head = p < N && (p == 0 || k[p] != k[p - 1]);
+    const uint64_t bal = __ballot(head);
+    if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
+    __syncthreads();
+    uint32_t base = base_s;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    if (p < N) inverse[(int64_t)v[p] * J + j] = (int32_t)(base + (uint32_t)__popcll(bal & le_mask) - 1);
+    __syncthreads();
+    if (threadIdx.x == 0) base_s += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+}
+
 // Segmented reduce.  A wave holds S = 64 / (D/4) lane groups of D/4 lanes
 // (one 16-byte column piece per lane); each group sums whole segments in a
 // grid-stride walk and writes their rows.  Most segments have one element,
@@ -355,6 +389,35 @@ hipError_t launch_sorted_scatter(const ScatterArgs& a, const SortBufs& b, int32_
   else
     hipLaunchKernelGGL(seg_reduce_kernel<ENGRAM_GRAD_SORTED_DENSE>, dim3(blocks), dim3(256), 0, s, a,
                        b.vals[cur], b.seg_start, b.seg_key, b.total);
+  return hipGetLastError();
+}
+
+hipError_t launch_dedup(const int32_t* idx, int64_t N, int32_t J, int32_t key_bits,
+                        const SortBufs& b, int32_t* inverse, hipStream_t s) {
+  if (N == 0) {  // zero heads: total 0
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(1024), 0, s, b.seg_count, 0, b.total, nullptr);
+    return hipGetLastError();
+  }
+  const int nb = (int)sort_blocks(N);
+  hipLaunchKernelGGL(sort_init_kernel, dim3((unsigned)((N + 255) / 256), J), dim3(256), 0, s, idx,
+                     b.keys[0], b.vals[0], N, J);
+  int cur = 0;
+  const int passes = (key_bits + 7) / 8;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = pass * 8;
+    hipLaunchKernelGGL(sort_hist_kernel, dim3(nb, J), dim3(kSortThreads), 0, s, b.keys[cur], b.hist,
+                       N, shift, nb);
+    hipLaunchKernelGGL(sort_scan_kernel, dim3(J), dim3(256), 0, s, b.hist, nb);
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3(nb, J), dim3(kSortThreads), 0, s, b.keys[cur],
+                       b.vals[cur], b.keys[cur ^ 1], b.vals[cur ^ 1], b.hist, N, shift, nb);
+    cur ^= 1;
+  }
+  hipLaunchKernelGGL(seg_count_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.seg_count, N, nb);
+  hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(1024), 0, s, b.seg_count, nb * J, b.total, nullptr);
+  hipLaunchKernelGGL(seg_write_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.seg_count,
+                     b.seg_start, b.seg_key, N, nb);
+  hipLaunchKernelGGL(seg_inverse_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.vals[cur],
+                     b.seg_count, inverse, N, nb, J);
   return hipGetLastError();
 }
 

@@ -201,8 +201,11 @@ typedef struct {
 enum {
   ENGRAM_OP_FORWARD = 0,
   ENGRAM_OP_BACKWARD = 1,         /* engram_backward with table gradients only */
-  ENGRAM_OP_BACKWARD_PARAMS = 2   /* engram_backward with parameter gradients too */
+  ENGRAM_OP_BACKWARD_PARAMS = 2,  /* engram_backward with parameter gradients too */
+  ENGRAM_OP_SHARD = 3             /* engram_shard_requests and engram_shard_grads */
 };
+
+#define ENGRAM_SHARD_MAX_GPUS 64
 
 /* Bytes of device workspace the operation needs for B x T tokens (0 on bad config). */
 size_t engram_workspace_size(const engram_config* cfg, int64_t B, int64_t T, int32_t op);
@@ -298,6 +301,62 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
                                    const int32_t* tokens_host, int64_t B, int64_t T,
                                    const void* const* host_tables, engram_compact* plan,
                                    void* side_stream);
+
+/*
+ * Table-sharded row exchange: the device steps of one GPU ("DeepSeek AI II",
+ * system-efficiency part: tables too large for one GPU are sharded over GPUs,
+ * and each step exchanges the requested rows, then their gradients, by
+ * All-to-All).  With G GPUs (1 <= G <= ENGRAM_SHARD_MAX_GPUS), GPU g owns rows
+ * [g S_j, (g+1) S_j) of table j, S_j = ceil(M_j / G) < 2^27, and a request
+ * names a row by the id (j << 27) | (row - g S_j).  The All-to-All transfers
+ * themselves (RCCL) are the caller's; these calls prepare and consume their
+ * buffers.  Errors: ENGRAM_E_INVALID for null or misaligned buffers or G out
+ * of range, ENGRAM_E_UNSUPPORTED for shards of 2^27 rows or more.
+ */
+
+/* Sender, forward: the distinct rows that idx (device [N][J], table-local
+ * rows from a forward's saved idx or engram_hash_indices) requests, grouped
+ * by owner.
+ *   send_ids: device [N*J] out: owner 0's requests first, each owner's table
+ *   by table in ascending rows; send_counts: device [G] int64 out;
+ *   inverse: device [N][J] int32 out: where token n's row of table j sits in
+ *   the send order, which is the order the owners' replies come back in.
+ *   The compact-mode forward then reads the replies (engram_compact:
+ *   rows_dev = the replies, inverse_dev = inverse, no host plan).
+ *   workspace >= engram_workspace_size(cfg, 1, N, ENGRAM_OP_SHARD). */
+engram_status engram_shard_requests(const engram_config* cfg, int32_t G, const int32_t* idx,
+                                    int64_t N, uint32_t* send_ids, int64_t* send_counts,
+                                    int32_t* inverse, void* workspace, size_t ws_bytes,
+                                    void* stream);
+
+/* Owner, forward: rows_out[i] = row (ids[i] & (2^27 - 1)) of this GPU's
+ * shard of table ids[i] >> 27, for n received request ids.
+ *   shard_tables: device [J] pointers to [S_j][D] dtype; rows_out: device
+ *   [n][D] dtype. */
+engram_status engram_shard_serve(const engram_config* cfg, int32_t G,
+                                 const void* const* shard_tables, const uint32_t* ids, int64_t n,
+                                 void* rows_out, void* stream);
+
+/* Sender, backward: the sparse table gradient (keys, rows, count of
+ * engram_backward with ENGRAM_GRAD_SORTED_SPARSE) grouped by owner in the
+ * order of engram_shard_requests.  count: device [1]; capacity >= count (N*J
+ * suffices); send_ids: device [capacity] out; send_rows: device [capacity][D]
+ * fp32 out; send_counts: device [G] out.
+ *   workspace >= engram_workspace_size(cfg, 1, 1, ENGRAM_OP_SHARD). */
+engram_status engram_shard_grads(const engram_config* cfg, int32_t G, const int64_t* keys,
+                                 const float* rows, const int64_t* count, int64_t capacity,
+                                 uint32_t* send_ids, float* send_rows, int64_t* send_counts,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Owner, backward: adds the received gradient rows into this GPU's shards
+ * of the fp32 table gradient, one sender's block after the other (a fixed
+ * order, no atomics: ids are distinct within a block).
+ *   ids, rows: device, nblocks blocks back to back, block b of
+ *   counts_host[b] ids and [counts_host[b]][D] fp32 rows; shard_grads: device
+ *   [J] pointers to [S_j][D] fp32, added to. */
+engram_status engram_shard_reduce(const engram_config* cfg, int32_t G, float* const* shard_grads,
+                                  const uint32_t* ids, const float* rows,
+                                  const int64_t* counts_host, int32_t nblocks, void* stream);
 
 /*
  * Kernel timing for measurement: while enabled, every kernel the library

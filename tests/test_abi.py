@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(eg):
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 14, names
     L = ctypes.CDLL(eg.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -225,6 +225,28 @@ def test_row_ring_validation(eg):
         plan.ring_pos = None if p is None else p.ctypes.data
         assert L.engram_prefetch_plan(cfg.ref, canon.ctypes.data, tokens.ctypes.data, 2, 8, tabs,
                                       ctypes.byref(plan), None) == eg.ENGRAM_E_INVALID
+
+
+def test_shard_validation(eg):
+    """Sharded exchange calls reject bad GPU counts, buffers and workspaces on the host."""
+    cfg = _cfg(eg)
+    L = eg.lib()
+    for G in (0, eg.ENGRAM_SHARD_MAX_GPUS + 1):
+        assert L.engram_shard_requests(cfg.ref, G, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                       None) == eg.ENGRAM_E_INVALID
+        assert L.engram_shard_serve(cfg.ref, G, FAKE, FAKE, 4, FAKE, None) == eg.ENGRAM_E_INVALID
+    assert L.engram_shard_requests(cfg.ref, 4, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 64,
+                                   None) == eg.ENGRAM_E_WORKSPACE
+    assert L.engram_shard_requests(cfg.ref, 4, None, 16, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                   None) == eg.ENGRAM_E_INVALID
+    assert L.engram_shard_grads(cfg.ref, 4, FAKE, FAKE + 4, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                None) == eg.ENGRAM_E_INVALID  # misaligned rows
+    counts = (ctypes.c_int64 * 2)(3, -1)
+    assert L.engram_shard_reduce(cfg.ref, 4, FAKE, FAKE, FAKE, counts, 2, None) == eg.ENGRAM_E_INVALID
+    # shards of 2^27 rows or more cannot be named by a request id
+    big = _cfg(eg, table_rows=np.array([(1 << 27) + 1] * 8, np.int64))
+    assert L.engram_shard_serve(big.ref, 1, FAKE, FAKE, 4, FAKE, None) == eg.ENGRAM_E_UNSUPPORTED
+    assert eg.engram_workspace_size(cfg, 2, 100, eg.ENGRAM_OP_SHARD) > 0
 
 
 def test_profile_api_without_launches(eg):
