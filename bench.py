@@ -538,6 +538,149 @@ def bench_ring(args, wl, inp, dp, host_tables, staging, inv_h, inv_dev, side, ev
     return res
 
 
+def bench_shard(args):
+    """Tables sharded over G GPUs, the device steps of one GPU at the 27B
+    shape: G GPUs are emulated in one process (GPU r with batch r of the
+    stream); GPU 0 is timed as sender (dedup + requests grouped by owner,
+    gradient rows grouped by owner) and as owner (serve the requests of all
+    G GPUs from its 1/G shard, add the gradient rows of all G GPUs), and its
+    forward runs on the served rows.  The All-to-All is a device copy here;
+    its bytes are reported with the time they take over xGMI links."""
+    import numpy as np
+    import torch
+
+    import hashed_gram_embedding_canon_amd as eg
+    import synth
+    from tests import harness as H
+    G = args.shard_gpus
+    wl = synth.get_workload("engram27b_bwd")
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp)
+    N, J, D = dp.N, wl.J, wl.dim
+    es = 2 if wl.dtype == "bf16" else 4
+    rb = D * es
+    S = [(int(m) + G - 1) // G for m in inp.table_rows]
+    shards0 = [dp.tables[j].view(-1)[: min(S[j], int(inp.table_rows[j])) * D] for j in range(J)]
+    ws = torch.empty(eg.engram_workspace_size(dp.cfg, 1, N, eg.ENGRAM_OP_SHARD), dtype=torch.uint8,
+                     device="cuda")
+    dy = H.to_dev(inp.dy)
+    cap = N * J
+    log(f"[bench-shard] G={G}: requests, gradients and forwards of {G} emulated GPUs")
+    ranks = []
+    for r in range(G):
+        tok = synth.zipf_tokens(synth.seed_of(wl.cfg, synth.S_TOKENS), N, wl.vocab, wl.zipf_s,
+                                offset=r * N).reshape(dp.B, dp.T)
+        dp.tokens_host, dp.tokens = tok, H.to_dev(tok)
+        saved = dp.alloc_saved(("idx", "stats", "k", "v"))
+        dp.forward(saved)
+        send_ids = torch.empty(cap, dtype=torch.int32, device="cuda")
+        counts = torch.empty(G, dtype=torch.int64, device="cuda")
+        inverse = torch.empty(N, J, dtype=torch.int32, device="cuda")
+        eg.engram_shard_requests(dp.cfg, G, saved["idx"], N, send_ids, counts, inverse, workspace=ws)
+        sp = dp.backward(saved, dy, eg.ENGRAM_GRAD_SORTED_SPARSE)
+        gids = torch.empty(cap, dtype=torch.int32, device="cuda")
+        grows = torch.empty(cap, D, dtype=torch.float32, device="cuda")
+        gcounts = torch.empty(G, dtype=torch.int64, device="cuda")
+        eg.engram_shard_grads(dp.cfg, G, sp["keys"], sp["rows"], sp["count"], cap, gids, grows, gcounts,
+                              workspace=ws)
+        c, gc = counts.cpu().numpy(), gcounts.cpu().numpy()
+        keep = {"c": c, "gc": gc}
+        # what GPU 0 receives as owner: block 0 of every GPU
+        keep["req0"] = send_ids[: c[0]].clone()
+        keep["g0"] = (gids[: gc[0]].clone(), grows[: gc[0]].clone())
+        if r == 0:
+            keep.update(tok=tok, saved=saved, send_ids=send_ids, inverse=inverse, sp=sp, gids=gids,
+                        grows=grows, gcounts_dev=gcounts)
+        else:
+            del saved, sp, gids, grows
+        ranks.append(keep)
+        torch.cuda.empty_cache()
+    r0 = ranks[0]
+    # owner 0: requests of all GPUs in GPU order, and their gradient rows
+    recv = torch.cat([rk["req0"] for rk in ranks])
+    served = torch.empty(recv.numel() * rb, dtype=torch.uint8, device="cuda")
+    gids0 = torch.cat([rk["g0"][0] for rk in ranks])
+    grows0 = torch.cat([rk["g0"][1] for rk in ranks]).contiguous()
+    gblocks = [int(rk["gc"][0]) for rk in ranks]
+    shard_grads = [torch.zeros(S[j] * D, dtype=torch.float32, device="cuda") for j in range(J)]
+    # GPU 0's replies: block 0 of each owner; owner 0's is served above, the
+    # others' are the same rows read from the whole tables (an owner's serve
+    # is the same kernel on its shard)
+    offs = np.concatenate([[0], np.cumsum(r0["c"])])
+    parts = []
+    for o in range(G):
+        ids_o = r0["send_ids"][offs[o]: offs[o + 1]]
+        out = torch.empty(max(ids_o.numel(), 1) * rb, dtype=torch.uint8, device="cuda")
+        sh = [dp.tables[j].view(-1)[o * S[j] * D: min((o + 1) * S[j], int(inp.table_rows[j])) * D]
+              for j in range(J)]
+        eg.engram_shard_serve(dp.cfg, G, sh, ids_o, ids_o.numel(), out)
+        parts.append(out[: ids_o.numel() * rb])
+    replies = torch.cat(parts)
+    plan = eg.engram_compact()
+    plan.rows_dev, plan.inverse_dev = replies.data_ptr(), r0["inverse"].data_ptr()
+    dp.tokens_host, dp.tokens = r0["tok"], H.to_dev(r0["tok"])
+    y_ref = dp.forward()
+    y = dp.forward(compact=plan)
+    torch.cuda.synchronize()
+    bit_identical = bool(torch.equal(y, y_ref))
+    fwd_ws = dp.workspace(eg.ENGRAM_OP_FORWARD)
+    steps = args.steps
+    timings = {}
+
+    def run(label, fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        eg.engram_profile_reset()
+        eg.engram_profile_enable(True)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(steps):
+            fn()
+        a1.record()
+        torch.cuda.synchronize()
+        eg.engram_profile_enable(False)
+        prof = {k: round(tot / max(n, 1), 5) for k, (n, tot) in eg.engram_profile_read().items()}
+        timings[label] = {"ms": round(a0.elapsed_time(a1) / steps, 4), "kernels_avg_ms": prof}
+
+    run("sender_requests", lambda: eg.engram_shard_requests(dp.cfg, G, r0["saved"]["idx"], N, r0["send_ids"],
+                                                            torch.empty(G, dtype=torch.int64, device="cuda"),
+                                                            torch.empty(N, J, dtype=torch.int32, device="cuda"),
+                                                            workspace=ws))
+    run("owner_serve", lambda: eg.engram_shard_serve(dp.cfg, G, shards0, recv, recv.numel(), served))
+    y_out = torch.empty_like(y)
+    run("forward_served_rows", lambda: dp.forward(compact=plan, ws=fwd_ws, y=y_out))
+    run("forward_whole_tables", lambda: dp.forward(ws=fwd_ws, y=y_out))
+    run("sender_grad_rows", lambda: eg.engram_shard_grads(dp.cfg, G, r0["sp"]["keys"], r0["sp"]["rows"],
+                                                          r0["sp"]["count"], cap, r0["gids"], r0["grows"],
+                                                          r0["gcounts_dev"], workspace=ws))
+    run("owner_grad_reduce", lambda: eg.engram_shard_reduce(dp.cfg, G, shard_grads, gids0, grows0, gblocks))
+    # bytes GPU 0 moves over the fabric per step (to or from the other G-1 GPUs)
+    c0 = r0["c"]
+    recv_from = [int(rk["c"][0]) for rk in ranks]
+    g_out = r0["gc"]
+    send, recv_b = [], []
+    for o in range(1, G):
+        # to peer o: requests, replies to its requests, gradient rows of its rows
+        send.append(int(c0[o]) * 4 + recv_from[o] * rb + int(g_out[o]) * (4 + 4 * D))
+        # from peer o: replies, its requests, its gradient rows of GPU 0's rows
+        recv_b.append(int(c0[o]) * rb + recv_from[o] * 4 + int(ranks[o]["gc"][0]) * (4 + 4 * D))
+    per_peer = [max(a, b) for a, b in zip(send, recv_b)]
+    link = 153e9
+    out = {
+        "metric": "table-sharded Engram step, device side of one of G GPUs",
+        "workload": wl.name, "gpus_emulated": G, "tokens_per_gpu": N, "tables": J,
+        "shard_rows_per_table": S[0], "distinct_rows_requested": int(c0.sum()),
+        "rows_served_by_owner": int(recv.numel()), "grad_rows_received_by_owner": int(gids0.numel()),
+        "forward_bit_identical": bit_identical, "timings": timings,
+        "fabric_bytes_sent": int(sum(send)), "fabric_bytes_received": int(sum(recv_b)),
+        "fabric_ms_at_153GBps_per_link": round(max(per_peer) / link * 1e3, 3),
+        "note": "one GPU; the All-to-All transfers are device copies here, their time modelled "
+                "as the largest per-peer volume over one xGMI link (pairwise exchange, 7 links)",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration(nbytes: int):
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -583,6 +726,8 @@ def main():
     ap.add_argument("--calibration-bytes", type=int, default=1 << 30)
     ap.add_argument("--branches", type=int, default=1,
                     help="M branches sharing the tables and W_V (own W_K, hidden state, gate, Y)")
+    ap.add_argument("--shard-gpus", type=int, default=8,
+                    help="GPUs the tables are sharded over for --workload shard27b")
     ap.add_argument("--ring-batches", type=int, default=8,
                     help="successive batches for the row-ring measurement of --workload host100b")
     ap.add_argument("--ring-factor", type=int, default=16,
@@ -604,6 +749,9 @@ def main():
               "the multi-GPU table sharding is a design note, not a code path", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "shard27b":
+        bench_shard(args)
+        return
     if args.workload == "host100b":
         bench_host(args)
         return
