@@ -193,8 +193,9 @@ struct BwdWs {
   // parameter gradients
   uint8_t* e;      // [N][d_mem] dtype, rows gathered again (when e was not saved)
   float* dw_part;  // [splits][2d][d_mem] (splits > 1)
-  float* pacc;     // [nblk][d][taps+1]
+  float* pacc;     // [M][nblk][d][taps+1]
   float* ptmp;     // bwd_param_tmp_floats
+  float* dv_acc;   // [N][d] fp32 with M > 1 branches
   int32_t splits;
 };
 
@@ -213,19 +214,22 @@ size_t backward_ws(const Shape& s, int64_t B, int64_t T, BwdWs* out, uint8_t* ba
     return p;
   };
   BwdWs w{};
-  w.dkv = take((size_t)round_pad(N) * 2 * s.d * eg);
+  const int64_t cols = (int64_t)(s.M + 1) * s.d;  // [dk of each branch | dv]
+  w.dkv = take((size_t)round_pad(N) * cols * eg);
+  if (s.M > 1) w.dv_acc = (float*)take((size_t)N * s.d * 4);
   if (table) {
-    w.wt = take((size_t)s.d_mem * 2 * s.d * eg);
+    w.wt = take((size_t)s.d_mem * cols * eg);
     w.de = (float*)take((size_t)N * s.d_mem * 4);
     w.sort = take(sort_workspace_bytes(N, s.J));
   }
   if (params) {
     if (need_e) w.e = take((size_t)N * s.d_mem * s.es);
-    w.splits = tn_splits(N, 2 * s.d, s.d_mem);
-    if (w.splits > 1) w.dw_part = (float*)take((size_t)w.splits * 2 * s.d * s.d_mem * 4);
+    w.splits = tn_splits(N, (int32_t)cols, s.d_mem);
+    if (w.splits > 1) w.dw_part = (float*)take((size_t)w.splits * cols * s.d_mem * 4);
     const int64_t nb = std::max<int64_t>(1, bwd_blocks(B, T));
-    w.pacc = (float*)take((size_t)nb * s.d * (s.taps + 1) * 4);
-    w.ptmp = (float*)take((size_t)std::max<int64_t>(1, bwd_param_tmp_floats(nb, s.d, s.taps)) * 4);
+    w.pacc = (float*)take((size_t)s.M * nb * s.d * (s.taps + 1) * 4);
+    w.ptmp = (float*)take(
+        (size_t)std::max<int64_t>(1, bwd_param_tmp_floats(s.M * nb, s.d, s.taps)) * 4);
   }
   if (out) *out = w;
   return off;
@@ -446,7 +450,6 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
   if (!p || (!out && !pg) || B < 0 || T < 0 || T > INT32_MAX || B > 65535) return ENGRAM_E_INVALID;
   if (s.d / 4 > 1024) return ENGRAM_E_UNSUPPORTED;
   if (s.D > 256) return ENGRAM_E_UNSUPPORTED;  // one 16-byte piece per lane of a row
-  if (s.M > 1) return ENGRAM_E_UNSUPPORTED;    // the backward has one branch
   const int64_t N = B * T;
   if ((uint64_t)N * (uint64_t)s.J >= (uint64_t(1) << 31)) return ENGRAM_E_UNSUPPORTED;
   if (out) {
@@ -486,7 +489,11 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
   hipStream_t hs = (hipStream_t)stream;
   const bool bf = s.dtype == ENGRAM_BF16;
 
-  if (N > 0) {
+  const int64_t nblk = bwd_blocks(B, T);
+  const int64_t cols = (int64_t)(s.M + 1) * s.d;
+  const size_t act = (size_t)N * s.d * s.es;  // bytes of one branch's [N][d] activations
+  // one launch per branch; the shared v's gradient gathers over them
+  for (int m = 0; m < s.M && N > 0; ++m) {
     BwdArgs ba;
     std::memset(&ba, 0, sizeof(ba));
     ba.B = B;
@@ -494,19 +501,23 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
     ba.d = s.d;
     ba.taps = s.taps;
     ba.io_dtype = s.dtype;
-    ba.dy = (const uint8_t*)dy;
+    ba.dy = (const uint8_t*)dy + m * act;
     ba.v = (const uint8_t*)saved->v;
-    ba.k = (const uint8_t*)saved->k;
-    ba.h = (const uint8_t*)hidden;
-    ba.stats = saved->stats;
+    ba.k = (const uint8_t*)saved->k + m * act;
+    ba.h = (const uint8_t*)hidden + m * act;
+    ba.stats = saved->stats + (size_t)m * N * 4;
     ba.conv_w = p->conv_w;
-    ba.gamma_q = p->gamma_q;
-    ba.gamma_k = p->gamma_k;
+    ba.gamma_q = p->gamma_q ? p->gamma_q + (size_t)m * s.d : nullptr;
+    ba.gamma_k = p->gamma_k ? p->gamma_k + (size_t)m * s.d : nullptr;
     ba.dkv = w.dkv;
+    ba.branches = s.M;
+    ba.branch = m;
+    ba.dv_acc = w.dv_acc;
+    ba.dv_mode = s.M == 1 ? 0 : (m == 0 ? 1 : (m + 1 < s.M ? 2 : 3));
     if (pg) {
-      ba.pacc = want_sums ? w.pacc : nullptr;
-      ba.dh = (uint8_t*)pg->hidden;
-      ba.pad_rows = want_w ? (int32_t)(round_pad(N) - N) : 0;
+      ba.pacc = want_sums ? w.pacc + (size_t)m * nblk * s.d * (s.taps + 1) : nullptr;
+      ba.dh = pg->hidden ? (uint8_t*)pg->hidden + m * act : nullptr;
+      ba.pad_rows = want_w && m == 0 ? (int32_t)(round_pad(N) - N) : 0;
     }
     Timed tm(pg ? "bwd_gate_conv_params" : "bwd_gate_conv", hs);
     if (launch_bwd_gate_conv(ba, hs) != hipSuccess) return ENGRAM_E_HIP;
@@ -514,7 +525,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
   if (out && N > 0) {
     {
       Timed tm("transpose_w", hs);
-      if (launch_transpose_w((const uint8_t*)p->w_kv, w.wt, 2 * s.d, s.d_mem, s.dtype, hs) !=
+      if (launch_transpose_w((const uint8_t*)p->w_kv, w.wt, (int32_t)cols, s.d_mem, s.dtype, hs) !=
           hipSuccess)
         return ENGRAM_E_HIP;
     }
@@ -524,7 +535,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
     ga.B = w.dkv;
     ga.M = N;
     ga.F = s.d_mem;
-    ga.K = 2 * s.d;
+    ga.K = (int32_t)cols;
     ga.group_m = 4;
     ga.stage_bytes = kBwdStageBytes;
     ga.persistent = ENGRAM_GEMM_PERSISTENT;
@@ -537,17 +548,34 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
     if (want_sums) {
       if (N > 0) {
         Timed tm("bwd_param_sums", hs);
-        if (launch_bwd_param_sums(w.pacc, w.ptmp, bwd_blocks(B, T), s.d, s.taps, p->gamma_q,
-                                  p->gamma_k, pg->conv_w, pg->gamma_q, pg->gamma_k,
-                                  hs) != hipSuccess)
-          return ENGRAM_E_HIP;
+        if (s.M == 1) {
+          if (launch_bwd_param_sums(w.pacc, w.ptmp, nblk, s.d, s.taps, p->gamma_q, p->gamma_k,
+                                    pg->conv_w, pg->gamma_q, pg->gamma_k, hs) != hipSuccess)
+            return ENGRAM_E_HIP;
+        } else {
+          // the conv is shared: its sums run over every branch's blocks; the
+          // RMSNorm scales are per branch
+          if (pg->conv_w && launch_bwd_param_sums(w.pacc, w.ptmp, s.M * nblk, s.d, s.taps, nullptr,
+                                                  nullptr, pg->conv_w, nullptr, nullptr,
+                                                  hs) != hipSuccess)
+            return ENGRAM_E_HIP;
+          for (int m = 0; m < s.M && (pg->gamma_q || pg->gamma_k); ++m) {
+            const size_t o = (size_t)m * s.d;
+            if (launch_bwd_param_sums(w.pacc + (size_t)m * nblk * s.d * (s.taps + 1), w.ptmp, nblk,
+                                      s.d, s.taps, p->gamma_q ? p->gamma_q + o : nullptr,
+                                      p->gamma_k ? p->gamma_k + o : nullptr, nullptr,
+                                      pg->gamma_q ? pg->gamma_q + o : nullptr,
+                                      pg->gamma_k ? pg->gamma_k + o : nullptr, hs) != hipSuccess)
+              return ENGRAM_E_HIP;
+          }
+        }
       } else {
         // no tokens: the sums are zero
         if (pg->conv_w && launch_zero_f32(pg->conv_w, (int64_t)s.d * s.taps, hs) != hipSuccess)
           return ENGRAM_E_HIP;
-        if (pg->gamma_q && launch_zero_f32(pg->gamma_q, s.d, hs) != hipSuccess)
+        if (pg->gamma_q && launch_zero_f32(pg->gamma_q, (int64_t)s.M * s.d, hs) != hipSuccess)
           return ENGRAM_E_HIP;
-        if (pg->gamma_k && launch_zero_f32(pg->gamma_k, s.d, hs) != hipSuccess)
+        if (pg->gamma_k && launch_zero_f32(pg->gamma_k, (int64_t)s.M * s.d, hs) != hipSuccess)
           return ENGRAM_E_HIP;
       }
     }
@@ -563,17 +591,17 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
         if (launch_gather(saved->idx, w.e, N, g, hs) != hipSuccess) return ENGRAM_E_HIP;
       }
       if (N == 0) {
-        if (launch_zero_f32(pg->w_kv, (int64_t)2 * s.d * s.d_mem, hs) != hipSuccess)
+        if (launch_zero_f32(pg->w_kv, cols * s.d_mem, hs) != hipSuccess)
           return ENGRAM_E_HIP;
       } else {
         GemmTnArgs ta;
         std::memset(&ta, 0, sizeof(ta));
         ta.x = w.dkv;
         ta.y = e;
-        ta.ldx = 2 * s.d;
+        ta.ldx = cols;
         ta.ldy = s.d_mem;
         ta.K = N;
-        ta.m = 2 * s.d;
+        ta.m = (int32_t)cols;
         ta.n = s.d_mem;
         ta.splits = w.splits;
         ta.kchunk = ((N + kTnPadTokens - 1) / kTnPadTokens + w.splits - 1) / w.splits * kTnPadTokens;

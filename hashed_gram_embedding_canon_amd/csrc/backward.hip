@@ -27,6 +27,10 @@
 //   dh_t = ca g_q g_k k_t - cq h_t,  cq = rq^3 ds rk P / (sqrt(d) d)
 // (the query's RMSNorm backward, the mirror of dk), and sums
 // ca h_t k_t, of which the RMSNorm scales' gradients are g_k and g_q times.
+// With M branches the kernel runs once per branch m (its dY, h, k, stats):
+// dk of branch m goes to its columns of the [dk_0 .. dk_{M-1} | dv] row, and
+// the shared v's gradient sum_m alpha_m dvt_m gathers in an fp32 buffer that
+// the last branch rounds into the row (dv_mode).
 #include <type_traits>
 
 #include "kernels.h"
@@ -36,6 +40,8 @@ namespace engram {
 constexpr int kBwTokens = 64;   // R
 constexpr int kBwBatch = 8;     // tokens per dalpha reduction batch
 constexpr int kBwMaxWaves = 16; // d / 4 / 64
+// dv of this launch: written (one branch), or gathered over the branches
+enum { kDvDirect = 0, kDvFirst = 1, kDvAdd = 2, kDvLast = 3 };
 
 template <bool BF16>
 using raw4_t = typename std::conditional<BF16, u32x2, u32x4>::type;
@@ -136,6 +142,7 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   const int nwaves = blockDim.x >> 6;
   const int64_t row0 = b * T;
   const int64_t tend = t0 + R < T ? t0 + R : T;  // tokens [t0, tend) are this block's
+  const int64_t ld = (int64_t)(a.branches + 1) * d;  // elements of a [dk_0 .. | dv] row
   float w[4][TAPS];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -248,7 +255,22 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       dv[c] = alpha * acc;
     }
     pb[pslot] = pd;
-    st4_grad<BF16>(a.dkv, (row0 + t) * 2 * d + d + f, dv);
+    if (a.dv_mode == kDvDirect) {
+      st4_grad<BF16>(a.dkv, (row0 + t) * ld + a.branches * d + f, dv);
+    } else {
+      floatx4* acc = reinterpret_cast<floatx4*>(a.dv_acc + (row0 + t) * d + f);
+      if (a.dv_mode == kDvFirst) {
+        *acc = floatx4{dv[0], dv[1], dv[2], dv[3]};
+      } else {
+        const floatx4 prev = *acc;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dv[c] += prev[c];
+        if (a.dv_mode == kDvAdd)
+          *acc = floatx4{dv[0], dv[1], dv[2], dv[3]};
+        else
+          st4_grad<BF16>(a.dkv, (row0 + t) * ld + a.branches * d + f, dv);
+      }
+    }
   };
 
   // warm-up: u = t0-NH .. t0+NH-1 (no token final yet)
@@ -320,7 +342,7 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       widen4<BF16>(rk[q], kv);
 #pragma unroll
       for (int c = 0; c < 4; ++c) dk[c] = ca * gqk[c] * hv[c] - cb * kv[c];
-      st4_grad<BF16>(a.dkv, (row0 + t) * 2 * d + f, dk);
+      st4_grad<BF16>(a.dkv, (row0 + t) * ld + a.branch * d + f, dk);
       if constexpr (PARAMS) {
         const float cq = rq * rq * rq * ds * rkk * P * inv_sqrt_d * inv_d;
         float dh[4];
@@ -342,10 +364,8 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
     if (blockIdx.x == 0 && blockIdx.y == 0) {
       const float z4[4] = {0.f, 0.f, 0.f, 0.f};
       const int64_t N = a.B * T;
-      for (int r = 0; r < a.pad_rows; ++r) {
-        st4_grad<BF16>(a.dkv, (N + r) * 2 * d + f, z4);
-        st4_grad<BF16>(a.dkv, (N + r) * 2 * d + d + f, z4);
-      }
+      for (int r = 0; r < a.pad_rows; ++r)
+        for (int c = 0; c <= a.branches; ++c) st4_grad<BF16>(a.dkv, (N + r) * ld + c * d + f, z4);
     }
   }
 }
@@ -381,6 +401,10 @@ hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s) {
   dim3 grid((unsigned)((a.T + kBwTokens - 1) / kBwTokens), (unsigned)a.B);
   const bool params = a.pacc || a.dh || a.pad_rows > 0;
   if (a.pad_rows < 0 || a.pad_rows > 64) return hipErrorInvalidValue;
+  if (a.branches < 1 || a.branch < 0 || a.branch >= a.branches || a.dv_mode < kDvDirect ||
+      a.dv_mode > kDvLast || (a.dv_mode != kDvDirect && !a.dv_acc) ||
+      (a.dv_mode == kDvDirect && a.branches != 1))
+    return hipErrorInvalidValue;
   const bool narrow = threads <= 768;
   if (a.io_dtype == ENGRAM_BF16) {
     if (!params) return launch_bwd_taps<true, false, 1024>(a, grid, threads, s);

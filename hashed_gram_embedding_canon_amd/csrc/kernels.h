@@ -84,7 +84,12 @@ struct BwdArgs {
   const float* conv_w;    // [d][taps]
   const float* gamma_q;
   const float* gamma_k;
-  uint8_t* dkv;           // [N][2d] fp16 (bf16 io) or fp32 (f32 io)
+  uint8_t* dkv;           // [N][(branches+1)d] fp16 (bf16 io) or fp32 (f32 io): dk of each
+                          // branch, then dv
+  int32_t branches;       // M (1 for one branch)
+  int32_t branch;         // the branch of this launch: its dy, h, k, stats, dh, pacc
+  float* dv_acc;          // [N][d] fp32 when branches > 1: the shared v's gradient so far
+  int32_t dv_mode;        // 0: write dv; 1: dv_acc = dv; 2: dv_acc += dv; 3: write dv + dv_acc
   // parameter gradients (null = not wanted)
   float* pacc;            // [nblk][d][taps+1]: per workgroup, sum_t dz_t vt_{t-i} per tap and
                           // sum_t (ds rq rk / sqrt d) h_t k_t (the RMSNorm scales' shared sum)

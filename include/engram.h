@@ -189,13 +189,13 @@ typedef struct {
  * II", section "DeepSeek Engram" (the pages print no backward).
  */
 typedef struct {
-  float* w_kv;     /* [2d][d_mem] fp32: dL/dW_KV = sum_t [dk_t; dv_t] e_t^T, rows as in
-                      params->w_kv (the key rows, then the value rows) */
+  float* w_kv;     /* [(M+1)d][d_mem] fp32: dL/dW_KV = sum_t [dk_t; dv_t] e_t^T, rows as in
+                      params->w_kv (each branch's key rows, then the value rows) */
   float* conv_w;   /* [d][conv_kernel] fp32: sum_t dz_t[c] vt_{t-i}[c] */
-  float* gamma_q;  /* [d] fp32: dL/dg_q (of params->gamma_q, or of all-ones scales when NULL) */
-  float* gamma_k;  /* [d] fp32: dL/dg_k */
-  void* hidden;    /* [B][T][d] dtype: the gate's part of dL/dh_t through the query's RMSNorm
-                      (the residual H + Y adds G itself, which is the caller's) */
+  float* gamma_q;  /* [M][d] fp32: dL/dg_q (of params->gamma_q, or of all-ones scales when NULL) */
+  float* gamma_k;  /* [M][d] fp32: dL/dg_k */
+  void* hidden;    /* [M][B][T][d] dtype: the gate's part of dL/dh_t through the query's
+                      RMSNorm (the residual H + Y adds G itself, which is the caller's) */
 } engram_param_grad;
 
 enum {
@@ -248,8 +248,9 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* para
  * they came from).  Chain rule through the conv, the gate, the RMSNorm of the
  * key and both projections to de_t, then dE_j[r] = sum_{t: idx_j(t)=r}
  * de_t[j*D:(j+1)*D] with fp32 accumulation.
- *   hidden, dy: device [B][T][d] dtype; saved: idx, stats, k, v from
- *   engram_forward on the same inputs (required); out: see engram_table_grad;
+ *   hidden, dy: device [M][B][T][d] dtype (M = branches); saved: idx,
+ *   stats, k, v from engram_forward on the same inputs (required); out: see
+ *   engram_table_grad (the gradients of all branches, summed);
  *   workspace: >= engram_workspace_size(cfg, B, T, ENGRAM_OP_BACKWARD).
  */
 engram_status engram_backward_table_grad(const engram_config* cfg, const engram_params* params,
@@ -270,7 +271,12 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
  *   when param_out is given, else ENGRAM_OP_BACKWARD.
  * dW_KV takes its operands in fp16 (bf16 io) like the de contraction and sums
  * in fp32 over token chunks, the chunks in a fixed order (deterministic).
- * One branch only (branches 0 or 1), d a multiple of 256, d_mem of 256.
+ * With M branches (the loss is the sum over the branches' outputs): hidden,
+ * dy, saved->k and saved->stats hold every branch ([M][...] as in
+ * engram_forward); the table, W_V and conv gradients sum the branches;
+ * dW_KV has the rows of params->w_kv ([(M+1)d][d_mem]); the RMSNorm scale
+ * gradients are [M][d] and the hidden-state gradient [M][B][T][d].
+ * d a multiple of 256, and d_mem of 256 for the parameter gradients.
  */
 engram_status engram_backward(const engram_config* cfg, const engram_params* params,
                               const void* hidden, const void* dy, int64_t B, int64_t T,

@@ -227,6 +227,15 @@ class Inputs:
             seed_of(wl.cfg, S_DY), wl.B * wl.T * wl.hidden, 1.0, wl.dtype).reshape(wl.B, wl.T, wl.hidden))
 
 
+    def dy_branch(self, m: int) -> np.ndarray:  # [B, T, d] upstream gradient of branch m's Y
+        if m == 0:
+            return self.dy
+        wl = self.wl
+        n = wl.B * wl.T * wl.hidden
+        return self._get(("dy", m), lambda: normal_stream(
+            seed_of(wl.cfg, S_DY), n, 1.0, wl.dtype, offset=m * n).reshape(wl.B, wl.T, wl.hidden))
+
+
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns (uint16) to float32."""
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)

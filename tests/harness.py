@@ -138,10 +138,12 @@ class DeviceProblem:
         """engram_backward with parameter gradients only -> dict of tensors."""
         torch = torch_mod()
         eg, wl = self.eg, self.wl
-        d = wl.hidden
-        shapes = {"w_kv": ((2 * d, wl.d_mem), torch.float32), "conv_w": ((d, wl.taps), torch.float32),
-                  "gamma_q": ((d,), torch.float32), "gamma_k": ((d,), torch.float32),
-                  "hidden": ((self.B, self.T, d), self.tdtype)}
+        d, M = wl.hidden, self.M
+        lead = () if M == 1 else (M,)
+        shapes = {"w_kv": (((M + 1) * d, wl.d_mem), torch.float32),
+                  "conv_w": ((d, wl.taps), torch.float32),
+                  "gamma_q": (lead + (d,), torch.float32), "gamma_k": (lead + (d,), torch.float32),
+                  "hidden": (lead + (self.B, self.T, d), self.tdtype)}
         res = {k: torch.full(shapes[k][0], float("nan"), dtype=shapes[k][1], device=self.device)
                for k in want}
         pg = eg.make_param_grad(**res)

@@ -77,12 +77,52 @@ def test_small_bf16_branches_sampled(torch, oracle_lib):
         assert err <= TOL["bf16"], (m, err)
 
 
-def test_backward_rejects_branches(torch):
+@pytest.mark.parametrize("dtype,M,B,T", [("f32", 2, 1, 300), ("bf16", 3, 2, 150)])
+def test_branch_backward(torch, oracle_lib, dtype, M, B, T):
+    """Training backward with M branches: the loss is the sum of the branches'
+    <G^(m), Y^(m)>, so the table, W_V and conv gradients are the sums of the
+    single-branch oracle's over the branches, and dW_K^(m), the RMSNorm
+    scales and dh are branch m's own."""
     import hashed_gram_embedding_canon_amd as eg
-    wl = dataclasses.replace(synth.get_workload("tiny"), branches=2).with_shape(1, 64)
+    wl = dataclasses.replace(synth.get_workload("tiny"), dtype=dtype, branches=M).with_shape(B, T)
+    print(f"[branch bwd {dtype}] M={M} B={B} T={T}", flush=True)
     inp = synth.Inputs(wl)
     dp = H.DeviceProblem(inp)
     bufs = dp.alloc_saved(("idx", "stats", "k", "v"))
     dp.forward(bufs)
-    with pytest.raises(eg.EngramError, match="status 2"):
-        dp.backward(bufs, H.to_dev(inp.dy), eg.ENGRAM_GRAD_SORTED_SPARSE)
+    dy = H.to_dev(np.ascontiguousarray(np.stack([inp.dy_branch(m) for m in range(M)])))
+    table = dp.backward(bufs, dy, eg.ENGRAM_GRAD_SORTED_DENSE)["dense"]
+    pg = dp.backward_params(bufs, dy)
+    torch.cuda.synchronize()
+    d = wl.hidden
+    ref_tab = None
+    ref = {"w_kv": np.zeros(((M + 1) * d, wl.d_mem)), "conv_w": 0.0, "gamma_q": [], "gamma_k": [],
+           "hidden": []}
+    for m in range(M):
+        p = H.oracle_problem(inp, branch=m)
+        dym = inp.dy_branch(m)
+        tg = p.table_grad_dense(dym)
+        ref_tab = tg if ref_tab is None else [a + b for a, b in zip(ref_tab, tg)]
+        g = p.backward_params(dym)
+        ref["w_kv"][m * d:(m + 1) * d] = g["w_k"]
+        ref["w_kv"][M * d:] += g["w_v"]
+        ref["conv_w"] = ref["conv_w"] + g["conv_w"]
+        for k in ("gamma_q", "gamma_k"):
+            ref[k].append(g[k])
+        ref["hidden"].append(g["h"])
+    got_tab = np.concatenate([t.cpu().numpy().astype(np.float64).ravel() for t in table])
+    err = H.rel_l2(got_tab, np.concatenate([r.ravel() for r in ref_tab]))
+    print(f"  table grads rel L2 {err:.2e}", flush=True)
+    assert err <= 1e-3, err
+    bf = dtype == "bf16"
+    for k in ("w_kv", "conv_w", "gamma_q", "gamma_k", "hidden"):
+        r = np.asarray(ref[k], np.float64)
+        got = H.to_host_f64(pg[k]).reshape(r.shape)
+        if k == "hidden" and bf:
+            e = H.rel_max_err(got, r)
+            bar = 1e-2
+        else:
+            e = H.rel_l2(got, r)
+            bar = 5e-3 if bf else 1e-5
+        print(f"  {k}: {e:.2e}", flush=True)
+        assert e <= bar, (k, e)
