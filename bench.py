@@ -217,16 +217,20 @@ def traffic_from_profile(workload: str) -> dict:
 
 
 def backward_units(wl, N):
-    """Algorithmic bytes / flops per launch of each table-gradient backward kernel."""
+    """Algorithmic bytes / flops per launch of each table-gradient backward
+    kernel.  With M branches the elementwise backward runs once per branch
+    (dv gathers over them in fp32) and the contractions run over (M+1)d."""
     es = 2 if wl.dtype == "bf16" else 4
     eg_ = 2 if wl.dtype == "bf16" else 4          # fp16 / fp32 GEMM operands
-    J, d, dm, D = wl.J, wl.hidden, wl.d_mem, wl.dim
+    J, d, dm, D, M = wl.J, wl.hidden, wl.d_mem, wl.dim, wl.branches
+    # dv per launch: written once (one branch), or fp32 first / add / last over M launches
+    dv = N * d * eg_ if M == 1 else (N * d * (4 + 8 * (M - 2) + 4) + N * d * eg_) / M
     return {
-        # dy, v, k, h in; stats; dk|dv out
-        "bwd_gate_conv": {"bound": "hbm", "bytes": 4 * N * d * es + N * 16 + N * 2 * d * eg_},
-        "transpose_w": {"bound": "hbm", "bytes": 2 * d * dm * es + 2 * d * dm * eg_},
-        "de_gemm": {"bound": "mfma", "flops": 2 * N * 2 * d * dm,
-                    "bytes": N * 2 * d * eg_ + 2 * d * dm * eg_ + N * dm * 4},
+        # dy, v, k, h in; stats; dk out, dv
+        "bwd_gate_conv": {"bound": "hbm", "bytes": 4 * N * d * es + N * 16 + N * d * eg_ + dv},
+        "transpose_w": {"bound": "hbm", "bytes": (M + 1) * d * dm * (es + eg_)},
+        "de_gemm": {"bound": "mfma", "flops": 2 * N * (M + 1) * d * dm,
+                    "bytes": N * (M + 1) * d * eg_ + (M + 1) * d * dm * eg_ + N * dm * 4},
         # idx + de in, at most one fp32 row + key per (token, table) out
         "sorted_scatter": {"bound": "hbm", "bytes": N * J * 4 + N * dm * 4 + N * J * (D * 4 + 8)},
         "atomic_scatter": {"bound": "hbm", "bytes": N * J * 4 + N * dm * 4 + N * J * D * 4},
@@ -247,8 +251,9 @@ def training_units(wl, N):
     # rows gathered again: indices + rows in, e out
     u["gather"] = {"bound": "hbm", "bytes": N * J * 4 + 2 * N * dm * es}
     # dW = [dk|dv]^T e: both token-major operands once, dW once
-    u["dw_gemm"] = {"bound": "mfma", "flops": 2 * N * 2 * d * dm,
-                    "bytes": N * 2 * d * eg_ + N * dm * es + 2 * d * dm * 4}
+    M = wl.branches
+    u["dw_gemm"] = {"bound": "mfma", "flops": 2 * N * (M + 1) * d * dm,
+                    "bytes": N * (M + 1) * d * eg_ + N * dm * es + (M + 1) * d * dm * 4}
     u["bwd_param_sums"] = {"bound": "hbm", "bytes": nblk * d * (taps + 1) * 4}
     return u
 
@@ -263,9 +268,11 @@ def bench_backward(dp, inp, steps: int) -> dict:
     import hashed_gram_embedding_canon_amd as eg
     from tests import harness as H
     wl, N = dp.wl, dp.N
+    import numpy as np
     saved = dp.alloc_saved(("idx", "stats", "k", "v"))
     dp.forward(saved)
-    dy = H.to_dev(inp.dy)
+    M = wl.branches
+    dy = H.to_dev(inp.dy if M == 1 else np.ascontiguousarray(np.stack([inp.dy_branch(m) for m in range(M)])))
     ws = dp.workspace(eg.ENGRAM_OP_BACKWARD_PARAMS)
     res = {}
     for mode, label in ((eg.ENGRAM_GRAD_SORTED_SPARSE, "sorted_sparse"),
@@ -766,7 +773,6 @@ def main():
     if args.branches != 1:
         import dataclasses
         wl = dataclasses.replace(wl, branches=args.branches)
-        args.no_backward = True  # the table-gradient backward has one branch
         args.no_cpu_baseline = True  # the oracle baseline is timed on one branch
     N = wl.n_tokens
     log(f"[bench] {wl.name}: B={wl.B} T={wl.T} J={wl.J} D={wl.dim} d={wl.hidden} "

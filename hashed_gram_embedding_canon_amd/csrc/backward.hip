@@ -113,7 +113,8 @@ __device__ inline float wave_sum8(float p[8], int lane) {
 // MAXT: the largest block it is launched with.  One workgroup of d/4 lanes
 // fits a CU at d = 2560 whatever the register count up to 168, and the
 // parameter sums need more than the 128 that 1024 threads leave.
-template <bool BF16, int TAPS, bool PARAMS, int MAXT>
+// MULTI: one of several branches (dv gathers in dv_acc); else dv is written.
+template <bool BF16, int TAPS, bool PARAMS, int MAXT, bool MULTI>
 __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   constexpr int R = kBwTokens;
   constexpr int NH = TAPS - 1;
@@ -142,7 +143,10 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   const int nwaves = blockDim.x >> 6;
   const int64_t row0 = b * T;
   const int64_t tend = t0 + R < T ? t0 + R : T;  // tokens [t0, tend) are this block's
-  const int64_t ld = (int64_t)(a.branches + 1) * d;  // elements of a [dk_0 .. | dv] row
+  // elements of a [dk_0 .. | dv] row, and where this launch's dk and the dv sit in it
+  const int64_t ld = MULTI ? (int64_t)(a.branches + 1) * d : 2 * (int64_t)d;
+  const int dk_col = MULTI ? a.branch * d : 0;
+  const int dv_col = MULTI ? a.branches * d : d;
   float w[4][TAPS];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -255,8 +259,8 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       dv[c] = alpha * acc;
     }
     pb[pslot] = pd;
-    if (a.dv_mode == kDvDirect) {
-      st4_grad<BF16>(a.dkv, (row0 + t) * ld + a.branches * d + f, dv);
+    if constexpr (!MULTI) {
+      st4_grad<BF16>(a.dkv, (row0 + t) * ld + dv_col + f, dv);
     } else {
       floatx4* acc = reinterpret_cast<floatx4*>(a.dv_acc + (row0 + t) * d + f);
       if (a.dv_mode == kDvFirst) {
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
         if (a.dv_mode == kDvAdd)
           *acc = floatx4{dv[0], dv[1], dv[2], dv[3]};
         else
-          st4_grad<BF16>(a.dkv, (row0 + t) * ld + a.branches * d + f, dv);
+          st4_grad<BF16>(a.dkv, (row0 + t) * ld + dv_col + f, dv);
       }
     }
   };
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       widen4<BF16>(rk[q], kv);
 #pragma unroll
       for (int c = 0; c < 4; ++c) dk[c] = ca * gqk[c] * hv[c] - cb * kv[c];
-      st4_grad<BF16>(a.dkv, (row0 + t) * ld + a.branch * d + f, dk);
+      st4_grad<BF16>(a.dkv, (row0 + t) * ld + dk_col + f, dk);
       if constexpr (PARAMS) {
         const float cq = rq * rq * rq * ds * rkk * P * inv_sqrt_d * inv_d;
         float dh[4];
@@ -365,18 +369,19 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       const float z4[4] = {0.f, 0.f, 0.f, 0.f};
       const int64_t N = a.B * T;
       for (int r = 0; r < a.pad_rows; ++r)
-        for (int c = 0; c <= a.branches; ++c) st4_grad<BF16>(a.dkv, (N + r) * ld + c * d + f, z4);
+        for (int c = 0; c <= (MULTI ? a.branches : 1); ++c)
+          st4_grad<BF16>(a.dkv, (N + r) * ld + c * d + f, z4);
     }
   }
 }
 
-template <bool BF16, bool PARAMS, int MAXT>
+template <bool BF16, bool PARAMS, int MAXT, bool MULTI>
 static hipError_t launch_bwd_taps(const BwdArgs& a, dim3 grid, int threads, hipStream_t s) {
   switch (a.taps) {
-#define ENGRAM_TAPS_CASE(K)                                                                   \
-  case K:                                                                                     \
-    hipLaunchKernelGGL((bwd_gate_conv_kernel<BF16, K, PARAMS, MAXT>), grid, dim3(threads), 0, \
-                       s, a);                                                                 \
+#define ENGRAM_TAPS_CASE(K)                                                                 \
+  case K:                                                                                   \
+    hipLaunchKernelGGL((bwd_gate_conv_kernel<BF16, K, PARAMS, MAXT, MULTI>), grid,         \
+                       dim3(threads), 0, s, a);                                             \
     break;
     ENGRAM_TAPS_CASE(1)
     ENGRAM_TAPS_CASE(2)
@@ -406,14 +411,27 @@ hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s) {
       (a.dv_mode == kDvDirect && a.branches != 1))
     return hipErrorInvalidValue;
   const bool narrow = threads <= 768;
+  const bool multi = a.dv_mode != kDvDirect;
   if (a.io_dtype == ENGRAM_BF16) {
-    if (!params) return launch_bwd_taps<true, false, 1024>(a, grid, threads, s);
-    return narrow ? launch_bwd_taps<true, true, 768>(a, grid, threads, s)
-                  : launch_bwd_taps<true, true, 1024>(a, grid, threads, s);
+    if (multi) {
+      if (!params) return narrow ? launch_bwd_taps<true, false, 768, true>(a, grid, threads, s)
+                                 : launch_bwd_taps<true, false, 1024, true>(a, grid, threads, s);
+      return narrow ? launch_bwd_taps<true, true, 768, true>(a, grid, threads, s)
+                    : launch_bwd_taps<true, true, 1024, true>(a, grid, threads, s);
+    }
+    if (!params) return launch_bwd_taps<true, false, 1024, false>(a, grid, threads, s);
+    return narrow ? launch_bwd_taps<true, true, 768, false>(a, grid, threads, s)
+                  : launch_bwd_taps<true, true, 1024, false>(a, grid, threads, s);
   }
-  if (!params) return launch_bwd_taps<false, false, 1024>(a, grid, threads, s);
-  return narrow ? launch_bwd_taps<false, true, 768>(a, grid, threads, s)
-                : launch_bwd_taps<false, true, 1024>(a, grid, threads, s);
+  if (multi) {
+    if (!params) return narrow ? launch_bwd_taps<false, false, 768, true>(a, grid, threads, s)
+                               : launch_bwd_taps<false, false, 1024, true>(a, grid, threads, s);
+    return narrow ? launch_bwd_taps<false, true, 768, true>(a, grid, threads, s)
+                  : launch_bwd_taps<false, true, 1024, true>(a, grid, threads, s);
+  }
+  if (!params) return launch_bwd_taps<false, false, 1024, false>(a, grid, threads, s);
+  return narrow ? launch_bwd_taps<false, true, 768, false>(a, grid, threads, s)
+                : launch_bwd_taps<false, true, 1024, false>(a, grid, threads, s);
 }
 
 int64_t bwd_blocks(int64_t B, int64_t T) { return B * ((T + kBwTokens - 1) / kBwTokens); }
