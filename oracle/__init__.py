@@ -58,6 +58,7 @@ class _Problem(ctypes.Structure):
         ("eps", ctypes.c_double),
         ("taps", ctypes.c_int32),
         ("conv_w", ctypes.c_void_p),
+        ("fp8_e", ctypes.c_int32),
     ]
 
 
@@ -78,6 +79,11 @@ def _load():
     lib.oracle_forward.argtypes = [P, i64, vp, vp, vp, vp, vp, vp]
     lib.oracle_backward_de.argtypes = [P, vp, i64, vp, vp]
     lib.oracle_backward_params.argtypes = [P, vp, i64, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_quantize_rows.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     lib.oracle_table_grad_rows.argtypes = [P, vp, vp, i64, vp, vp, vp]
     lib.oracle_table_grad_dense.argtypes = [P, vp, vp]
     lib.oracle_prefetch_plan.argtypes = [i64, i32, vp, vp, vp, vp]
@@ -111,7 +117,8 @@ class Problem:
     """
 
     def __init__(self, *, orders, heads, mult, table_rows, pad_id, canon_map, tokens, tables,
-                 w_k=None, w_v=None, h=None, conv_w=None, gamma_q=None, gamma_k=None, eps=1e-6):
+                 w_k=None, w_v=None, h=None, conv_w=None, gamma_q=None, gamma_k=None, eps=1e-6,
+                 fp8=False):
         J = len(orders) * heads
         assert len(orders) <= 4 and J <= 64 and len(tables) == J
         self.orders = tuple(int(o) for o in orders)
@@ -133,6 +140,10 @@ class Problem:
         self.d_mem = J * self.dim
         self.w_k = None if w_k is None else np.ascontiguousarray(w_k)
         self.w_v = None if w_v is None else np.ascontiguousarray(w_v)
+        if fp8 and self.w_k is not None:
+            # the FP8 projection reads each weight row in e4m3 with its own scale
+            self.w_k = quantize_rows(self.w_k)[2]
+            self.w_v = quantize_rows(self.w_v)[2]
         self.hidden = 0 if self.w_k is None else self.w_k.shape[0]
         if self.w_k is not None:
             assert self.w_k.shape == (self.hidden, self.d_mem) and self.w_v.shape == self.w_k.shape
@@ -171,6 +182,7 @@ class Problem:
         s.eps = self.eps
         s.taps = self.taps
         s.conv_w = _ptr(self.conv_w)
+        s.fp8_e = 1 if fp8 else 0
         self._s = s
 
     @classmethod
@@ -287,6 +299,29 @@ class Problem:
         ptrs = (ctypes.c_void_p * self.J)(*[g.ctypes.data for g in grads])
         _load().oracle_table_grad_dense(self.ref, _ptr(dy), ctypes.cast(ptrs, ctypes.c_void_p))
         return grads
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of an OCP E4M3 code (0..255; the NaN codes decode as their bit pattern says)."""
+    return float(_load().oracle_e4m3_decode(code))
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code, ties to even, saturating at 448."""
+    return int(_load().oracle_e4m3_encode(float(x)))
+
+
+def quantize_rows(x: np.ndarray):
+    """Per-row E4M3 quantization of a 2-D array (bf16 bits, fp32 or fp64):
+    (codes uint8, scales float32, dequantized float64), scale = max|row| / 448
+    and codes of x / scale, both in fp32."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols), np.uint8)
+    scales = np.empty(rows, np.float32)
+    deq = np.empty((rows, cols), np.float64)
+    _load().oracle_quantize_rows(_ptr(x), _dt(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(deq))
+    return codes, scales, deq
 
 
 def prefetch_plan(idx: np.ndarray):

@@ -66,6 +66,10 @@ typedef struct {
   double eps;
   int32_t taps;                  /* conv kernel width */
   const double* conv_w;          /* [d][taps], tap i multiplies position t-i */
+  /* FP8 projection [P1 "DeepSeek Engram", multi-branch integration: the
+   * projections as one dense FP8 matmul]: nonzero = e_t is quantized to e4m3
+   * per token before W_K and W_V apply (W is passed already quantized) */
+  int32_t fp8_e;
 } oracle_problem;
 
 static int n_tables(const oracle_problem* p) { return p->num_orders * p->heads; }
@@ -81,6 +85,77 @@ static double load_val(const void* base, int32_t dtype, int64_t i) {
 }
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* ------------------------------------------------------------------ FP8
+ * OCP 8-bit floating point, E4M3 ("fn": bias 7, no infinities, largest
+ * finite 448 = 1.75 * 2^8, code S.1111.111 is NaN).  Normal codes (exponent
+ * field E >= 1) are (1 + m/8) 2^(E-7); E = 0 holds the subnormals m 2^-9.
+ */
+double oracle_e4m3_decode(uint8_t code) {
+  int sgn = code >> 7, E = (code >> 3) & 15, m = code & 7;
+  double v = E ? ldexp(1.0 + m / 8.0, E - 7) : ldexp((double)m, -9);
+  return sgn ? -v : v;
+}
+
+/* Round x (any finite double) to the nearest E4M3 value, ties to the even
+ * mantissa, magnitudes above 448 saturating to 448. */
+uint8_t oracle_e4m3_encode(double x) {
+  uint8_t sgn = x < 0 ? 0x80 : 0;
+  double a = fabs(x);
+  if (a >= 448.0) return sgn | 0x7E;
+  if (a < ldexp(1.0, -6)) {                       /* subnormal range: units of 2^-9 */
+    double u = a * 512.0;
+    double r = floor(u);
+    double f = u - r;
+    if (f > 0.5 || (f == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    return sgn | (uint8_t)r;                      /* r == 8 is the smallest normal, code 0x08 */
+  }
+  int e;
+  double fr = frexp(a, &e);                       /* a = fr 2^e, fr in [0.5, 1) */
+  int E = e - 1;                                   /* a = (2 fr) 2^E, 2 fr in [1, 2) */
+  double u = (2.0 * fr - 1.0) * 8.0;              /* mantissa in units of 1/8 */
+  double r = floor(u);
+  double f = u - r;
+  if (f > 0.5 || (f == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  if (r == 8.0) {
+    r = 0.0;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && r > 6.0)) return sgn | 0x7E;
+  return sgn | (uint8_t)(((E + 7) << 3) | (int)r);
+}
+
+/* Per-row quantization: s = max_i |x_i| / 448 and codes e4m3(x_i / s), both
+ * in fp32 arithmetic (the scale and the quotient rounded to fp32 as a device
+ * computes them); an all-zero row gets s = 1.  deq (optional) = decode * s. */
+void oracle_quantize_row(const double* x, int64_t n, uint8_t* codes, float* scale, double* deq) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = fabsf((float)x[i]);
+    if (a > amax) amax = a;
+  }
+  float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float q = (float)x[i] / s;
+    uint8_t c = oracle_e4m3_encode((double)q);
+    if (codes) codes[i] = c;
+    if (deq) deq[i] = oracle_e4m3_decode(c) * (double)s;
+  }
+  *scale = s;
+}
+
+/* rows x cols of a dtype-coded array (see load_val) */
+int oracle_quantize_rows(const void* src, int32_t dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                         float* scales, double* deq) {
+  double* x = (double*)malloc(sizeof(double) * (cols ? cols : 1));
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) x[c] = load_val(src, dtype, r * cols + c);
+    oracle_quantize_row(x, cols, codes ? codes + r * cols : NULL, scales + r,
+                        deq ? deq + r * cols : NULL);
+  }
+  free(x);
+  return 0;
+}
 
 /* ------------------------------------------------------------------ M0
  * [P1 "DeepSeek Engram", tokenizer compression] x'_t = P(x_t); positions
@@ -221,6 +296,10 @@ static void token_forward(const oracle_problem* p, int64_t b, int64_t t, tok_sta
   int32_t idx[64];
   oracle_hash_at(p, b, t, idx);
   gather_row(p, idx, st->e);
+  if (p->fp8_e) {  /* e_t in e4m3 with its own scale, as the FP8 projection reads it */
+    float s;
+    oracle_quantize_row(st->e, d_mem(p), NULL, &s, st->e);
+  }
   for (int c = 0; c < d; ++c) st->h[c] = load_val(p->h, p->act_dtype, (b * p->T + t) * d + c);
   project(p, p->w_k, st->e, st->k);
   project(p, p->w_v, st->e, st->v);
