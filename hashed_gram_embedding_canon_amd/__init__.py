@@ -112,6 +112,7 @@ class EngramError(RuntimeError):
 EXPORTS = ("engram_workspace_size", "engram_status_string", "engram_hash_indices", "engram_forward",
            "engram_backward_table_grad", "engram_backward", "engram_prefetch_plan",
            "engram_shard_requests", "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce",
+           "engram_quantize_fp8",
            "engram_profile_enable",
            "engram_profile_reset", "engram_profile_read")
 
@@ -141,6 +142,7 @@ def lib():
     L.engram_backward.argtypes = [C, P, _vp, _vp, i64, i64, S, G, PG, _vp, sz, _vp]
     L.engram_prefetch_plan.argtypes = [C, _vp, _vp, i64, i64, _vp, K, _vp]
     L.engram_shard_requests.argtypes = [C, i32, _vp, i64, _vp, _vp, _vp, _vp, sz, _vp]
+    L.engram_quantize_fp8.argtypes = [_vp, i32, i64, i32, _vp, _vp, _vp]
     L.engram_shard_serve.argtypes = [C, i32, _vp, _vp, i64, _vp, _vp]
     L.engram_shard_grads.argtypes = [C, i32, _vp, _vp, _vp, i64, _vp, _vp, _vp, _vp, sz, _vp]
     L.engram_shard_reduce.argtypes = [C, i32, _vp, _vp, _vp, _vp, i32, _vp]
@@ -152,7 +154,8 @@ def lib():
     L.engram_profile_read.restype = i32
     for name in ("engram_hash_indices", "engram_forward", "engram_backward_table_grad",
                  "engram_backward", "engram_prefetch_plan", "engram_shard_requests",
-                 "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce"):
+                 "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce",
+                 "engram_quantize_fp8"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -293,6 +296,11 @@ def _ws_bytes(workspace, ws_bytes):
     if ws_bytes is None:
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return ws_bytes
+
+
+def engram_quantize_fp8(src, dtype: int, rows: int, cols: int, codes, scales, *, stream=None):
+    _check(lib().engram_quantize_fp8(_ptr(src), dtype, rows, cols, _ptr(codes), _ptr(scales),
+                                     _stream(stream)), "engram_quantize_fp8")
 
 
 def engram_shard_requests(cfg: Config, G: int, idx, N: int, send_ids, send_counts, inverse, *,

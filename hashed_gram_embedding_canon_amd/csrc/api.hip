@@ -856,6 +856,17 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
   return ENGRAM_OK;
 }
 
+engram_status engram_quantize_fp8(const void* src, int32_t dtype, int64_t rows, int32_t cols,
+                                  uint8_t* codes, float* scales, void* stream) {
+  if (dtype != ENGRAM_BF16 && dtype != ENGRAM_F32) return ENGRAM_E_UNSUPPORTED;
+  if (rows < 0 || cols <= 0 || cols % 8 != 0) return ENGRAM_E_INVALID;
+  if (rows == 0) return ENGRAM_OK;
+  if (!src || !codes || !scales || !aligned16(src) || ((uintptr_t)codes & 7)) return ENGRAM_E_INVALID;
+  hipStream_t hs = (hipStream_t)stream;
+  Timed tm("quant_rows", hs);
+  return hip_status(launch_quant_rows((const uint8_t*)src, dtype, rows, cols, codes, scales, hs));
+}
+
 engram_status engram_shard_requests(const engram_config* cfg, int32_t G, const int32_t* idx,
                                     int64_t N, uint32_t* send_ids, int64_t* send_counts,
                                     int32_t* inverse, void* workspace, size_t ws_bytes,

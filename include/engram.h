@@ -309,6 +309,17 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
                                    void* side_stream);
 
 /*
+ * E4M3 quantization as the FP8 projection applies it ("DeepSeek AI II",
+ * section "DeepSeek Engram", multi-branch integration: the projections as one
+ * dense FP8 matmul): per row, s = max|x| / 448 (1 for an all-zero row) and
+ * the OCP E4M3 codes of x / s (fp32 division, round to nearest even).
+ *   src: device [rows][cols] dtype (ENGRAM_BF16 or ENGRAM_F32), cols % 8 == 0;
+ *   codes: device [rows][cols] out; scales: device [rows] fp32 out.
+ */
+engram_status engram_quantize_fp8(const void* src, int32_t dtype, int64_t rows, int32_t cols,
+                                  uint8_t* codes, float* scales, void* stream);
+
+/*
  * Table-sharded row exchange: the device steps of one GPU ("DeepSeek AI II",
  * system-efficiency part: tables too large for one GPU are sharded over GPUs,
  * and each step exchanges the requested rows, then their gradients, by

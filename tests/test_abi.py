@@ -26,12 +26,12 @@ def eg():
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "engram.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(engram_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(engram_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(eg):
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     L = ctypes.CDLL(eg.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
