@@ -22,6 +22,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 MFMA_F32_PEAK_TFLOPS = 157.3
 
 
@@ -46,6 +47,13 @@ def kernel_units(wl, N):
                              "bytes": N * J * 4 + proj_bytes},
         # v is read once for all branches; each branch writes its own Y
         "gate_conv": {"bound": "hbm", "bytes": (M + 1) * N * d * es + M * N * nkt * 12},
+        # FP8 projection: E4M3 e and W (one byte each) with their fp32 scales
+        "proj_gemm_fp8": {"bound": "mfma_fp8", "flops": 2 * N * dm * (M + 1) * d,
+                          "bytes": N * dm + N * 4 + (M + 1) * d * (dm + 4) + (M + 1) * N * d * es
+                          + M * N * nkt * 12},
+        "quant_w": {"bound": "hbm", "bytes": (M + 1) * d * (dm * es + dm + 4)},
+        # indices + bf16 rows in, E4M3 e and its scale out
+        "gather_quant": {"bound": "hbm", "bytes": N * J * 4 + N * dm * es + N * dm + N * 4},
     }
 
 
@@ -733,6 +741,8 @@ def main():
     ap.add_argument("--calibration-bytes", type=int, default=1 << 30)
     ap.add_argument("--branches", type=int, default=1,
                     help="M branches sharing the tables and W_V (own W_K, hidden state, gate, Y)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="the projection as one E4M3 matmul (ENGRAM_FLAG_FP8_PROJ); not the headline")
     ap.add_argument("--shard-gpus", type=int, default=8,
                     help="GPUs the tables are sharded over for --workload shard27b")
     ap.add_argument("--ring-batches", type=int, default=8,
@@ -779,7 +789,8 @@ def main():
         f"table params={wl.table_params / 1e9:.2f}B; generating inputs")
     t = time.perf_counter()
     inp = synth.Inputs(wl)
-    dp = H.DeviceProblem(inp, flags=eg.ENGRAM_FLAG_FUSED_GATHER if args.fused_gather else 0)
+    flags = (eg.ENGRAM_FLAG_FUSED_GATHER if args.fused_gather else 0) | (eg.ENGRAM_FLAG_FP8_PROJ if args.fp8 else 0)
+    dp = H.DeviceProblem(inp, flags=flags)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM after {time.perf_counter() - t:.1f} s")
     lead = (wl.B, wl.T) if wl.branches == 1 else (wl.branches, wl.B, wl.T)
@@ -828,8 +839,9 @@ def main():
     if dom is not None:
         u = units[dom]
         avg_s = prof[dom][1] / prof[dom][0] * 1e-3
-        if u["bound"] == "mfma":
-            peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        if u["bound"] in ("mfma", "mfma_fp8"):
+            peak = (MFMA_FP8_PEAK_TFLOPS if u["bound"] == "mfma_fp8" else
+                    MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS)
             ach = u["flops"] / avg_s / 1e12
             roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(ach / peak, 4),
@@ -839,7 +851,7 @@ def main():
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                     "traffic": int(traffic[dom]) if dom in traffic else None}
-    mem_names = [k for k in ("gather", "gate_conv") if k in prof]
+    mem_names = [k for k in ("gather", "gather_quant", "gate_conv") if k in prof]
     mem_ms = sum(prof[k][1] / prof[k][0] for k in mem_names)
     mem_bytes = sum(units[k]["bytes"] for k in mem_names)
     es = 2 if wl.dtype == "bf16" else 4
@@ -864,7 +876,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "dtype": ("fp8 e4m3 projection, bf16 elsewhere" if args.fp8 else
+                  "bf16" if wl.dtype == "bf16" else "f32"),
         "data": "synthetic",
         "config": {"workload": wl.name, "branches": wl.branches, "row_gather": "fused into projection" if args.fused_gather else "gathered into workspace", "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
                    "rows_per_table": list(wl.rows[:1]) + ["..."], "dim": wl.dim,

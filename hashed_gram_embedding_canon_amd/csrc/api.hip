@@ -30,6 +30,10 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // latency (fewer cycles per tile) but runs at a lower clock under the power
 // limit and measured slower.
 constexpr int32_t kFwdStageBytes = 128;
+#ifndef ENGRAM_FP8_STAGE_BYTES
+#define ENGRAM_FP8_STAGE_BYTES 64
+#endif
+constexpr int32_t kFp8StageBytes = ENGRAM_FP8_STAGE_BYTES;  // E4M3 projection: K bytes per stage
 #ifndef ENGRAM_GEMM_PERSISTENT
 #define ENGRAM_GEMM_PERSISTENT 1
 #endif
@@ -54,7 +58,11 @@ engram_status check_config(const engram_config* c, Shape* s) {
   if (c->dim < 1 || c->hidden < 1) return ENGRAM_E_INVALID;
   if (c->conv_kernel < 1 || c->conv_kernel > 8) return ENGRAM_E_UNSUPPORTED;
   if (!(c->rms_eps >= 0.f)) return ENGRAM_E_INVALID;
-  if (c->flags & ~(uint32_t)ENGRAM_FLAG_FUSED_GATHER) return ENGRAM_E_INVALID;
+  if (c->flags & ~(uint32_t)(ENGRAM_FLAG_FUSED_GATHER | ENGRAM_FLAG_FP8_PROJ)) return ENGRAM_E_INVALID;
+  // the FP8 projection quantizes bf16 rows; the fused row gather reads bf16 tables itself
+  if ((c->flags & ENGRAM_FLAG_FP8_PROJ) &&
+      (c->dtype != ENGRAM_BF16 || (c->flags & ENGRAM_FLAG_FUSED_GATHER)))
+    return ENGRAM_E_UNSUPPORTED;
   if (c->branches < 0 || c->branches > ENGRAM_MAX_BRANCHES) return ENGRAM_E_INVALID;
   const int es = (int)dtype_size(c->dtype);
   if ((c->dim * es) % 16 != 0) return ENGRAM_E_UNSUPPORTED;
@@ -143,6 +151,11 @@ struct FwdWs {
   uint8_t* e;
   uint8_t* v;
   float* partials;
+  // ENGRAM_FLAG_FP8_PROJ: E4M3 codes and scales of e and of W_KV
+  uint8_t* e8;
+  float* se;
+  uint8_t* w8;
+  float* sw;
 };
 
 // By default e is gathered into memory and the projection reads it as a dense
@@ -150,7 +163,7 @@ struct FwdWs {
 // directly (row gather fused into its B operand) unless the caller asks for e
 // or the shape is outside what the fused loads handle.
 bool fused_gather(const Shape& s, const engram_saved* sv) {
-  if (!(s.flags & ENGRAM_FLAG_FUSED_GATHER)) return false;
+  if (!(s.flags & ENGRAM_FLAG_FUSED_GATHER) || (s.flags & ENGRAM_FLAG_FP8_PROJ)) return false;
   if (sv && sv->e) return false;
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
@@ -173,12 +186,20 @@ size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out,
   };
   FwdWs w{};
   w.idx = (sv && sv->idx) ? sv->idx : (int32_t*)take((size_t)N * s.J * 4);
+  const bool fp8 = (s.flags & ENGRAM_FLAG_FP8_PROJ) != 0;
   if (sv && sv->e)
     w.e = (uint8_t*)sv->e;
-  else if (worst_case || !fused_gather(s, sv))
+  else if (!fp8 && (worst_case || !fused_gather(s, sv)))
     w.e = take((size_t)N * s.d_mem * s.es);
   else
     w.e = nullptr;
+  if (fp8) {  // E4M3 codes and scales of e (per token) and of W_KV (per row)
+    const int64_t F = (int64_t)(s.M + 1) * s.d;
+    w.e8 = take((size_t)N * s.d_mem);
+    w.se = (float*)take((size_t)N * 4);
+    w.w8 = take((size_t)F * s.d_mem);
+    w.sw = (float*)take((size_t)F * 4);
+  }
   w.v = (sv && sv->v) ? (uint8_t*)sv->v : take((size_t)N * s.d * s.es);
   w.partials = (float*)take((size_t)s.M * N * (s.d / kGemmBF) * 3 * 4);
   if (out) *out = w;
@@ -380,16 +401,29 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
       return ENGRAM_E_HIP;
     for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
   }
-  const bool fused = w.e == nullptr;
-  if (!fused) {
+  const bool fp8 = (s.flags & ENGRAM_FLAG_FP8_PROJ) != 0;
+  const bool fused = w.e == nullptr && !fp8;
+  if (w.e) {  // bf16 e: the projection's operand, or kept for the caller
     Timed tm("gather", hs);
     if (launch_gather(idx, w.e, N, g, hs) != hipSuccess) return ENGRAM_E_HIP;
+  }
+  if (fp8) {
+    const int64_t F = (int64_t)(s.M + 1) * s.d;
+    {
+      Timed tm("quant_w", hs);
+      if (launch_quant_rows((const uint8_t*)p->w_kv, s.dtype, F, s.d_mem, w.w8, w.sw, hs) != hipSuccess)
+        return ENGRAM_E_HIP;
+    }
+    Timed tm("gather_quant", hs);
+    if (launch_gather_quant(idx, N, g, s.d_mem, w.e8, w.se, hs) != hipSuccess) return ENGRAM_E_HIP;
   }
   {
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
-    ga.A = (const uint8_t*)p->w_kv;
-    ga.B = w.e;
+    ga.A = fp8 ? w.w8 : (const uint8_t*)p->w_kv;
+    ga.B = fp8 ? w.e8 : w.e;
+    ga.scale_a = w.sw;
+    ga.scale_b = w.se;
     if (fused) {
       ga.idx = idx;
       ga.J = s.J;
@@ -404,7 +438,9 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     // rows are still in the Infinity Cache (measured ~1 % faster)
     ga.reverse_m = 1;
     ga.persistent = ENGRAM_GEMM_PERSISTENT;
-    ga.stage_bytes = kFwdStageBytes;
+    // E4M3 fragments are twice as wide: 64-byte stages (one 64-element K
+    // step each) keep the fragments of the next step within the registers
+    ga.stage_bytes = fp8 ? kFp8StageBytes : kFwdStageBytes;
     ga.d = s.d;
     ga.branches = s.M;
     ga.io_dtype = s.dtype;
@@ -414,9 +450,9 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     ga.partials = w.partials;
     ga.k_out = saved ? (uint8_t*)saved->k : nullptr;
     ga.v_out = w.v;
-    Timed tm(fused ? "gather_proj_gemm" : "proj_gemm", hs);
-    if (launch_gemm(s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32, EPI_KV, ga, hs) != hipSuccess)
-      return ENGRAM_E_HIP;
+    Timed tm(fused ? "gather_proj_gemm" : (fp8 ? "proj_gemm_fp8" : "proj_gemm"), hs);
+    const GemmType gt = fp8 ? GEMM_FP8 : (s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32);
+    if (launch_gemm(gt, EPI_KV, ga, hs) != hipSuccess) return ENGRAM_E_HIP;
   }
   {
     GateConvArgs gc;

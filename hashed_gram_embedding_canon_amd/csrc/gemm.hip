@@ -98,7 +98,7 @@ template <int GT, int EPI, bool GATHER, int SB>
 __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   using S = Stage<SB>;
   constexpr int NS = S::kStages;
-  constexpr int ES = (GT == GEMM_F32) ? 4 : 2;
+  constexpr int ES = (GT == GEMM_F32) ? 4 : (GT == GEMM_FP8 ? 1 : 2);
   constexpr int FB = 4, TB = 4;  // 32-blocks per wave along f and tokens
   constexpr int kTS = S::kOperandBytes;
   // One LDS object per stage (A then B): the compiler tracks the direct-to-LDS
@@ -113,6 +113,8 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) int32_t sIdx[GATHER ? kBT * kGatherMaxJ : kRedFloats + kBF];
   int32_t* const sIdxOrRed = sIdx;
   __shared__ const uint8_t* sTab[GATHER ? kGatherMaxJ : 1];
+  // E4M3: the dequantization scales of the tile's 256 A rows (features)
+  __shared__ __attribute__((aligned(16))) float sScaleA[GT == GEMM_FP8 ? kBF : 1];
 
   // ---- workgroup id -> (token tile, feature tile), XCD-grouped.  Slot s of
   // XCD x (workgroups x, x+8, ...) walks the tiles of that XCD; a grid of
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // 64u + r (w: wave half, u: which 64 of it) lives in part u (two buffers,
   // row 64w + r) or part 2u + w (four buffers, row r), so the first two
   // token blocks of every wave (u = 0) sit in the first half of the parts.
-  constexpr bool kBf16Epi = EPI == EPI_KV && GT == GEMM_BF16;
+  constexpr bool kBf16Epi = EPI == EPI_KV && (GT == GEMM_BF16 || GT == GEMM_FP8);
   auto part_base = [&](int X) __attribute__((always_inline)) -> uint8_t* {
     return X == 0 ? st0 : (X == 1 ? st1 : (X == 2 ? st2 : st3));
   };
@@ -309,21 +311,33 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int lhalf = lane >> 5;
   const int swl = S::swz(l32);  // fragment rows are blk*32 + l32; the swizzle reads bits 0..4 only
 
-  auto frag_one = [&](const uint8_t* sa, const uint8_t* sb, int ss, int blk, u32x4& af, u32x4& bf)
-                      __attribute__((always_inline)) {
-    const int phys = ((ss * 2 + lhalf) ^ swl) * 16;
-    af = *reinterpret_cast<const u32x4*>(sa + ((wf * FB + blk) * 32 + l32) * SB + phys);
-    bf = *reinterpret_cast<const u32x4*>(sb + ((wt * TB + blk) * 32 + l32) * SB + phys);
+  // A fragment is 16 bytes of a row (32-byte K steps), or for E4M3 32 bytes
+  // (64-element K steps: pieces 4 ss + 2 lhalf and the next one).
+  using Frag = std::conditional_t<GT == GEMM_FP8, u32x8, u32x4>;
+  auto piece = [&](const uint8_t* row, int ss, int k) __attribute__((always_inline)) {
+    constexpr int PPS = GT == GEMM_FP8 ? 4 : 2;  // pieces per K step
+    constexpr int PPL = PPS / 2;                 // pieces per lane half
+    return *reinterpret_cast<const u32x4*>(row + (((ss * PPS + lhalf * PPL + k) ^ swl) * 16));
   };
-  auto frag = [&](const uint8_t* sa, const uint8_t* sb, int ss, u32x4* af, u32x4* bf)
+  auto read_frag = [&](const uint8_t* row, int ss) __attribute__((always_inline)) {
+    if constexpr (GT == GEMM_FP8) {
+      const u32x4 lo = piece(row, ss, 0), hi = piece(row, ss, 1);
+      return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return piece(row, ss, 0);
+    }
+  };
+  auto frag_one = [&](const uint8_t* sa, const uint8_t* sb, int ss, int blk, Frag& af, Frag& bf)
+                      __attribute__((always_inline)) {
+    af = read_frag(sa + ((wf * FB + blk) * 32 + l32) * SB, ss);
+    bf = read_frag(sb + ((wt * TB + blk) * 32 + l32) * SB, ss);
+  };
+  auto frag = [&](const uint8_t* sa, const uint8_t* sb, int ss, Frag* af, Frag* bf)
                   __attribute__((always_inline)) {
-    const int phys = ((ss * 2 + lhalf) ^ swl) * 16;
 #pragma unroll
-    for (int a = 0; a < FB; ++a)
-      af[a] = *reinterpret_cast<const u32x4*>(sa + ((wf * FB + a) * 32 + l32) * SB + phys);
+    for (int a = 0; a < FB; ++a) af[a] = read_frag(sa + ((wf * FB + a) * 32 + l32) * SB, ss);
 #pragma unroll
-    for (int b = 0; b < TB; ++b)
-      bf[b] = *reinterpret_cast<const u32x4*>(sb + ((wt * TB + b) * 32 + l32) * SB + phys);
+    for (int b = 0; b < TB; ++b) bf[b] = read_frag(sb + ((wt * TB + b) * 32 + l32) * SB, ss);
   };
   // kKSteps 16-element K steps per stage, each FB groups of TB MFMAs (one
   // feature block against the TB token blocks).  The fragments of step s+1
@@ -340,13 +354,13 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   auto compute = [&](const uint8_t* sa, const uint8_t* sb, int kl, uint32_t nla, auto kSlots)
                      __attribute__((always_inline)) {
     constexpr int SLOTS = decltype(kSlots)::value;
-    constexpr int KS = S::kKSteps;
+    constexpr int KS = GT == GEMM_FP8 ? SB / 64 : S::kKSteps;
     constexpr int NG = KS * FB;           // MFMA groups per stage
     constexpr int NI = 2 * NL;            // load slots per stage
     constexpr int MPER = GT == GEMM_F32 ? 4 : 1;  // MFMA instructions per fragment pair
     static_assert(FB == TB, "one A and one B fragment of the next step per group");
     static_assert(SLOTS < kSlotH || kHOverlap, "h parts only in the bf16 key/value epilogue");
-    u32x4 af[2][FB], bf[2][TB];
+    Frag af[2][FB], bf[2][TB];
     if constexpr (!kSpreadLoads && SLOTS == kSlotNext) issue(kl, nla);
     if constexpr (!kSpreadLoads && SLOTS >= kSlotH) {
 #pragma unroll
@@ -364,10 +378,13 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         for (int b = 0; b < TB; ++b) Mma<GT>::run(af[cur][a], bf[cur][b], acc[a][b]);
         if (ss + 1 < KS) {
           frag_one(sa, sb, ss + 1, a, af[nx][a], bf[nx][a]);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * MPER, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * MPER, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          // the group's LDS reads (2, or 4 for E4M3) between its TB MFMAs
+          constexpr int NR = GT == GEMM_FP8 ? 4 : 2;
+#pragma unroll
+          for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, TB * MPER / NR, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
         } else {
           __builtin_amdgcn_sched_group_barrier(0x008, TB * MPER, 0);
         }
@@ -463,7 +480,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
 
   // ---- epilogues.  acc[a][b][q*4+r] holds C^T[f][m] with
   //      f = f0 + (wf*FB + a)*32 + q*8 + lhalf*4 + r,  m = m0 + (wt*TB + b)*32 + l32
-  if constexpr (EPI == EPI_KV && GT == GEMM_BF16) {
+  if constexpr (kBf16Epi) {
     // bf16: the whole 256-token x 256-feature tile goes through LDS as bf16,
     // token rows of 512 bytes (64 rows per stage buffer), 16-byte pieces
     // XOR-swizzled by (token & 31).  h is brought in and v goes out as whole
@@ -493,6 +510,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         const int f = fk + tid;
         sg[tid] = (gqB ? gqB[f] : 1.f) * (gkB ? gkB[f] : 1.f);
       }
+      if constexpr (GT == GEMM_FP8) sScaleA[tid] = g.scale_a[f0 + tid];
       if (hov) {
         // parts of the first two token blocks landed (at most the last 16
         // h loads, the parts of blocks 2 and 3, still in flight), gamma written
@@ -514,6 +532,9 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
           const int t = (wt * TB + b) * 32 + l32;
           const int64_t m = m0 + t;
           const uint8_t* hrow = trow(t);
+          // E4M3: k = acc * scale_a[f] * scale_b[m]; the token's scale_b factors
+          // out of the sums and is applied once per token
+          const float sb = GT == GEMM_FP8 ? g.scale_b[m < g.M ? m : g.M - 1] : 1.f;
           u32x2 hr[FB * 4];
 #pragma unroll
           for (int j = 0; j < FB * 4; ++j) {
@@ -537,9 +558,13 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
                 hx *= *reinterpret_cast<const floatx4*>(sg + fl);
               }
               float kv[4];
+              floatx4 sa4 = floatx4{1.f, 1.f, 1.f, 1.f};
+              if constexpr (GT == GEMM_FP8)
+                sa4 = *reinterpret_cast<const floatx4*>(sScaleA + (wf * FB + a) * 32 + q * 8 + lhalf * 4);
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 kv[r] = acc_read(acc[a][b][q * 4 + r]);
+                if constexpr (GT == GEMM_FP8) kv[r] *= sa4[r];
                 skk += kv[r] * kv[r];
                 shk += hx[r] * kv[r];
               }
@@ -547,12 +572,16 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
                 if (m < g.M) {
                   const int f = fk + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
                   *reinterpret_cast<u32x2*>(koutB + (m * d + f) * 2) =
-                      u32x2{pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
+                      u32x2{pack_bf16x2(kv[0] * sb, kv[1] * sb), pack_bf16x2(kv[2] * sb, kv[3] * sb)};
                 }
               }
             }
           }
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (GT == GEMM_FP8) {
+            skk *= sb * sb;
+            shk *= sb;
+          }
           skk += __shfl_xor(skk, 32);
           shk += __shfl_xor(shk, 32);
           shh += __shfl_xor(shh, 32);
@@ -601,18 +630,35 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     } else {
       // value tile: accumulators -> bf16 rows in LDS -> whole rows to v
       // (8-byte stores straight from the accumulators measured 3 % slower)
+      if constexpr (GT == GEMM_FP8) {
+        sScaleA[tid] = g.scale_a[f0 + tid];
+        __syncthreads();
+      }
 #pragma unroll
       for (int b = 0; b < TB; ++b) {
         const int t = (wt * TB + b) * 32 + l32;
         uint8_t* row = trow(t);
+        float sb = 1.f;
+        if constexpr (GT == GEMM_FP8) {
+          const int64_t m = m0 + t;
+          sb = g.scale_b[m < g.M ? m : g.M - 1];
+        }
 #pragma unroll
         for (int a = 0; a < FB; ++a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int c16 = (wf * FB + a) * 4 + q;
+            float x[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = acc_read(acc[a][b][q * 4 + r]);
+            if constexpr (GT == GEMM_FP8) {
+              const floatx4 sa4 = *reinterpret_cast<const floatx4*>(sScaleA + (wf * FB + a) * 32 + q * 8 + lhalf * 4);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) x[r] *= sa4[r] * sb;
+            }
             u32x2 u;
-            u[0] = pack_bf16x2(acc_read(acc[a][b][q * 4]), acc_read(acc[a][b][q * 4 + 1]));
-            u[1] = pack_bf16x2(acc_read(acc[a][b][q * 4 + 2]), acc_read(acc[a][b][q * 4 + 3]));
+            u[0] = pack_bf16x2(x[0], x[1]);
+            u[1] = pack_bf16x2(x[2], x[3]);
             *reinterpret_cast<u32x2*>(row + ((c16 ^ (t & 31)) << 4) + lhalf * 8) = u;
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -796,7 +842,8 @@ static hipError_t launch_one(const GemmArgs& g0, hipStream_t s) {
 }
 
 bool gemm_supported(GemmType type, const GemmArgs& g, bool gather) {
-  const int es = type == GEMM_F32 ? 4 : 2;
+  const int es = type == GEMM_F32 ? 4 : (type == GEMM_FP8 ? 1 : 2);
+  if (type == GEMM_FP8 && (gather || !g.scale_a || !g.scale_b)) return false;
   if (g.F % kBF != 0 || g.group_m < 1) return false;
   if (g.stage_bytes != 64 && g.stage_bytes != 128) return false;
   if (((int64_t)g.K * es) % 256 != 0) return false;  // whole ring turns for either stage shape
@@ -821,6 +868,7 @@ hipError_t launch_gemm(GemmType type, GemmEpilogue epi, const GemmArgs& g, hipSt
     if (type == GEMM_F32)
       return gather ? launch_one<GEMM_F32, EPI_KV, true>(g, s)
                     : launch_one<GEMM_F32, EPI_KV, false>(g, s);
+    if (type == GEMM_FP8 && !gather) return launch_one<GEMM_FP8, EPI_KV, false>(g, s);
   } else if (!gather) {
     if (type == GEMM_F16) return launch_one<GEMM_F16, EPI_STORE_F32, false>(g, s);
     if (type == GEMM_F32) return launch_one<GEMM_F32, EPI_STORE_F32, false>(g, s);

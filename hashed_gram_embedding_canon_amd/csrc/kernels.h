@@ -21,7 +21,8 @@ hipError_t launch_gather(const int32_t* idx, uint8_t* e, int64_t N, const Gather
 
 // ---------------------------------------------------------------- GEMM
 // C^T[f][m] = sum_k A[f][k] * B[m][k]; A: [F][K] (weights), B: [M][K] (tokens).
-enum GemmType { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2 };
+// GEMM_FP8: E4M3 operands with per-row scales (scale_a per A row, scale_b per B row)
+enum GemmType { GEMM_BF16 = 0, GEMM_F16 = 1, GEMM_F32 = 2, GEMM_FP8 = 3 };
 enum GemmEpilogue {
   EPI_KV = 0,   // forward: f < d -> gate partial sums (and optional k), f >= d -> v
   EPI_STORE_F32 = 1  // plain fp32 store of C[m][f] (backward de)
@@ -52,6 +53,9 @@ struct GemmArgs {
   const int32_t* idx;  // [M][J] or null (then B is read as a dense matrix)
   const uint8_t* tables[ENGRAM_MAX_TABLES];
   int32_t J, D;
+  // GEMM_FP8: C^T[f][m] = scale_a[f] scale_b[m] sum_k A[f][k] B[m][k] over the codes
+  const float* scale_a;  // [F]
+  const float* scale_b;  // [M]
 };
 // Feature-tile width of the GEMM (the k/v boundary and partials use it).
 constexpr int kGemmBF = 256;

@@ -25,6 +25,17 @@ struct Mma<GEMM_F16> {
   }
 };
 
+// E4M3 x E4M3 (format codes 0 and 0, no block scales): lanes 0-31 hold
+// k = 0..31 of a 64-element K slice, lanes 32-63 hold k = 32..63.
+template <>
+struct Mma<GEMM_FP8> {
+  __device__ static inline void run(const u32x8& a, const u32x8& b, floatx16& c) {
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
+                                                         __builtin_bit_cast(i32x8, b), c, 0, 0, 0, 0,
+                                                         0, 0);
+  }
+};
+
 // fp32: lanes 0-31 hold k = 0..3 of the 32-byte K slice, lanes 32-63 hold
 // k = 4..7; step i multiplies the pair (i, 4+i), so four steps cover all 8.
 template <>

@@ -75,7 +75,14 @@ enum {
    * gathering e into the workspace first (saves e's write and re-read, but the
    * row-indexed loads cost the projection more than the gather costs).  Ignored
    * when saved->e is requested or the shape is outside the fused loads. */
-  ENGRAM_FLAG_FUSED_GATHER = 1u
+  ENGRAM_FLAG_FUSED_GATHER = 1u,
+  /* The projections as one dense FP8 matmul ("DeepSeek AI II", section
+   * "DeepSeek Engram", multi-branch integration): each row of W_KV and each
+   * token's e_t are quantized to E4M3 with their own scale (as
+   * engram_quantize_fp8), and the E4M3 matrix cores accumulate in fp32.  bf16
+   * only; not with ENGRAM_FLAG_FUSED_GATHER.  The backward is unchanged (it
+   * takes the saved k, v of this forward and the bf16 weights). */
+  ENGRAM_FLAG_FP8_PROJ = 2u
 };
 
 /* Shapes and addressing constants.  Host struct, read during the call only. */

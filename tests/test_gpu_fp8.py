@@ -43,3 +43,65 @@ def test_quantize_matches_oracle(torch, oracle_lib):
         assert np.array_equal(scales, rs)
         mism = np.argwhere(codes != rc)
         assert mism.size == 0, (mism[:5], codes[tuple(mism[0])], rc[tuple(mism[0])])
+
+
+def _fp8_problem(inp, branch=0, tokens=None):
+    import oracle
+    over = {"fp8": True}
+    if branch:
+        over["w_k"] = oracle.widen(inp.w_k_branch(branch))
+        over["h"] = inp.hidden_branch(branch)
+    if tokens is not None:
+        over["tokens"] = tokens
+    return oracle.Problem.from_inputs(inp, **over)
+
+
+@pytest.mark.parametrize("B,T,M", [(2, 300, 1), (3, 77, 1), (1, 256, 2)])
+def test_fp8_forward_matches_oracle(torch, oracle_lib, B, T, M):
+    """Y, the saved k and the gates of the FP8 projection against the oracle
+    in its FP8 mode (the same E4M3 codes and scales), to the bf16 bars."""
+    import dataclasses
+    import hashed_gram_embedding_canon_amd as eg
+    wl = dataclasses.replace(synth.get_workload("tiny"), dtype="bf16", branches=M).with_shape(B, T)
+    print(f"[fp8 forward] B={B} T={T} M={M}", flush=True)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp, flags=eg.ENGRAM_FLAG_FP8_PROJ)
+    bufs = dp.alloc_saved(("idx", "stats", "k"))
+    y = dp.forward(bufs)
+    torch.cuda.synchronize()
+    for m in range(M):
+        p = _fp8_problem(inp, branch=m)
+        ref = p.forward(want=("y", "k", "alpha"))
+        ym = y if M == 1 else y[m]
+        km = bufs["k"] if M == 1 else bufs["k"][m]
+        sm = bufs["stats"] if M == 1 else bufs["stats"][m]
+        ey = H.rel_max_err(H.to_host_f64(ym).reshape(ref["y"].shape), ref["y"])
+        ek = H.rel_max_err(H.to_host_f64(km).reshape(ref["k"].shape), ref["k"])
+        ea = np.abs(sm[:, 0].cpu().numpy().astype(np.float64) - ref["alpha"]).max()
+        print(f"  branch {m}: y {ey:.2e} k {ek:.2e} alpha {ea:.2e}", flush=True)
+        assert ey <= 1e-2 and ek <= 1e-2 and ea <= 1e-3, (ey, ek, ea)
+
+
+def test_fp8_small_sampled(torch, oracle_lib):
+    import hashed_gram_embedding_canon_amd as eg
+    wl = synth.get_workload("small").with_shape(8, 4096)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp, flags=eg.ENGRAM_FLAG_FP8_PROJ)
+    y = dp.forward()
+    torch.cuda.synchronize()
+    pos = H.sample_positions(wl.B, wl.T, 96)
+    ref = _fp8_problem(inp).forward(pos, want=("y",))["y"]
+    got = H.to_host_f64(y).reshape(-1, wl.hidden)[pos]
+    err = H.rel_max_err(got, ref)
+    print(f"  small fp8: {err:.2e}", flush=True)
+    assert err <= 1e-2, err
+
+
+def test_fp8_rejects_fused_gather(torch):
+    import hashed_gram_embedding_canon_amd as eg
+    wl = synth.get_workload("tiny").with_shape(1, 64)
+    import dataclasses
+    wl = dataclasses.replace(wl, dtype="bf16")
+    dp = H.DeviceProblem(synth.Inputs(wl), flags=eg.ENGRAM_FLAG_FP8_PROJ | eg.ENGRAM_FLAG_FUSED_GATHER)
+    with pytest.raises(eg.EngramError, match="status 2"):
+        dp.forward()
