@@ -116,23 +116,29 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // E4M3: the dequantization scales of the tile's 256 A rows (features)
   __shared__ __attribute__((aligned(16))) float sScaleA[GT == GEMM_FP8 ? kBF : 1];
 
-  // ---- workgroup id -> (token tile, feature tile), XCD-grouped.  Slot s of
-  // XCD x (workgroups x, x+8, ...) walks the tiles of that XCD; a grid of
-  // fewer workgroups than slots makes each workgroup loop over slots
-  // s, s + gridDim/8, ... (persistent: no per-tile dispatch gap).
+  // ---- workgroup id -> (token tile, feature tile), XCD-grouped.  XCD list x
+  // holds the token tiles x, x+8, ... in groups of group_m; its slots run
+  // over a group's f-tiles, each f-tile over the group's token tiles, so the
+  // f-tiles of a group share rows and weight slabs in one XCD's L2.  A grid
+  // of fewer workgroups than slots makes each workgroup of list x
+  // (workgroups x, x+8, ...) loop over slots s, s + gridDim/8, ...
+  // (persistent: no per-tile dispatch gap).
   const int xcd = blockIdx.x & 7;
   const int slot_step = gridDim.x >> 3;
-  for (int slot = blockIdx.x >> 3; slot < g.slots_per_xcd; slot += slot_step) {
   const int tiles_f = g.F / kBF;
+  const int64_t tiles_m = (g.M + kBT - 1) / kBT;
+  const int tx = xcd < tiles_m ? (int)((tiles_m - 1 - xcd) / 8 + 1) : 0;  // token tiles of list x
+  const int nslots = tx * tiles_f;
+  for (int slot = blockIdx.x >> 3; slot < nslots; slot += slot_step) {
   const int gm = g.group_m;
   const int per_group = gm * tiles_f;
   const int grp = slot / per_group;
   const int in_g = slot - grp * per_group;
-  const int tf = in_g / gm;
-  const int tm_local = in_g - tf * gm;
-  const int64_t tm_fwd = (int64_t)(grp * gm + tm_local) * 8 + xcd;
-  const int64_t tiles_m = (g.M + kBT - 1) / kBT;
-  if (tm_fwd >= tiles_m) continue;  // uniform over the workgroup
+  const int full = tx / gm;                          // groups of group_m token tiles
+  const int gsz = grp < full ? gm : tx - full * gm;  // token tiles in this group
+  const int tf = in_g / gsz;
+  const int tm_local = in_g - tf * gsz;
+  const int64_t tm_fwd = (int64_t)(grp * gm + tm_local) * 8 + xcd;  // < tiles_m
   // token tiles walked last to first when asked (the newest rows of B first)
   const int64_t tm = g.reverse_m ? tiles_m - 1 - tm_fwd : tm_fwd;
   const int f0 = tf * kBF;
@@ -819,11 +825,8 @@ static hipError_t launch_one(const GemmArgs& g0, hipStream_t s) {
   GemmArgs g = g0;
   const int64_t tiles_m = (g.M + kBT - 1) / kBT;
   const int tiles_f = g.F / kBF;
-  const int64_t tiles_m_x = (tiles_m + 7) / 8;
-  const int64_t groups = (tiles_m_x + g.group_m - 1) / g.group_m;
-  const int64_t slots = groups * g.group_m * tiles_f;  // per XCD
-  if (slots >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  g.slots_per_xcd = (int32_t)slots;
+  const int64_t slots = (tiles_m + 7) / 8 * tiles_f;  // of the longest XCD list
+  if (slots >= (int64_t(1) << 30)) return hipErrorInvalidValue;  // slot + step stays in int
   // persistent: one workgroup per CU (the LDS use allows no second one), 8 XCDs
   int64_t per_xcd = slots;
   if (g.persistent) {

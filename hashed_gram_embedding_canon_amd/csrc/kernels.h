@@ -35,7 +35,6 @@ struct GemmArgs {
   int32_t group_m;     // token tiles walked per f-tile inside one XCD group
   int32_t reverse_m;   // nonzero: token tiles in descending order
   int32_t persistent;  // nonzero: one workgroup per CU loops over its XCD's tiles
-  int32_t slots_per_xcd;  // set by the launcher
   int32_t stage_bytes; // bytes of K per LDS stage: 64 (4-deep ring) or 128 (2-deep)
   // EPI_KV
   int32_t d;           // hidden width: f < branches*d are the branch keys, the rest v
