@@ -481,6 +481,10 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   if (hov) {
     ENGRAM_BARRIER();
   } else {
+    // A value tile's last stages issued placeholder h loads into the rows its
+    // epilogue writes next; the compiler cannot see those asm loads, so
+    // __syncthreads() alone would not wait for them.
+    ENGRAM_WAIT_VM(0);
     __syncthreads();
   }
 

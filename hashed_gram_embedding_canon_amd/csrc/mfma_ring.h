@@ -83,7 +83,7 @@ __device__ inline void load_lds16(const void* src, uint32_t m0v) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(src), "s"(m0v)
-               : "memory");
+               : "memory", "m0");
 }
 __device__ inline void load_lds16_s(uint32_t voff, const void* sbase, uint32_t m0v) {
   m0v = __builtin_amdgcn_readfirstlane(m0v);
@@ -91,7 +91,7 @@ __device__ inline void load_lds16_s(uint32_t voff, const void* sbase, uint32_t m
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(m0v)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Workgroup barrier without a memory fence: LDS written by this wave's

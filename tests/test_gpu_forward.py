@@ -177,6 +177,43 @@ def test_engram27b_forward(torch, oracle_lib, c27):
     assert a_err <= 1e-2
 
 
+def _forward_on_streams(torch, dp, y_like, chunks=8, streams=3):
+    """Forwards of `chunks` batch slices issued round-robin on `streams` torch
+    streams at once (each stream with its own workspace) -> Y."""
+    import hashed_gram_embedding_canon_amd as eg
+    bc = dp.B // chunks
+    sts = [torch.cuda.Stream() for _ in range(streams)]
+    ws = [torch.empty(eg.engram_workspace_size(dp.cfg, bc, dp.T, eg.ENGRAM_OP_FORWARD), dtype=torch.uint8,
+                      device="cuda")
+          for _ in range(streams)]
+    y = torch.full_like(y_like, float("nan"))
+    ev = torch.cuda.Event()
+    ev.record()
+    for st in sts:
+        st.wait_event(ev)
+    for c in range(chunks):
+        sl = slice(c * bc, (c + 1) * bc)
+        eg.engram_forward(dp.cfg, dp.params, dp.tokens[sl], dp.hidden[sl], y[sl], B=bc, T=dp.T,
+                          workspace=ws[c % streams], stream=sts[c % streams])
+    torch.cuda.synchronize()
+    return y
+
+
+def test_engram27b_concurrent_streams(torch, c27):
+    """Slices of the batch run on three streams at once give Y bit-identical to
+    one forward over the whole batch.  Kernels of other streams slow the
+    placeholder h loads that the projection's value tiles issue in their last
+    K stage; those loads land in LDS rows the value epilogue then writes, so
+    the epilogue waits for them (without that wait, late loads overwrote
+    pieces of v under this load)."""
+    inp, dp, bufs, y_ref = c27
+    for rep in range(4):
+        y = _forward_on_streams(torch, dp, y_ref)
+        bad = int((y != y_ref).reshape(dp.N, -1).any(dim=1).sum())
+        print(f"  rep {rep}: tokens differing {bad}", flush=True)
+        assert bad == 0
+
+
 @pytest.fixture(scope="module")
 def c40(torch):
     wl = synth.get_workload("engram40b")

@@ -105,3 +105,19 @@ def test_fp8_rejects_fused_gather(torch):
     dp = H.DeviceProblem(synth.Inputs(wl), flags=eg.ENGRAM_FLAG_FP8_PROJ | eg.ENGRAM_FLAG_FUSED_GATHER)
     with pytest.raises(eg.EngramError, match="status 2"):
         dp.forward()
+
+
+def test_fp8_concurrent_streams(torch):
+    """The FP8 projection (four-deep stage ring) with batch slices on three
+    streams at once: Y bit-identical to one forward over the batch."""
+    import hashed_gram_embedding_canon_amd as eg
+    from tests.test_gpu_forward import _forward_on_streams
+    wl = synth.get_workload("small").with_shape(8, 4096)
+    dp = H.DeviceProblem(synth.Inputs(wl), flags=eg.ENGRAM_FLAG_FP8_PROJ)
+    y_ref = dp.forward()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y = _forward_on_streams(torch, dp, y_ref, chunks=8, streams=3)
+        bad = int((y != y_ref).reshape(dp.N, -1).any(dim=1).sum())
+        print(f"  rep {rep}: tokens differing {bad}", flush=True)
+        assert bad == 0
