@@ -128,3 +128,58 @@ def test_engram27b_table_grads_sampled(torch, oracle_lib):
     torch.cuda.synchronize()
     got_a = np.stack([dense[int(j)][int(r)].cpu().numpy().astype(np.float64) for j, r in zip(rj, rr)])
     assert H.rel_l2(got_a, got) <= 1e-3
+
+
+def test_training_backward_concurrent_streams(torch):
+    """Training backward (sparse table gradients and every parameter gradient)
+    of single-sequence slices issued on three streams at once equals the same
+    calls made one after another on one stream, bit for bit."""
+    import hashed_gram_embedding_canon_amd as eg
+    wl = synth.get_workload("small").with_shape(6, 4096)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp)
+    saved = dp.alloc_saved(("idx", "stats", "k", "v"))
+    dp.forward(saved)
+    dy = H.to_dev(inp.dy)
+    T, J, D, d = dp.T, wl.J, wl.dim, wl.hidden
+    n_ws = eg.engram_workspace_size(dp.cfg, 1, T, eg.ENGRAM_OP_BACKWARD_PARAMS)
+
+    def run(streams):
+        ws = [torch.empty(n_ws, dtype=torch.uint8, device="cuda") for _ in streams]
+        outs = []
+        ev = torch.cuda.Event()
+        ev.record()
+        for st in streams:
+            st.wait_event(ev)
+        for b in range(dp.B):
+            rows = slice(b * T, (b + 1) * T)
+            o = {"keys": torch.empty(T * J, dtype=torch.int64, device="cuda"),
+                 "rows": torch.empty(T * J, D, dtype=torch.float32, device="cuda"),
+                 "count": torch.zeros(1, dtype=torch.int64, device="cuda"),
+                 "w_kv": torch.empty(2 * d, wl.d_mem, dtype=torch.float32, device="cuda"),
+                 "conv_w": torch.empty(d, wl.taps, dtype=torch.float32, device="cuda"),
+                 "gamma_q": torch.empty(d, dtype=torch.float32, device="cuda"),
+                 "gamma_k": torch.empty(d, dtype=torch.float32, device="cuda"),
+                 "hidden": torch.empty(1, T, d, dtype=dp.tdtype, device="cuda")}
+            tg = eg.engram_table_grad()
+            tg.mode = eg.ENGRAM_GRAD_SORTED_SPARSE
+            tg.keys, tg.rows, tg.count = o["keys"].data_ptr(), o["rows"].data_ptr(), o["count"].data_ptr()
+            pg = eg.make_param_grad(**{k: o[k] for k in ("w_kv", "conv_w", "gamma_q", "gamma_k", "hidden")})
+            sv = eg.make_saved(**{k: t[rows] for k, t in saved.items()})
+            eg.engram_backward(dp.cfg, dp.params, dp.hidden[b:b + 1], dy[b:b + 1], B=1, T=T, saved=sv,
+                               table_out=tg, param_out=pg, workspace=ws[b % len(streams)],
+                               stream=streams[b % len(streams)])
+            outs.append(o)
+        torch.cuda.synchronize()
+        return outs
+
+    serial = run([torch.cuda.current_stream()])
+    for rep in range(2):
+        conc = run([torch.cuda.Stream() for _ in range(3)])
+        for b, (x, y) in enumerate(zip(serial, conc)):
+            n = int(x["count"].item())
+            assert n == int(y["count"].item()), (rep, b)
+            assert torch.equal(x["keys"][:n], y["keys"][:n]) and torch.equal(x["rows"][:n], y["rows"][:n]), (rep, b)
+            for k in ("w_kv", "conv_w", "gamma_q", "gamma_k", "hidden"):
+                assert torch.equal(x[k], y[k]), (rep, b, k)
+        print(f"  rep {rep}: {dp.B} slices identical", flush=True)
