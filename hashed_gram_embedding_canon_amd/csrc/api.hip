@@ -708,6 +708,10 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
   if (!reuse)
     for (int64_t n = 0; n < N; ++n)
       if (tokens_host[n] < 0 || tokens_host[n] >= cfg->vocab) return ENGRAM_E_INVALID;
+  // the previous copies of this plan read inverse_host and staging_host until
+  // its event fires: wait before rewriting them
+  if (plan->ready_event && hipEventSynchronize((hipEvent_t)plan->ready_event) != hipSuccess)
+    return ENGRAM_E_HIP;
   const HashArgs ha = make_hash_args(cfg, s);
   const int nthr = (int)std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
   auto parallel = [&](int64_t count, auto&& fn) {

@@ -304,7 +304,10 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* par
  * and queued in chunks, so the copy of one chunk runs while the next is
  * gathered.  With plan->ring_rows > 0 only the rows missing from the ring
  * are gathered and copied (see engram_compact).  Returns when the host work
- * is done; the copies run asynchronously.  With ENGRAM_PLAN_REUSE in plan->flags the plan fields are
+ * is done; the copies run asynchronously and read inverse_host and
+ * staging_host until ready_event fires, so a call on the same plan first
+ * waits for that event (with no event, the caller must not reuse those
+ * buffers before the copies end).  With ENGRAM_PLAN_REUSE in plan->flags the plan fields are
  * taken as given (a plan-only call made them) and only gather and copy run.
  *   canon_map_host: host [vocab]; tokens_host: host [B][T];
  *   host_tables: NULL (plan only) or host [J] pointers to [M_j][D] dtype
