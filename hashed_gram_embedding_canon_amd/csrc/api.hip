@@ -68,6 +68,7 @@ engram_status check_config(const engram_config* c, Shape* s) {
   if ((c->dim * es) % 16 != 0) return ENGRAM_E_UNSUPPORTED;
   const int d_mem = J * c->dim;
   if (d_mem % kGemmBF != 0) return ENGRAM_E_UNSUPPORTED;
+  if ((c->flags & ENGRAM_FLAG_FP8_PROJ) && d_mem > kQuantMaxDmem) return ENGRAM_E_UNSUPPORTED;
   if (c->hidden % kGemmBF != 0) return ENGRAM_E_UNSUPPORTED;
   if (c->hidden / (c->dtype == ENGRAM_BF16 ? 8 : 4) > 1024) return ENGRAM_E_UNSUPPORTED;
   int64_t max_rows = 1;

@@ -112,7 +112,9 @@ hipError_t launch_bwd_param_sums(const float* pacc, float* tmp, int64_t nblk, in
 // codes [rows][cols] and scales [rows] of a bf16 / fp32 matrix (cols % 8 == 0)
 hipError_t launch_quant_rows(const uint8_t* src, int32_t io_dtype, int64_t rows, int32_t cols,
                              uint8_t* codes, float* scales, hipStream_t s);
-// e_n = concat_j base[j][idx[n][j]] (bf16 rows) quantized per token: e8 [N][d_mem], se [N]
+// e_n = concat_j base[j][idx[n][j]] (bf16 rows) quantized per token: e8 [N][d_mem], se [N];
+// one wavefront holds a token's row pieces, so d_mem <= kQuantMaxDmem
+constexpr int kQuantMaxDmem = 4096;
 hipError_t launch_gather_quant(const int32_t* idx, int64_t N, const GatherArgs& g, int32_t d_mem,
                                uint8_t* e8, float* se, hipStream_t s);
 

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint8_t* __restri
 // Row gather with quantization: one wavefront per token n gathers its J rows
 // (bf16, 16-byte pieces), takes the scale of the whole e_n and writes e_n's
 // codes [d_mem] and se[n].  A lane holds pieces lane, lane + 64, ...
-constexpr int kQuantMaxPieces = 8;  // per lane: d_mem <= 4096
+constexpr int kQuantMaxPieces = kQuantMaxDmem / (64 * 8);  // bf16 16-byte pieces per lane
 __global__ __launch_bounds__(256) void gather_quant_kernel(const int32_t* __restrict__ idx, int64_t N,
                                                            GatherArgs g, int32_t d_mem,
                                                            uint8_t* __restrict__ e8,

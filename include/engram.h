@@ -80,7 +80,8 @@ enum {
    * "DeepSeek Engram", multi-branch integration): each row of W_KV and each
    * token's e_t are quantized to E4M3 with their own scale (as
    * engram_quantize_fp8), and the E4M3 matrix cores accumulate in fp32.  bf16
-   * only; not with ENGRAM_FLAG_FUSED_GATHER.  The backward is unchanged (it
+   * only, d_mem <= 4096; not with ENGRAM_FLAG_FUSED_GATHER (else
+   * ENGRAM_E_UNSUPPORTED).  The backward is unchanged (it
    * takes the saved k, v of this forward and the bf16 weights). */
   ENGRAM_FLAG_FP8_PROJ = 2u
 };

@@ -97,6 +97,15 @@ def test_forward_validation(eg):
     assert _fwd(eg, cfg, T=0) == eg.ENGRAM_OK
     rows = np.array([10007] * 7 + [0], np.int64)
     assert _fwd(eg, _cfg(eg, table_rows=rows)) == eg.ENGRAM_E_INVALID
+    # the FP8 projection: bf16 only, d_mem <= 4096, not with the fused gather
+    fp8 = eg.ENGRAM_FLAG_FP8_PROJ
+    assert _fwd(eg, _cfg(eg, flags=fp8)) == eg.ENGRAM_E_UNSUPPORTED  # fp32
+    assert _fwd(eg, _cfg(eg, flags=fp8 | eg.ENGRAM_FLAG_FUSED_GATHER,
+                         dtype=eg.ENGRAM_BF16)) == eg.ENGRAM_E_UNSUPPORTED
+    wide = dict(dtype=eg.ENGRAM_BF16, flags=fp8, heads=8, dim=512,
+                table_rows=np.full(16, 10007, np.int64), multipliers=np.ones((16, 3), np.uint64))
+    assert _fwd(eg, _cfg(eg, **wide)) == eg.ENGRAM_E_UNSUPPORTED  # d_mem 8192
+    assert eg.engram_workspace_size(_cfg(eg, **dict(wide, dim=256)), 2, 8, 0) > 0  # d_mem 4096
 
 
 def test_backward_and_hash_validation(eg):
