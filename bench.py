@@ -89,6 +89,8 @@ def kernel_key(name: str) -> str:
         gt, epi, gather = targs[0], targs[1], targs[2]
         if epi == "1":
             return "de_gemm"
+        if gt == "3":
+            return "proj_gemm_fp8"
         return "gather_proj_gemm" if gather == "true" else "proj_gemm"
     if "gemm_tn_kernel" in base or "tn_reduce_kernel" in base:
         return "dw_gemm"
@@ -97,9 +99,20 @@ def kernel_key(name: str) -> str:
     if "bwd_gate_conv_kernel<" in base:
         targs = base.split("<", 1)[1].rstrip(">").replace(" ", "").split(",")
         return "bwd_gate_conv_params" if targs[2] == "true" else "bwd_gate_conv"
-    for key in ("gate_conv", "gather", "hash", "transpose_w", "atomic_scatter"):
-        if f"{key}_kernel" in base:
+    if "quant_rows_kernel" in base:
+        return "quant_w"
+    for key in ("gather_quant", "gate_conv", "gather", "hash", "transpose_w", "atomic_scatter"):
+        if f"engram::{key}_kernel" in base:
             return key
+    # the per-GPU steps of the sharded exchange
+    if "owner_bounds_kernel" in base or "shard_pack_kernel" in base or "remap_kernel" in base:
+        return "shard_pack"
+    if "serve_kernel" in base:
+        return "shard_serve"
+    if "grad_add_kernel" in base:
+        return "shard_reduce"
+    if "seg_inverse_kernel" in base:
+        return "shard_dedup"
     for key in ("sort_", "seg_"):
         if "engram::" + key in base:
             return "sorted_scatter"
@@ -124,7 +137,9 @@ def csrc_digest() -> str:
 
 # bench names made of several dispatches per call: the kernel that runs once per call
 GROUP_LEADER = {"sorted_scatter": "sort_init_kernel", "dw_gemm": "gemm_tn_kernel",
-                "bwd_param_sums": "param_finish_kernel"}
+                "bwd_param_sums": "param_finish_kernel", "shard_pack": "owner_bounds_kernel"}
+# names whose leader is the last dispatch of a call (the others' is the first)
+GROUP_LEADER_LAST = {"bwd_param_sums"}
 
 
 def _pmc_per_kernel(csv_dir: str, counter: str) -> dict:
@@ -163,7 +178,7 @@ def summarize_trace(trace_dir: str) -> str:
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     calls: dict = {}
     names: dict = {}
-    prev_key, cur = None, None
+    prev_key, prev_name, cur = None, "", None
     for r in rows:
         k = kernel_key(r["Kernel_Name"])
         if not k or k == "copy":
@@ -171,12 +186,14 @@ def summarize_trace(trace_dir: str) -> str:
             continue
         ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         names.setdefault(k, set()).add(r["Kernel_Name"].split("(")[0])
-        if k == prev_key and k in GROUP_LEADER:
-            cur[-1] += ns
+        lead = GROUP_LEADER.get(k, "")
+        new_call = (lead in prev_name) if k in GROUP_LEADER_LAST else (lead in r["Kernel_Name"])
+        if k == prev_key and lead and not new_call:
+            cur[-1] += ns  # a later dispatch of the same call
         else:
             cur = calls.setdefault(k, [])
             cur.append(ns)
-        prev_key = k
+        prev_key, prev_name = k, r["Kernel_Name"]
     lines = [f"{'kernel':<21} {'calls':>5} {'mean_us':>9} {'median_us':>10} {'min_us':>9} {'max_us':>9}  kernels"]
     for k, v in sorted(calls.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{k:<21} {len(v):>5} {statistics.mean(v) / 1e3:>9.2f} {statistics.median(v) / 1e3:>10.2f} "
@@ -829,7 +846,9 @@ def main():
         if "flops" in u:
             ent["TFLOPs"] = round(u["flops"] / (avg * 1e-3) / 1e12, 1)
         kernels[name] = ent
-    traffic = traffic_from_profile(wl.name)
+    # the counters were taken on the default configuration (one branch, bf16
+    # projection, rows gathered first): other configurations report none
+    traffic = traffic_from_profile(wl.name) if wl.branches == 1 and flags == 0 else {}
     for name, ent in kernels.items():
         if name in traffic:
             ent["counter_bytes"] = int(traffic[name])
