@@ -222,6 +222,30 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
     return "\n".join(out)
 
 
+def summarize_pmc(csv_dir: str) -> str:
+    """Mean per dispatch of every counter of a rocprofv3 --pmc run, for the
+    MFMA kernels (the weight-gradient GEMM without its chunk-sum kernel)."""
+    import csv
+    import glob
+    vals: dict = {}
+    for path in glob.glob(os.path.join(csv_dir, "*counter_collection.csv")):
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                k = kernel_key(r["Kernel_Name"])
+                if k not in ("proj_gemm", "proj_gemm_fp8", "gather_proj_gemm", "de_gemm", "dw_gemm"):
+                    continue
+                if k == "dw_gemm" and "gemm_tn_kernel" not in r["Kernel_Name"]:
+                    continue
+                vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    counters = sorted({c for v in vals.values() for c in v})
+    lines = [f"{'kernel':<16} {'dispatches':>10} " + " ".join(f"{c:>28}" for c in counters)]
+    for k, v in sorted(vals.items()):
+        n = max(len(x) for x in v.values())
+        lines.append(f"{k:<16} {n:>10} " + " ".join(
+            f"{(sum(v[c]) / len(v[c]) if c in v else float('nan')):>28.6g}" for c in counters))
+    return "\n".join(lines)
+
+
 def traffic_from_profile(workload: str) -> dict:
     """{kernel: HBM bytes per launch} from profiles/traffic_<workload>.txt when
     that file was taken from the current sources, else {}."""
@@ -751,6 +775,8 @@ def main():
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats csv run")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="print per-dispatch counter means of the MFMA kernels of a rocprofv3 --pmc csv run")
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="print HBM bytes per dispatch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
@@ -771,6 +797,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
         return
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, args.calibration_bytes))

@@ -30,10 +30,6 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // latency (fewer cycles per tile) but runs at a lower clock under the power
 // limit and measured slower.
 constexpr int32_t kFwdStageBytes = 128;
-#ifndef ENGRAM_FP8_STAGE_BYTES
-#define ENGRAM_FP8_STAGE_BYTES 64
-#endif
-constexpr int32_t kFp8StageBytes = ENGRAM_FP8_STAGE_BYTES;  // E4M3 projection: K bytes per stage
 #ifndef ENGRAM_GEMM_PERSISTENT
 #define ENGRAM_GEMM_PERSISTENT 1
 #endif
@@ -439,9 +435,10 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     // rows are still in the Infinity Cache (measured ~1 % faster)
     ga.reverse_m = 1;
     ga.persistent = ENGRAM_GEMM_PERSISTENT;
-    // E4M3 fragments are twice as wide: 64-byte stages (one 64-element K
-    // step each) keep the fragments of the next step within the registers
-    ga.stage_bytes = fp8 ? kFp8StageBytes : kFwdStageBytes;
+    // E4M3 uses the same 128-byte stages (two 64-element K steps each): the
+    // four-deep ring of 64-byte stages measured 1-2 % slower, with 8x the LDS
+    // bank conflicts of the two-piece fragment reads
+    ga.stage_bytes = kFwdStageBytes;
     ga.d = s.d;
     ga.branches = s.M;
     ga.io_dtype = s.dtype;
