@@ -126,3 +126,26 @@ def test_branch_backward(torch, oracle_lib, dtype, M, B, T):
             bar = 5e-3 if bf else 1e-5
         print(f"  {k}: {e:.2e}", flush=True)
         assert e <= bar, (k, e)
+
+
+def test_engram27b_four_branches_sampled(torch, oracle_lib):
+    """The 27B-scale forward with M = 4 branches, as the bench runs it: every
+    branch's Y and gate against the oracle at sampled positions."""
+    wl = dataclasses.replace(synth.get_workload("engram27b"), branches=4)
+    print("[engram27b, 4 branches] generating and uploading 5.7B table parameters", flush=True)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp)
+    bufs = dp.alloc_saved(("stats",))
+    y = dp.forward(bufs).reshape(4, -1, wl.hidden)
+    torch.cuda.synchronize()
+    pos = H.sample_positions(dp.B, dp.T, 64, seed=23)
+    ipos = torch.as_tensor(pos, device=y.device)
+    for m in range(4):
+        p = H.oracle_problem(inp, branch=m)
+        ref = p.forward(pos, want=("y", "alpha"))
+        err = H.rel_max_err(H.to_host_f64(y[m][ipos]), ref["y"])
+        a_err = float(np.abs(bufs["stats"][m][ipos, 0].cpu().numpy() - ref["alpha"]).max())
+        print(f"  branch {m}: max-abs-err/max|ref| = {err:.3e}, alpha err {a_err:.2e}", flush=True)
+        assert err <= TOL["bf16"] and a_err <= 1e-2, (m, err, a_err)
+    del dp, bufs, y
+    torch.cuda.empty_cache()

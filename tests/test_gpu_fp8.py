@@ -121,3 +121,23 @@ def test_fp8_concurrent_streams(torch):
         bad = int((y != y_ref).reshape(dp.N, -1).any(dim=1).sum())
         print(f"  rep {rep}: tokens differing {bad}", flush=True)
         assert bad == 0
+
+
+def test_fp8_engram27b_sampled(torch, oracle_lib):
+    """The FP8 projection at the 27B scale, as the bench's --fp8 run: Y against
+    the oracle's FP8 mode at sampled positions."""
+    import hashed_gram_embedding_canon_amd as eg
+    wl = synth.get_workload("engram27b")
+    print("[engram27b fp8] generating and uploading 5.7B table parameters", flush=True)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp, flags=eg.ENGRAM_FLAG_FP8_PROJ)
+    y = dp.forward()
+    torch.cuda.synchronize()
+    pos = H.sample_positions(wl.B, wl.T, 96, seed=31)
+    ref = _fp8_problem(inp).forward(pos, want=("y",))["y"]
+    got = H.to_host_f64(y).reshape(-1, wl.hidden)[pos]
+    err = H.rel_max_err(got, ref)
+    print(f"  engram27b fp8: {err:.2e}", flush=True)
+    assert err <= 1e-2, err
+    del dp, y
+    torch.cuda.empty_cache()
