@@ -30,7 +30,9 @@
  *
  * Conventions for every entry point:
  *   - Ownership: the caller allocates every device, pinned-host and workspace
- *     buffer; the library never allocates or frees memory.
+ *     buffer; the library never allocates or frees device or pinned memory
+ *     (only the host-side planner of engram_prefetch_plan uses ordinary host
+ *     memory for its scratch, and the optional timing calls create events).
  *   - Streams: work is queued on the caller's hipStream_t (passed as void*,
  *     NULL = the default stream) without host synchronisation.  Calls are
  *     reentrant and may run on several streams at once if their buffers do
