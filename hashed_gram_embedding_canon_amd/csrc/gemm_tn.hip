@@ -138,12 +138,13 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
     const uint32_t my = mx + kTnOperand;
     // last row of Y in this stage (KS-1 except in the stage holding row K-1)
     const int last = (int)(g.K - 1 - k0 < KS - 1 ? g.K - 1 - k0 : KS - 1);
+    const M0Keep keep;
 #pragma unroll
-    for (int q = 0; q < NL; ++q) load_lds16_s(voffX[q], bx, mx + q * 1024);
+    for (int q = 0; q < NL; ++q) load_lds16_s_kept(voffX[q], bx, mx + q * 1024);
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
       const int r = rowL[q] < last ? rowL[q] : last;
-      load_lds16_s((uint32_t)(r * ldyb + pieceL[q] * 16), by, my + q * 1024);
+      load_lds16_s_kept((uint32_t)(r * ldyb + pieceL[q] * 16), by, my + q * 1024);
     }
   };
 

@@ -74,25 +74,46 @@ __device__ inline const void* uniform_ptr(const void* p) {
 // that the compiler does not treat every later LDS read as aliasing the write
 // and wait for all loads in flight; the ring below waits with explicit vmcnt
 // counts.  The instructions have no destination register, so nothing the
-// compiler allocates can be overwritten while they are in flight.
+// compiler allocates can be overwritten while they are in flight.  M0 is a
+// register the compiler reserves and assumes unchanged across asm, so each
+// block restores it (the load reads M0 when it issues).
 //   load_lds16:   per-lane 64-bit address
 //   load_lds16_s: wave-uniform 64-bit base (SGPRs) + per-lane 32-bit offset,
 //                 so a stage's loads need no per-lane address arithmetic
 __device__ inline void load_lds16(const void* src, uint32_t m0v) {
   m0v = __builtin_amdgcn_readfirstlane(m0v);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "v"(src), "s"(m0v)
-               : "memory", "m0");
+               : "memory");
 }
 __device__ inline void load_lds16_s(uint32_t voff, const void* sbase, uint32_t m0v) {
+  m0v = __builtin_amdgcn_readfirstlane(m0v);
+  sbase = uniform_ptr(sbase);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(voff), "s"(sbase), "s"(m0v)
+               : "memory");
+}
+
+// The same load for a caller that keeps M0 for a group of loads: it saves M0
+// once (M0Keep) and restores it when the group ends (two scalar moves per
+// group instead of per load).
+__device__ inline void load_lds16_s_kept(uint32_t voff, const void* sbase, uint32_t m0v) {
   m0v = __builtin_amdgcn_readfirstlane(m0v);
   sbase = uniform_ptr(sbase);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(m0v)
-               : "memory", "m0");
+               : "memory");
 }
+struct M0Keep {
+  uint32_t saved;
+  __device__ M0Keep() { asm volatile("s_mov_b32 %0, m0" : "=s"(saved)); }
+  __device__ ~M0Keep() { asm volatile("s_mov_b32 m0, %0" : : "s"(saved) : "memory"); }
+};
 
 // Workgroup barrier without a memory fence: LDS written by this wave's
 // direct-to-LDS loads is complete once vmcnt says so (waited for explicitly
