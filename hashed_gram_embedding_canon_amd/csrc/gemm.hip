@@ -9,7 +9,7 @@
 // each lane of a 32x32 accumulator block owns one token and 16 of its
 // features.  That makes the gate's per-token reductions (sum k^2,
 // sum g_q g_k h k, sum h^2) plain in-register sums in the epilogue: the key
-// never goes to HBM, and h is read exactly once, here.
+// goes to HBM only when the caller saves it, and h is read exactly once, here.
 //
 // Row gather fused into the B operand: with GATHER, the 16-byte pieces of a
 // token row of B are read straight from the embedding tables through the
@@ -17,15 +17,17 @@
 // never written to or read back from HBM.
 //
 // Tiling: 256 features x 256 tokens per workgroup of 4 wavefronts, each
-// owning a 128 x 128 block (16 accumulators of 32x32).  K advances 64 bytes
-// per stage through a 4-stage LDS ring filled by direct-to-LDS 16-byte global
-// loads (no staging registers); rows are 64 bytes in LDS with the 16-byte
-// pieces XOR-swizzled by sw(r) = ((r >> 1) ^ (r >> 3)) & 3 so that the
-// ds_read_b128 of 32-row fragments hit distinct banks.  Matrix cores:
-// v_mfma_f32_32x32x16_bf16 / _f16; fp32 inputs use four
-// v_mfma_f32_32x32x2f32 per 16-byte fragment.  Workgroup ids reach the 8
-// XCDs round-robin; the id -> tile map keeps the f-tiles of a small group of
-// token tiles on one XCD so they share rows and weight slabs in its L2.
+// owning a 128 x 128 block (16 accumulators of 32x32).  K advances 128 bytes
+// per stage through two LDS buffers (or 64 bytes through four) filled by
+// direct-to-LDS 16-byte global loads (no staging registers); the 16-byte
+// pieces of a row are XOR-swizzled (Stage::swz) so that the ds_read_b128 of
+// 32-row fragments hit distinct banks.  Matrix cores:
+// v_mfma_f32_32x32x16_bf16 / _f16, v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// scales for E4M3; fp32 inputs use four v_mfma_f32_32x32x2f32 per 16-byte
+// fragment.  The grid is persistent (one workgroup per CU).  Workgroup ids
+// reach the 8 XCDs round-robin; the id -> tile map keeps the f-tiles of a
+// small group of token tiles on one XCD so they share rows and weight slabs
+// in its L2.
 #include <algorithm>
 #include <type_traits>
 
