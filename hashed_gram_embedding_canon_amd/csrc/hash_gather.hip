@@ -7,8 +7,8 @@
 // id and its canonical-map entry are read once per wave.
 //
 // Gather ("DeepSeek AI II", section "DeepSeek Engram": all retrieved
-// embeddings are concatenated into e_t): one block column per table, 16-byte
-// lanes walking each row, so a table row is read as whole contiguous
+// embeddings are concatenated into e_t): e is numbered in 16-byte pieces and
+// each lane copies pieces of it, so table rows are read as whole contiguous
 // 16-byte pieces and e is written in order.
 #include "kernels.h"
 

@@ -5,8 +5,9 @@
 // Deterministic path: per table, a stable LSD radix sort of the row ids
 // (8-bit digits, token ids as payload, so equal rows keep token order),
 // segment heads -> one segment per distinct (table, row), then a segmented
-// fp32 reduction in sorted order.  Zipf-heavy rows become long segments that
-// a single wavefront sums with several lane groups in a fixed order.
+// fp32 reduction in sorted order: a group of D/4 lanes sums each segment,
+// Zipf-heavy rows (long segments) included, with two accumulators in a fixed
+// order.
 // Comparison path: every token adds its slice with fp32 atomics (summation
 // order varies run to run).
 #include "kernels.h"
