@@ -25,7 +25,7 @@ def torch():
 
 
 @pytest.mark.parametrize("dtype,M,B,T", [("f32", 3, 2, 300), ("bf16", 2, 3, 77), ("f32", 1, 1, 64),
-                                         ("bf16", 4, 1, 513)])
+                                         ("bf16", 4, 1, 513), ("bf16", 8, 1, 130)])  # 8: the most
 def test_tiny_branches_full(torch, oracle_lib, dtype, M, B, T):
     wl = dataclasses.replace(synth.get_workload("tiny"), dtype=dtype, branches=M).with_shape(B, T)
     print(f"[branches tiny {dtype}] M={M} B={B} T={T}", flush=True)
@@ -77,7 +77,7 @@ def test_small_bf16_branches_sampled(torch, oracle_lib):
         assert err <= TOL["bf16"], (m, err)
 
 
-@pytest.mark.parametrize("dtype,M,B,T", [("f32", 2, 1, 300), ("bf16", 3, 2, 150)])
+@pytest.mark.parametrize("dtype,M,B,T", [("f32", 2, 1, 300), ("bf16", 3, 2, 150), ("f32", 8, 1, 70)])
 def test_branch_backward(torch, oracle_lib, dtype, M, B, T):
     """Training backward with M branches: the loss is the sum of the branches'
     <G^(m), Y^(m)>, so the table, W_V and conv gradients are the sums of the
