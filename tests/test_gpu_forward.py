@@ -232,3 +232,22 @@ def test_engram40b_forward(torch, oracle_lib, c40):
     print(f"  engram40b max-abs-err/max|ref| = {err:.3e}, alpha err {a_err:.2e}", flush=True)
     assert err <= TOL["bf16"], err
     assert a_err <= 1e-2
+
+
+def test_widest_hidden_forward(torch, oracle_lib):
+    """The widest hidden state the forward takes in bf16 (d = 8192: the gate +
+    conv workgroup is 1024 lanes of 8 features), against the oracle at every
+    position; the backward stops at d = 4096 and says so."""
+    import hashed_gram_embedding_canon_amd as eg
+    wl = dataclasses.replace(synth.get_workload("tiny"), name="tiny_wide", dtype="bf16",
+                             hidden=8192).with_shape(1, 100)
+    inp, dp, bufs, y = _run_full(torch, wl, saved=("idx", "stats", "k", "v"))
+    p = H.oracle_problem(inp)
+    ref = p.forward(want=("y", "alpha"))
+    err = H.rel_max_err(H.to_host_f64(y).reshape(-1, wl.hidden), ref["y"])
+    a_err = float(np.abs(bufs["stats"][:, 0].cpu().numpy() - ref["alpha"]).max())
+    print(f"  d = 8192: max-abs-err/max|ref| = {err:.3e}, alpha err {a_err:.2e}", flush=True)
+    assert err <= TOL["bf16"] and a_err <= 1e-2, (err, a_err)
+    dy = H.to_dev(np.zeros((1, 100, wl.hidden), np.float32).astype(np.uint16))
+    with pytest.raises(eg.EngramError, match="status 2"):
+        dp.backward(bufs, dy, eg.ENGRAM_GRAD_SORTED_SPARSE)
