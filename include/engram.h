@@ -95,8 +95,10 @@ typedef struct {
   int32_t num_orders;     /* 1..ENGRAM_MAX_ORDERS */
   int32_t orders[ENGRAM_MAX_ORDERS]; /* N-gram orders, strictly ascending, each 1..4 */
   int32_t heads;          /* K hash heads per order; J = num_orders*heads <= 32 */
-  int32_t dim;            /* D columns per table row; D*sizeof(dtype) % 16 == 0, J*D % 256 == 0 */
-  int32_t hidden;         /* d, width of h_t, k_t, v_t, Y_t; d % 256 == 0 */
+  int32_t dim;            /* D columns per table row; D*sizeof(dtype) % 16 == 0, J*D % 256 == 0;
+                             D <= 256 for the backward */
+  int32_t hidden;         /* d, width of h_t, k_t, v_t, Y_t; d % 256 == 0, d <= 8192 (bf16)
+                             or 4096 (fp32) in the forward, d <= 4096 in the backward */
   int32_t conv_kernel;    /* taps of the causal depthwise conv, 1..8 */
   int32_t dtype;          /* ENGRAM_F32 or ENGRAM_BF16 */
   float rms_eps;          /* eps inside both RMSNorms (e.g. 1e-6) */
