@@ -808,8 +808,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU table sharding is a design note, not a code path", file=sys.stderr)
+        print(f"bench.py: the Engram path runs on one GPU only (asked for --gpus {args.gpus}); "
+              "table sharding over several GPUs has its per-GPU steps here (--workload shard27b) "
+              "but no multi-GPU run", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == "shard27b":
