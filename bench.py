@@ -31,9 +31,11 @@ def log(*a):
 
 
 def kernel_units(wl, N):
-    """Algorithmic bytes / flops per launch of each forward kernel.
-    With M branches the projection has (M+1)*d outputs and reads M hidden
-    states; gate + conv reads v once and writes one Y per branch."""
+    """Algorithmic bytes / flops per launch of each forward kernel: the bytes a
+    kernel must move (each input read once, each output written once) and the
+    multiply-adds of its contraction.  With M branches the projection has
+    (M+1)*d outputs and reads M hidden states; gate + conv reads v once and
+    writes one Y per branch."""
     es = 2 if wl.dtype == "bf16" else 4
     J, d, dm, M = wl.J, wl.hidden, wl.d_mem, wl.branches
     nkt = d // 256
