@@ -86,7 +86,9 @@ def test_sorted_path_is_deterministic(torch):
 
 
 def test_engram27b_table_grads_sampled(torch, oracle_lib):
-    """27B-scale shapes: every key exact; rows of the heaviest and of random keys vs the oracle."""
+    """27B-scale shapes: every key exact; against the oracle, the rows of the
+    64 most-hit keys (the longest segments), the most-hit row of every table
+    and 24 seeded random keys."""
     import hashed_gram_embedding_canon_amd as eg
     wl = synth.get_workload("engram27b_bwd")
     print("[engram27b_bwd] forward + sorted and atomic backward", flush=True)
@@ -105,15 +107,16 @@ def test_engram27b_table_grads_sampled(torch, oracle_lib):
     want = np.unique(np.concatenate([(np.int64(j) << 32) | idx[:, j].astype(np.int64)
                                      for j in range(wl.J)]))
     assert np.array_equal(keys, want)
-    # pick rows: the most hit row of two tables plus seeded random keys
-    sel = []
-    for j in (0, wl.J - 1):
-        vals, cnt = np.unique(idx[:, j], return_counts=True)
-        sel.append((j, int(vals[np.argmax(cnt)])))
+    # pick rows: the 64 most-hit keys, the most-hit row of every table, seeded random keys
+    all_keys = np.concatenate([(np.int64(j) << 32) | idx[:, j].astype(np.int64) for j in range(wl.J)])
+    uk, cnt = np.unique(all_keys, return_counts=True)
+    picked = set(int(k) for k in uk[np.argsort(-cnt, kind="stable")[:64]])
+    for j in range(wl.J):
+        vals, c = np.unique(idx[:, j], return_counts=True)
+        picked.add((j << 32) | int(vals[np.argmax(c)]))
     picks = synth.u64_stream(21, 24) % np.uint64(len(keys))
-    for q in picks:
-        k = int(keys[int(q)])
-        sel.append((k >> 32, k & 0xFFFFFFFF))
+    picked.update(int(keys[int(q)]) for q in picks)
+    sel = [(k >> 32, k & 0xFFFFFFFF) for k in sorted(picked)]
     rj = np.array([s[0] for s in sel], np.int32)
     rr = np.array([s[1] for s in sel], np.int32)
     ref, npos = p.table_grad_rows(inp.dy, idx, rj, rr)
