@@ -67,7 +67,13 @@ def cpu_baseline(inp, budget_s: float):
     from tests import harness as H
     wl = inp.wl
     p = oracle.Problem.from_inputs(inp)
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    cores = int(oracle._load().oracle_threads())  # the threads its OpenMP loops use
+    host = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            host = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     pos_all = H.sample_positions(wl.B, wl.T, 1 << 16, seed=99)
     done = 0
     t0 = time.perf_counter()
@@ -79,7 +85,8 @@ def cpu_baseline(inp, budget_s: float):
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} sampled token positions of the {wl.name} workload "
-                      f"(each: hash, gather, both projections, gate of 4 tokens, conv), {dt:.1f} s"}
+                      f"(each: hash, gather, both projections, gate of 4 tokens, conv), {dt:.1f} s",
+            "host_cpu": host}
 
 
 # ------------------------------------------------------------ rocprofv3 summaries

@@ -87,6 +87,7 @@ def _load():
     lib.oracle_table_grad_rows.argtypes = [P, vp, vp, i64, vp, vp, vp]
     lib.oracle_table_grad_dense.argtypes = [P, vp, vp]
     lib.oracle_prefetch_plan.argtypes = [i64, i32, vp, vp, vp, vp]
+    lib.oracle_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 

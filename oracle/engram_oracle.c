@@ -34,6 +34,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <omp.h>
 
 #define OR_MAX_ORDERS 4
 
@@ -691,3 +692,6 @@ int oracle_prefetch_plan(int64_t N, int32_t J, const int32_t* idx, int32_t* uniq
   free(col);
   return 0;
 }
+
+/* Threads the parallel loops above use (for reporting the oracle's timing). */
+int oracle_threads(void) { return omp_get_max_threads(); }
