@@ -43,6 +43,8 @@ def kernel_units(wl, N):
     return {
         "hash": {"bound": "hbm", "bytes": N * 4 + N * J * 4},
         "gather": {"bound": "hbm", "bytes": N * J * 4 + 2 * N * dm * es},
+        # hash and gather in one kernel: token ids in, rows in, e out (no indices)
+        "hash_gather": {"bound": "hbm", "bytes": N * 4 + 2 * N * dm * es},
         "proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * (M + 1) * d, "bytes": proj_bytes},
         # the same projection reading the table rows itself (row gather fused)
         "gather_proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * (M + 1) * d,
@@ -110,7 +112,8 @@ def kernel_key(name: str) -> str:
         return "bwd_gate_conv_params" if targs[2] == "true" else "bwd_gate_conv"
     if "quant_rows_kernel" in base:
         return "quant_w"
-    for key in ("gather_quant", "gate_conv", "gather", "hash", "transpose_w", "atomic_scatter"):
+    for key in ("hash_gather", "gather_quant", "gate_conv", "gather", "hash", "transpose_w",
+                "atomic_scatter"):
         if f"engram::{key}_kernel" in base:
             return key
     # the per-GPU steps of the sharded exchange
@@ -909,7 +912,7 @@ def main():
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                     "traffic": int(traffic[dom]) if dom in traffic else None}
-    mem_names = [k for k in ("gather", "gather_quant", "gate_conv") if k in prof]
+    mem_names = [k for k in ("hash_gather", "gather", "gather_quant", "gate_conv") if k in prof]
     mem_ms = sum(prof[k][1] / prof[k][0] for k in mem_names)
     mem_bytes = sum(units[k]["bytes"] for k in mem_names)
     es = 2 if wl.dtype == "bf16" else 4

@@ -391,16 +391,28 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
                          hipMemcpyDeviceToDevice, hs) != hipSuccess)
         return ENGRAM_E_HIP;
     }
-  } else {
-    HashArgs ha = make_hash_args(cfg, s);
-    Timed tm("hash", hs);
-    if (launch_hash(tokens, p->canon_map, N, (int32_t)T, w.idx, ha, hs) != hipSuccess)
-      return ENGRAM_E_HIP;
-    for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
   }
   const bool fp8 = (s.flags & ENGRAM_FLAG_FP8_PROJ) != 0;
   const bool fused = w.e == nullptr && !fp8;
-  if (w.e) {  // bf16 e: the projection's operand, or kept for the caller
+  // Gathering bf16 e from the tables, one kernel hashes and gathers (the
+  // indices go to memory only for the caller); the row-indexed projection,
+  // the quantizing gather and the compact mode read indices from memory.
+  const bool hash_in_gather = !compact && w.e && !fp8;
+  if (!compact) {
+    const HashArgs ha = make_hash_args(cfg, s);
+    for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
+    if (hash_in_gather) {
+      Timed tm("hash_gather", hs);
+      if (launch_hash_gather(tokens, p->canon_map, N, (int32_t)T, ha, g, w.e,
+                             saved && saved->idx ? saved->idx : nullptr, hs) != hipSuccess)
+        return ENGRAM_E_HIP;
+    } else {
+      Timed tm("hash", hs);
+      if (launch_hash(tokens, p->canon_map, N, (int32_t)T, w.idx, ha, hs) != hipSuccess)
+        return ENGRAM_E_HIP;
+    }
+  }
+  if (w.e && !hash_in_gather) {  // bf16 e: the projection's operand, or kept for the caller
     Timed tm("gather", hs);
     if (launch_gather(idx, w.e, N, g, hs) != hipSuccess) return ENGRAM_E_HIP;
   }

@@ -91,6 +91,83 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   }
 }
 
+// Hash and gather in one kernel, for the forward that gathers e into memory:
+// a block first hashes the tokens its pieces of e belong to (their canonical
+// ids, with the N-gram context before them, staged in LDS), then copies its
+// pieces as gather_kernel does, reading the row indices from LDS.  The
+// indices of a token are written out (when asked) by the block that holds
+// its first piece.  One kernel boundary fewer than hash + gather; the hashes
+// of a token whose pieces straddle two blocks are computed twice.
+constexpr int kHgPieces = 256 * kGatherPer;      // pieces of e per block
+constexpr int kHgMaxTok = kHgPieces / 32 + 1;   // tokens a block touches (>= 32 pieces a token)
+__global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restrict__ tokens,
+                                                          const int32_t* __restrict__ canon,
+                                                          int32_t T, uint32_t pieces, GatherArgs g,
+                                                          HashArgs a, uint8_t* __restrict__ e,
+                                                          int32_t* __restrict__ idx_out) {
+  __shared__ const uint8_t* base_s[ENGRAM_MAX_TABLES];
+  __shared__ uint32_t c_s[kHgMaxTok + ENGRAM_MAX_ORDERS - 1];
+  __shared__ int32_t idx_s[kHgMaxTok * ENGRAM_MAX_TABLES];
+  const uint32_t rc = (uint32_t)g.row_chunks;
+  const uint32_t J = (uint32_t)g.J;
+  const uint32_t tp = rc * J;  // pieces per token
+  const uint32_t c_begin = blockIdx.x * (uint32_t)kHgPieces;
+  const uint32_t c_end = c_begin + kHgPieces < pieces ? c_begin + kHgPieces : pieces;
+  const int64_t n0 = c_begin / tp;
+  const int ntok = (int)((c_end - 1) / tp - n0) + 1;
+  const int H = a.max_order - 1;  // context tokens before n0
+  if (threadIdx.x < J) base_s[threadIdx.x] = g.base[threadIdx.x];
+  for (int i = threadIdx.x; i < ntok + H; i += 256) {
+    const int64_t n = n0 - H + i;
+    c_s[i] = n >= 0 ? (uint32_t)canon[tokens[n]] : 0u;  // n < 0 is never read (pad instead)
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < ntok * (int)J; q += 256) {
+    const int k = q / (int)J, j = q - k * (int)J;  // token n0 + k, table j
+    const int64_t n = n0 + k;
+    const int t = (int)(n % T);
+    uint32_t c[ENGRAM_MAX_ORDERS];
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDERS; ++i)
+      c[i] = i < a.max_order ? (t - i < 0 ? (uint32_t)a.pad_id : c_s[k + H - i]) : 0u;
+    const int32_t r = (int32_t)hash_one(a, j, a.orders[j / a.heads], c);
+    idx_s[q] = r;
+    if (idx_out && (uint64_t)n * tp >= c_begin) idx_out[n * J + j] = r;
+  }
+  __syncthreads();
+  const uint32_t c0 = c_begin + threadIdx.x;
+  u32x4 v[kGatherPer];
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) {
+    const uint32_t c = c0 + u * 256u;
+    if (c < c_end) {
+      const uint32_t nj = c / rc;  // token * J + table
+      const uint32_t part = c - nj * rc;
+      const uint32_t j = nj % J;
+      const int64_t row = idx_s[nj - (uint32_t)n0 * J];
+      v[u] = *(reinterpret_cast<const u32x4*>(base_s[j] + row * rc * 16) + part);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) {
+    const uint32_t c = c0 + u * 256u;
+    if (c < c_end) *(reinterpret_cast<u32x4*>(e) + c) = v[u];
+  }
+}
+
+hipError_t launch_hash_gather(const int32_t* tokens, const int32_t* canon, int64_t N, int32_t T,
+                              const HashArgs& a, const GatherArgs& g, uint8_t* e, int32_t* idx_out,
+                              hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  const int64_t tp = (int64_t)g.J * g.row_chunks;
+  const int64_t pieces = N * tp;
+  if (tp < 32 || pieces >= (int64_t(1) << 32) - kHgPieces) return hipErrorInvalidValue;
+  const int64_t blocks = (pieces + kHgPieces - 1) / kHgPieces;
+  hipLaunchKernelGGL(hash_gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, tokens, canon, T,
+                     (uint32_t)pieces, g, a, e, idx_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const int32_t* idx, uint8_t* e, int64_t N, const GatherArgs& g,
                          hipStream_t s) {
   if (N == 0) return hipSuccess;

@@ -18,6 +18,10 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const int32_t* idx, uint8_t* e, int64_t N, const GatherArgs& g,
                          hipStream_t s);
+// hash + gather in one launch; idx_out [N][J] (may be null) receives the indices
+hipError_t launch_hash_gather(const int32_t* tokens, const int32_t* canon, int64_t N, int32_t T,
+                              const HashArgs& a, const GatherArgs& g, uint8_t* e, int32_t* idx_out,
+                              hipStream_t s);
 
 // ---------------------------------------------------------------- GEMM
 // C^T[f][m] = sum_k A[f][k] * B[m][k]; A: [F][K] (weights), B: [M][K] (tokens).

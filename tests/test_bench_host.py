@@ -26,6 +26,9 @@ import synth  # noqa: E402
     ("void engram::bwd_gate_conv_kernel<true, 4, true, 768, false>(engram::BwdArgs)", "bwd_gate_conv_params"),
     ("void engram::gate_conv_kernel<8, true, 4>(engram::GateConvArgs)", "gate_conv"),
     ("engram::gather_kernel(int const*, unsigned char*, unsigned int, engram::GatherArgs)", "gather"),
+    ("engram::hash_gather_kernel(int const*, int const*, int, unsigned int, engram::GatherArgs)",
+     "hash_gather"),
+    ("engram::hash_kernel(int const*, int const*, long, int, int*, engram::HashArgs)", "hash"),
     ("engram::gather_quant_kernel(int const*, long, engram::GatherArgs, int, unsigned char*, float*)",
      "gather_quant"),
     ("void engram::quant_rows_kernel<true>(unsigned char const*, long, int, unsigned char*, float*)", "quant_w"),
