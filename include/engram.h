@@ -328,8 +328,10 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
  * section "DeepSeek Engram", multi-branch integration: the projections as one
  * dense FP8 matmul): per row, s = max|x| / 448 (1 for an all-zero row) and
  * the OCP E4M3 codes of x / s (fp32 division, round to nearest even).
- *   src: device [rows][cols] dtype (ENGRAM_BF16 or ENGRAM_F32), cols % 8 == 0;
- *   codes: device [rows][cols] out; scales: device [rows] fp32 out.
+ *   src: device [rows][cols] dtype (ENGRAM_BF16 or ENGRAM_F32), cols % 8 == 0,
+ *   16-byte aligned; codes: device [rows][cols] out, 8-byte aligned; scales:
+ *   device [rows] fp32 out.  Errors: ENGRAM_E_UNSUPPORTED for another dtype,
+ *   ENGRAM_E_INVALID for a null or misaligned pointer or a bad size.
  */
 engram_status engram_quantize_fp8(const void* src, int32_t dtype, int64_t rows, int32_t cols,
                                   uint8_t* codes, float* scales, void* stream);

@@ -263,3 +263,16 @@ def test_profile_api_without_launches(eg):
     eg.engram_profile_reset()
     assert eg.engram_profile_read() == {}
     eg.engram_profile_enable(False)
+
+
+def test_quantize_fp8_validation(eg):
+    L = eg.lib()
+    q = lambda *a: L.engram_quantize_fp8(*a, None)  # noqa: E731
+    assert q(FAKE, 7, 4, 64, FAKE, FAKE) == eg.ENGRAM_E_UNSUPPORTED        # dtype
+    assert q(FAKE, eg.ENGRAM_BF16, -1, 64, FAKE, FAKE) == eg.ENGRAM_E_INVALID
+    assert q(FAKE, eg.ENGRAM_BF16, 4, 60, FAKE, FAKE) == eg.ENGRAM_E_INVALID  # cols % 8
+    assert q(FAKE, eg.ENGRAM_BF16, 4, 0, FAKE, FAKE) == eg.ENGRAM_E_INVALID
+    assert q(None, eg.ENGRAM_BF16, 4, 64, FAKE, FAKE) == eg.ENGRAM_E_INVALID
+    assert q(FAKE + 8, eg.ENGRAM_BF16, 4, 64, FAKE, FAKE) == eg.ENGRAM_E_INVALID  # src alignment
+    assert q(FAKE, eg.ENGRAM_BF16, 4, 64, FAKE + 4, FAKE) == eg.ENGRAM_E_INVALID  # codes alignment
+    assert q(FAKE, eg.ENGRAM_BF16, 0, 64, FAKE, FAKE) == eg.ENGRAM_OK         # nothing to do
