@@ -133,17 +133,26 @@ def kernel_key(name: str) -> str:
     return ""
 
 
-def csrc_digest() -> str:
-    """sha256 over the library sources; traffic figures are tied to it."""
+def code_tokens(src: str) -> str:
+    """C/C++ source without its comments and with whitespace runs collapsed:
+    what the compiler sees, so edits of comments do not count as changes."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def csrc_digest(root: str | None = None) -> str:
+    """sha256 over the code of the library sources (comments excluded);
+    traffic figures are tied to it."""
     import hashlib
+    root = root or ROOT
     h = hashlib.sha256()
-    d = os.path.join(ROOT, "hashed_gram_embedding_canon_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
-    with open(os.path.join(ROOT, "include", "engram.h"), "rb") as fh:
-        h.update(fh.read())
+    d = os.path.join(root, "hashed_gram_embedding_canon_amd", "csrc")
+    files = [os.path.join(d, f) for f in sorted(os.listdir(d)) if f.endswith((".hip", ".h"))]
+    for path in files + [os.path.join(root, "include", "engram.h")]:
+        with open(path, encoding="utf-8") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -129,3 +129,10 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_digest_ignores_comments_only():
+    a = "int f(int x) { // the input\n  return x + 1; /* one more */ }\n"
+    b = "int f(int x) {\n  /* changed words */ return x + 1;   }  // other\n"
+    c = "int f(int x) { return x + 2; }"
+    assert bench.code_tokens(a) == bench.code_tokens(b) != bench.code_tokens(c)
