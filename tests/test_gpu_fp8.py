@@ -71,6 +71,8 @@ def test_fp8_forward_matches_oracle(torch, oracle_lib, B, T, M):
     torch.cuda.synchronize()
     for m in range(M):
         p = _fp8_problem(inp, branch=m)
+        if m == 0:  # the indices the quantizing gather hashed and saved
+            assert np.array_equal(bufs["idx"].cpu().numpy(), p.hash())
         ref = p.forward(want=("y", "k", "alpha"))
         ym = y if M == 1 else y[m]
         km = bufs["k"] if M == 1 else bufs["k"][m]
