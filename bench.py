@@ -479,6 +479,20 @@ def bench_host(args):
     host_ms = (time.perf_counter() - t) * 1e3
     torch.cuda.synchronize()
     copy_ms = s0.elapsed_time(ev)
+    # the compact forward against the forward over the same tables in HBM
+    # (uploaded for this check only)
+    y_c = torch.empty(wl.B, wl.T, wl.hidden, dtype=dp.tdtype, device="cuda")
+    dp.forward(compact=plan, y=y_c)
+    dev_tables = [H.to_dev(tb) for tb in host_tables]
+    params_full = eg.make_params(canon_map=dp.canon, tables=dev_tables, w_kv=dp.w_kv, conv_w=dp.conv_w)
+    y_full = torch.empty_like(y_c)
+    eg.engram_forward(dp.cfg, params_full, dp.tokens, dp.hidden, y_full, B=wl.B, T=wl.T,
+                      workspace=dp.workspace(eg.ENGRAM_OP_FORWARD))
+    torch.cuda.synchronize()
+    compact_identical = bool(torch.equal(y_c, y_full))
+    del dev_tables, params_full, y_full, y_c
+    torch.cuda.empty_cache()
+    log(f"[bench-host] compact forward bit-identical to the HBM-table forward: {compact_identical}")
     # 3. compact forward alone, and the stand-in GEMM
     y = torch.empty(wl.B, wl.T, wl.hidden, dtype=dp.tdtype, device="cuda")
     ws = dp.workspace(eg.ENGRAM_OP_FORWARD)
@@ -524,12 +538,12 @@ def bench_host(args):
                       "tokens_per_s": round(N / (t_ovl * 1e-3), 1)})
     ring = bench_ring(args, wl, inp, dp, host_tables, staging, inv_h, inv_dev, side, ev, y, ws,
                       lambda: torch.matmul(xa, wg, out=yg), timed)
-    # the compact forward is bit-identical to the one reading the tables in HBM
     out = {
         "metric": "host-table Engram forward: tokens/s and exposed copy time",
         "workload": wl.name, "batch": wl.B, "seq_len": wl.T, "tables": J,
         "rows_per_table": list(wl.rows[:1]) + ["..."], "dim": wl.dim, "hidden": wl.hidden,
         "table_params": wl.table_params, "unique_rows": int(plan.total_rows),
+        "compact_forward_bit_identical": compact_identical,
         "plan_ahead_ms": round(plan_ms, 2), "gather_host_ms": round(host_ms, 2),
         "h2d_copy_ms": round(copy_ms, 3), "copy_bytes": copy_bytes,
         "h2d_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
