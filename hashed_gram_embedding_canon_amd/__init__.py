@@ -22,6 +22,7 @@ ENGRAM_MAX_TABLES = 32
 ENGRAM_MAX_BRANCHES = 8
 ENGRAM_FLAG_FUSED_GATHER = 1
 ENGRAM_FLAG_FP8_PROJ = 2
+ENGRAM_FLAG_CHECK_IDS = 4
 ENGRAM_PLAN_REUSE = 1
 ENGRAM_GRAD_SORTED_SPARSE, ENGRAM_GRAD_SORTED_DENSE, ENGRAM_GRAD_ATOMIC_DENSE = 0, 1, 2
 ENGRAM_OP_FORWARD, ENGRAM_OP_BACKWARD, ENGRAM_OP_BACKWARD_PARAMS, ENGRAM_OP_SHARD = 0, 1, 2, 3
@@ -47,6 +48,7 @@ class engram_config(ctypes.Structure):
         ("multipliers", _vp),
         ("flags", ctypes.c_uint32),
         ("branches", ctypes.c_int32),
+        ("bad_ids", _vp),
     ]
 
 
@@ -192,7 +194,8 @@ class Config:
     """engram_config plus the host arrays it points at (kept alive here)."""
 
     def __init__(self, *, vocab, canon_vocab, orders, heads, dim, hidden, table_rows, multipliers,
-                 dtype=ENGRAM_BF16, conv_kernel=4, rms_eps=1e-6, pad_id=0, flags=0, branches=1):
+                 dtype=ENGRAM_BF16, conv_kernel=4, rms_eps=1e-6, pad_id=0, flags=0, branches=1,
+                 bad_ids=None):
         import numpy as np
         self.table_rows = np.ascontiguousarray(table_rows, dtype=np.int64)
         self.multipliers = np.ascontiguousarray(multipliers, dtype=np.uint64)
@@ -208,6 +211,7 @@ class Config:
         c.multipliers = self.multipliers.ctypes.data
         c.flags = int(flags)
         c.branches = int(branches)
+        c.bad_ids = _ptr(bad_ids)
         self.c = c
         self.branches = max(1, int(branches))
         self.J = len(orders) * int(heads)

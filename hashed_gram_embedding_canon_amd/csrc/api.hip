@@ -54,7 +54,10 @@ engram_status check_config(const engram_config* c, Shape* s) {
   if (c->dim < 1 || c->hidden < 1) return ENGRAM_E_INVALID;
   if (c->conv_kernel < 1 || c->conv_kernel > 8) return ENGRAM_E_UNSUPPORTED;
   if (!(c->rms_eps >= 0.f)) return ENGRAM_E_INVALID;
-  if (c->flags & ~(uint32_t)(ENGRAM_FLAG_FUSED_GATHER | ENGRAM_FLAG_FP8_PROJ)) return ENGRAM_E_INVALID;
+  if (c->flags & ~(uint32_t)(ENGRAM_FLAG_FUSED_GATHER | ENGRAM_FLAG_FP8_PROJ | ENGRAM_FLAG_CHECK_IDS))
+    return ENGRAM_E_INVALID;
+  if ((c->flags & ENGRAM_FLAG_CHECK_IDS) && (!c->bad_ids || ((uintptr_t)c->bad_ids & 3u)))
+    return ENGRAM_E_INVALID;
   // the FP8 projection quantizes bf16 rows; the fused row gather reads bf16 tables itself
   if ((c->flags & ENGRAM_FLAG_FP8_PROJ) &&
       (c->dtype != ENGRAM_BF16 || (c->flags & ENGRAM_FLAG_FUSED_GATHER)))
@@ -102,7 +105,26 @@ HashArgs make_hash_args(const engram_config* c, const Shape& s) {
     a.recip[j] = mod_recip(a.prime[j]);
     for (int i = 0; i < s.max_order; ++i) a.mult[j * s.max_order + i] = c->multipliers[j * s.max_order + i];
   }
+  a.bad = (c->flags & ENGRAM_FLAG_CHECK_IDS) ? c->bad_ids : nullptr;
+  a.vocab = c->vocab;
   return a;
+}
+
+// ENGRAM_FLAG_CHECK_IDS: zero the caller's counter before the hash kernels
+// run (a kernel, not a memset, so the call can sit in a captured graph)...
+engram_status id_check_begin(const engram_config* c, hipStream_t s) {
+  if (!(c->flags & ENGRAM_FLAG_CHECK_IDS)) return ENGRAM_OK;
+  return launch_zero_f32(reinterpret_cast<float*>(c->bad_ids), 1, s) == hipSuccess ? ENGRAM_OK
+                                                                                  : ENGRAM_E_HIP;
+}
+// ... and after the call's kernels: wait for them and report bad ids.
+engram_status id_check_end(const engram_config* c, hipStream_t s) {
+  if (!(c->flags & ENGRAM_FLAG_CHECK_IDS)) return ENGRAM_OK;
+  uint32_t bad = 0;
+  if (hipMemcpyAsync(&bad, c->bad_ids, sizeof(bad), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return ENGRAM_E_HIP;
+  return bad ? ENGRAM_E_INVALID : ENGRAM_OK;
 }
 
 inline engram_status hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_E_HIP; }
@@ -331,8 +353,12 @@ engram_status engram_hash_indices(const engram_config* cfg, const int32_t* canon
   if (!canon_map || !tokens || !idx) return ENGRAM_E_INVALID;
   hipStream_t hs = (hipStream_t)stream;
   HashArgs ha = make_hash_args(cfg, s);
-  Timed tm("hash", hs);
-  return hip_status(launch_hash(tokens, canon_map, B * T, (int32_t)T, idx, ha, hs));
+  if ((st = id_check_begin(cfg, hs)) != ENGRAM_OK) return st;
+  {
+    Timed tm("hash", hs);
+    if (launch_hash(tokens, canon_map, B * T, (int32_t)T, idx, ha, hs) != hipSuccess) return ENGRAM_E_HIP;
+  }
+  return id_check_end(cfg, hs);
 }
 
 engram_status engram_forward(const engram_config* cfg, const engram_params* p,
@@ -400,6 +426,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
   const bool hash_in_gather = !compact && w.e && !fp8;
   if (!compact) {
     const HashArgs ha = make_hash_args(cfg, s);
+    if ((st = id_check_begin(cfg, hs)) != ENGRAM_OK) return st;
     for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
     if (hash_in_gather) {
       Timed tm("hash_gather", hs);
@@ -482,7 +509,7 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     Timed tm("gate_conv", hs);
     if (launch_gate_conv(gc, hs) != hipSuccess) return ENGRAM_E_HIP;
   }
-  return ENGRAM_OK;
+  return compact ? ENGRAM_OK : id_check_end(cfg, hs);
 }
 
 engram_status engram_backward(const engram_config* cfg, const engram_params* p,

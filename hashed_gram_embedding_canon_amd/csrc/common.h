@@ -72,7 +72,26 @@ struct HashArgs {
   uint32_t prime[ENGRAM_MAX_TABLES];
   uint64_t recip[ENGRAM_MAX_TABLES];
   uint64_t mult[ENGRAM_MAX_TABLES * ENGRAM_MAX_ORDERS];  // [j][i], i < max_order
+  // id check (null: ids are trusted): an id outside [0, vocab) is counted
+  // into *bad and read as canonical pad_id, so canon_map is never indexed
+  // out of bounds
+  uint32_t* bad;
+  int32_t vocab;
 };
+
+#if defined(__HIPCC__)
+// Canonical id of raw token x under the id check of a (see HashArgs::bad).
+// Several lanes may read one token (context windows); only the read that
+// owns it (own = true) counts it, so *bad ends up as the number of bad ids.
+__device__ inline uint32_t canon_of(const int32_t* __restrict__ canon, int32_t x, const HashArgs& a,
+                                    bool own) {
+  if (a.bad != nullptr && (uint32_t)x >= (uint32_t)a.vocab) {
+    if (own) atomicAdd(a.bad, 1u);
+    return (uint32_t)a.pad_id;
+  }
+  return (uint32_t)canon[x];
+}
+#endif
 
 // idx_j for one token given its canonical context c[i] = c_{t-i} (i < max_order).
 __host__ __device__ inline uint32_t hash_one(const HashArgs& a, int j, int n, const uint32_t* c) {

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void hash_kernel(const int32_t* __restrict__ t
   const int64_t nc = live ? n : N - 1;  // dead lanes still take part in the shifts
   const int t = (int)(nc % T);
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t c0 = (uint32_t)canon[tokens[nc]];
+  const uint32_t c0 = canon_of(canon, tokens[nc], a, live);
   uint32_t c[ENGRAM_MAX_ORDERS];
   c[0] = c0;
 #pragma unroll
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void hash_kernel(const int32_t* __restrict__ t
       if (t - i < 0)
         c[i] = (uint32_t)a.pad_id;
       else if (lane < i)
-        c[i] = (uint32_t)canon[tokens[nc - i]];
+        c[i] = canon_of(canon, tokens[nc - i], a, false);
       else
         c[i] = from_left;
     } else {
@@ -119,7 +119,9 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
   if (threadIdx.x < J) base_s[threadIdx.x] = g.base[threadIdx.x];
   for (int i = threadIdx.x; i < ntok + H; i += 256) {
     const int64_t n = n0 - H + i;
-    c_s[i] = n >= 0 ? (uint32_t)canon[tokens[n]] : 0u;  // n < 0 is never read (pad instead)
+    // the block holding a token's first piece owns it (counts a bad id)
+    const bool own = i >= H && (uint64_t)n * tp >= c_begin;
+    c_s[i] = n >= 0 ? canon_of(canon, tokens[n], a, own) : 0u;  // n < 0 is never read (pad instead)
   }
   __syncthreads();
   for (int q = threadIdx.x; q < ntok * (int)J; q += 256) {

@@ -41,7 +41,8 @@
  *     rejected call returns a non-zero engram_status and queues nothing.  A
  *     failed launch returns ENGRAM_E_HIP; faults inside kernels surface when
  *     the caller synchronises.  Token ids must lie in [0, vocab): this is a
- *     precondition, not checked on the device.
+ *     precondition that the device does not check unless the config asks
+ *     for ENGRAM_FLAG_CHECK_IDS (the host planner always checks).
  *   - Layout: row-major, densely packed; N = B*T tokens, token n = b*T + t.
  *     Every pointer must be 16-byte aligned.
  *   - dtype: ENGRAM_F32 (float) or ENGRAM_BF16 (bfloat16) for tables,
@@ -85,7 +86,19 @@ enum {
    * only, d_mem <= 4096; not with ENGRAM_FLAG_FUSED_GATHER (else
    * ENGRAM_E_UNSUPPORTED).  The backward is unchanged (it
    * takes the saved k, v of this forward and the bf16 weights). */
-  ENGRAM_FLAG_FP8_PROJ = 2u
+  ENGRAM_FLAG_FP8_PROJ = 2u,
+  /* Token-id check for engram_hash_indices and engram_forward (over device
+   * tables).  Retrieval depends on the token ids alone ("DeepSeek AI II",
+   * section "DeepSeek Engram"), so an id outside [0, vocab) has no defined
+   * canonical id.  Unchecked, such an id is a precondition violation: the
+   * kernels would read canon_map out of bounds.  With this flag the call
+   * zeroes *bad_ids, the kernels read every out-of-range id as canonical
+   * pad_id (canon_map is never indexed out of bounds) and add one to
+   * *bad_ids per such id, and the call then synchronises the stream and
+   * returns ENGRAM_E_INVALID when *bad_ids > 0.  The outputs are still
+   * written in full (with pad_id in place of the bad ids).  Costs one
+   * stream synchronisation per call; compact-mode forwards read no ids. */
+  ENGRAM_FLAG_CHECK_IDS = 4u
 };
 
 /* Shapes and addressing constants.  Host struct, read during the call only. */
@@ -110,6 +123,8 @@ typedef struct {
                                   its own W_K, hidden state, gate and output ("DeepSeek AI
                                   II", section "DeepSeek Engram", multi-branch integration);
                                   0 or 1 = one branch, at most ENGRAM_MAX_BRANCHES */
+  uint32_t* bad_ids;           /* device [1], 4-byte aligned: out-of-range ids counted under
+                                  ENGRAM_FLAG_CHECK_IDS (required then, ignored otherwise) */
 } engram_config;
 
 #define ENGRAM_MAX_BRANCHES 8

@@ -108,6 +108,23 @@ def test_forward_validation(eg):
     assert eg.engram_workspace_size(_cfg(eg, **dict(wide, dim=256)), 2, 8, 0) > 0  # d_mem 4096
 
 
+def test_id_check_validation(eg):
+    """ENGRAM_FLAG_CHECK_IDS needs a 4-byte aligned device counter; without one
+    the call is rejected on the host, before any GPU work."""
+    chk = eg.ENGRAM_FLAG_CHECK_IDS
+    L = eg.lib()
+    for bad in (None, FAKE + 2):
+        cfg = _cfg(eg, flags=chk, bad_ids=bad)
+        assert _fwd(eg, cfg) == eg.ENGRAM_E_INVALID
+        assert L.engram_hash_indices(cfg.ref, FAKE, FAKE, 2, 8, FAKE, None) == eg.ENGRAM_E_INVALID
+        assert eg.engram_workspace_size(cfg, 2, 8, eg.ENGRAM_OP_FORWARD) == 0
+    ok = _cfg(eg, flags=chk, bad_ids=FAKE + 4)
+    assert eg.engram_workspace_size(ok, 2, 8, eg.ENGRAM_OP_FORWARD) == \
+        eg.engram_workspace_size(_cfg(eg), 2, 8, eg.ENGRAM_OP_FORWARD)
+    assert _fwd(eg, ok, B=0) == eg.ENGRAM_OK  # no tokens: nothing queued, no sync
+    assert _fwd(eg, _cfg(eg, flags=8)) == eg.ENGRAM_E_INVALID  # unknown flag bit
+
+
 def test_backward_and_hash_validation(eg):
     cfg = _cfg(eg)
     L = eg.lib()
