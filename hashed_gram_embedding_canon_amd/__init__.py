@@ -15,7 +15,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libengram.so")
 
-ENGRAM_OK, ENGRAM_E_INVALID, ENGRAM_E_UNSUPPORTED, ENGRAM_E_WORKSPACE, ENGRAM_E_HIP = range(5)
+ENGRAM_OK, ENGRAM_E_INVALID, ENGRAM_E_UNSUPPORTED, ENGRAM_E_WORKSPACE, ENGRAM_E_HIP, ENGRAM_E_SCRATCH = range(6)
+ENGRAM_NOALLOC_SCRATCH_BYTES = 64 << 20
 ENGRAM_F32, ENGRAM_BF16 = 0, 1
 ENGRAM_MAX_ORDERS = 4
 ENGRAM_MAX_TABLES = 32
@@ -113,6 +114,7 @@ class EngramError(RuntimeError):
 
 
 EXPORTS = ("engram_workspace_size", "engram_status_string", "engram_hash_indices", "engram_forward",
+           "engram_forward_noalloc",
            "engram_backward_table_grad", "engram_backward", "engram_prefetch_plan",
            "engram_shard_requests", "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce",
            "engram_quantize_fp8",
@@ -141,6 +143,7 @@ def lib():
     L.engram_status_string.restype = ctypes.c_char_p
     L.engram_hash_indices.argtypes = [C, _vp, _vp, i64, i64, _vp, _vp]
     L.engram_forward.argtypes = [C, P, _vp, _vp, i64, i64, _vp, S, K, _vp, sz, _vp]
+    L.engram_forward_noalloc.argtypes = [C, P, _vp, _vp, i64, i64, _vp, S, K, _vp]
     L.engram_backward_table_grad.argtypes = [C, P, _vp, _vp, i64, i64, S, G, _vp, sz, _vp]
     L.engram_backward.argtypes = [C, P, _vp, _vp, i64, i64, S, G, PG, _vp, sz, _vp]
     L.engram_prefetch_plan.argtypes = [C, _vp, _vp, i64, i64, _vp, K, _vp]
@@ -155,7 +158,8 @@ def lib():
     L.engram_profile_reset.restype = None
     L.engram_profile_read.argtypes = [ctypes.c_char_p, sz, _vp, _vp, i32]
     L.engram_profile_read.restype = i32
-    for name in ("engram_hash_indices", "engram_forward", "engram_backward_table_grad",
+    for name in ("engram_hash_indices", "engram_forward", "engram_forward_noalloc",
+                 "engram_backward_table_grad",
                  "engram_backward", "engram_prefetch_plan", "engram_shard_requests",
                  "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce",
                  "engram_quantize_fp8"):
@@ -263,6 +267,15 @@ def engram_forward(cfg: Config, params: engram_params, tokens, hidden, y, *, B: 
                                 _ptr(y), ctypes.byref(saved) if saved is not None else None,
                                 ctypes.byref(compact) if compact is not None else None,
                                 _ptr(workspace), ws_bytes, _stream(stream)), "engram_forward")
+
+
+def engram_forward_noalloc(cfg: Config, params: engram_params, tokens, hidden, y, *, B: int, T: int,
+                           saved: engram_saved | None = None, compact: engram_compact | None = None,
+                           stream=None):
+    _check(lib().engram_forward_noalloc(cfg.ref, ctypes.byref(params), _ptr(tokens), _ptr(hidden), B,
+                                        T, _ptr(y), ctypes.byref(saved) if saved is not None else None,
+                                        ctypes.byref(compact) if compact is not None else None,
+                                        _stream(stream)), "engram_forward_noalloc")
 
 
 def engram_backward_table_grad(cfg: Config, params: engram_params, hidden, dy, *, B: int, T: int,

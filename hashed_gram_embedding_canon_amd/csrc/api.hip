@@ -138,12 +138,20 @@ struct ProfRec {
 };
 std::vector<ProfRec> g_prof;
 
+// Set while an allocation-free call runs on this thread: no timing events.
+thread_local bool t_quiet = false;
+struct QuietTiming {
+  bool prev;
+  explicit QuietTiming(bool on) : prev(t_quiet) { t_quiet = t_quiet || on; }
+  ~QuietTiming() { t_quiet = prev; }
+};
+
 class Timed {
  public:
   Timed(const char* name, hipStream_t s) : name_(name), s_(s) {
     {
       std::lock_guard<std::mutex> l(g_prof_mu);
-      on_ = g_prof_on;
+      on_ = g_prof_on && !t_quiet;
     }
     if (on_) {
       on_ = hipEventCreate(&a_) == hipSuccess && hipEventCreate(&b_) == hipSuccess &&
@@ -163,6 +171,33 @@ class Timed {
   hipEvent_t a_{}, b_{};
   bool on_ = false;
 };
+
+// ---------------------------------------------------------------- fixed scratch
+// engram_forward_noalloc's workspace: a device array in the library's code
+// object, so the call allocates nothing.  In host code `scratch` names a
+// host-side stand-in, not the device address: the address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that pointer is handed to kernels.  Every call on a device shares its
+// array, so calls that overlap on one device race.
+constexpr size_t kScratchBytes = ENGRAM_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+engram_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ENGRAM_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ENGRAM_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> l(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return ENGRAM_E_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return ENGRAM_OK;
+}
 
 // ---------------------------------------------------------------- workspace
 struct FwdWs {
@@ -338,6 +373,8 @@ const char* engram_status_string(engram_status st) {
       return "workspace missing or too small";
     case ENGRAM_E_HIP:
       return "HIP runtime or launch error";
+    case ENGRAM_E_SCRATCH:
+      return "input needs more than the fixed scratch of the allocation-free entry point";
   }
   return "unknown status";
 }
@@ -361,10 +398,12 @@ engram_status engram_hash_indices(const engram_config* cfg, const int32_t* canon
   return id_check_end(cfg, hs);
 }
 
-engram_status engram_forward(const engram_config* cfg, const engram_params* p,
-                             const int32_t* tokens, const void* hidden, int64_t B, int64_t T,
-                             void* y, const engram_saved* saved, const engram_compact* compact,
-                             void* workspace, size_t ws_bytes, void* stream) {
+// The forward of engram_forward; with noalloc (engram_forward_noalloc) the
+// workspace is this device's fixed scratch array instead of the caller's.
+static engram_status forward_impl(const engram_config* cfg, const engram_params* p,
+                                  const int32_t* tokens, const void* hidden, int64_t B, int64_t T,
+                                  void* y, const engram_saved* saved, const engram_compact* compact,
+                                  void* workspace, size_t ws_bytes, void* stream, bool noalloc) {
   Shape s;
   engram_status st = check_config(cfg, &s);
   if (st != ENGRAM_OK) return st;
@@ -395,6 +434,12 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
       return ENGRAM_E_INVALID;
   }
   const size_t need = forward_ws(s, N, saved, nullptr, nullptr);
+  QuietTiming quiet(noalloc);  // no timing events: they are allocations too
+  if (noalloc) {
+    if (need > kScratchBytes) return ENGRAM_E_SCRATCH;
+    if ((st = scratch_ptr(&workspace)) != ENGRAM_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
   if (need > 0 && (!workspace || ws_bytes < need || !aligned16(workspace))) return ENGRAM_E_WORKSPACE;
   FwdWs w;
   forward_ws(s, N, saved, &w, (uint8_t*)workspace);
@@ -510,6 +555,21 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* p,
     if (launch_gate_conv(gc, hs) != hipSuccess) return ENGRAM_E_HIP;
   }
   return compact ? ENGRAM_OK : id_check_end(cfg, hs);
+}
+
+engram_status engram_forward(const engram_config* cfg, const engram_params* p,
+                             const int32_t* tokens, const void* hidden, int64_t B, int64_t T,
+                             void* y, const engram_saved* saved, const engram_compact* compact,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(cfg, p, tokens, hidden, B, T, y, saved, compact, workspace, ws_bytes, stream,
+                      false);
+}
+
+engram_status engram_forward_noalloc(const engram_config* cfg, const engram_params* p,
+                                     const int32_t* tokens, const void* hidden, int64_t B, int64_t T,
+                                     void* y, const engram_saved* saved,
+                                     const engram_compact* compact, void* stream) {
+  return forward_impl(cfg, p, tokens, hidden, B, T, y, saved, compact, nullptr, 0, stream, true);
 }
 
 engram_status engram_backward(const engram_config* cfg, const engram_params* p,

@@ -64,7 +64,9 @@ typedef enum {
   ENGRAM_E_INVALID = 1,     /* null pointer, bad size/shape, misalignment */
   ENGRAM_E_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle */
   ENGRAM_E_WORKSPACE = 3,   /* workspace missing or smaller than engram_workspace_size() */
-  ENGRAM_E_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  ENGRAM_E_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  ENGRAM_E_SCRATCH = 5      /* engram_forward_noalloc: the call needs more than its fixed
+                               scratch (ENGRAM_NOALLOC_SCRATCH_BYTES) */
 } engram_status;
 
 enum { ENGRAM_F32 = 0, ENGRAM_BF16 = 1 };
@@ -268,6 +270,28 @@ engram_status engram_forward(const engram_config* cfg, const engram_params* para
                              const int32_t* tokens, const void* hidden, int64_t B, int64_t T,
                              void* y, const engram_saved* saved, const engram_compact* compact,
                              void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): engram_forward without the workspace argument.  Its scratch
+ * (the gathered e, v and the gate partial sums) is a fixed device array of
+ * ENGRAM_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; the call itself allocates nothing (no hipMalloc, no
+ * events, no allocating library routine).  Inputs and outputs are the
+ * caller's, as for engram_forward.  A call that needs more scratch than
+ * that (engram_workspace_size(cfg, B, T, ENGRAM_OP_FORWARD) bounds it)
+ * returns ENGRAM_E_SCRATCH before any GPU work.  The array belongs to the
+ * current device (the stream must be one of its streams).  Every call on a
+ * GPU shares that GPU's array and finds the last call's contents there
+ * (nothing in the forward needs it cleared), so calls that overlap on one
+ * GPU -- on two streams, or from two threads -- race: serialise them.
+ */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+engram_status engram_forward_noalloc(const engram_config* cfg, const engram_params* params,
+                                     const int32_t* tokens, const void* hidden, int64_t B, int64_t T,
+                                     void* y, const engram_saved* saved,
+                                     const engram_compact* compact, void* stream);
 
 /*
  * Table-gradient backward ("DeepSeek AI II", system-efficiency part: in

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(eg):
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     L = ctypes.CDLL(eg.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(eg):
 
 def test_status_strings(eg):
     assert eg.engram_status_string(0) == "ok"
-    for s in range(1, 5):
+    for s in range(1, 6):
         assert eg.engram_status_string(s) not in ("ok", "unknown status")
     assert eg.engram_status_string(99) == "unknown status"
 
@@ -123,6 +123,25 @@ def test_id_check_validation(eg):
         eg.engram_workspace_size(_cfg(eg), 2, 8, eg.ENGRAM_OP_FORWARD)
     assert _fwd(eg, ok, B=0) == eg.ENGRAM_OK  # no tokens: nothing queued, no sync
     assert _fwd(eg, _cfg(eg, flags=8)) == eg.ENGRAM_E_INVALID  # unknown flag bit
+
+
+def test_noalloc_forward_host_checks(eg):
+    """The allocation-free forward validates like engram_forward and refuses an
+    input whose scratch exceeds its fixed array, before any GPU work."""
+    L = eg.lib()
+    cfg = _cfg(eg)
+    p = eg.make_params(canon_map=FAKE, tables=[FAKE] * cfg.J, w_kv=FAKE, conv_w=FAKE)
+
+    def call(cfg, B, T, hidden=FAKE):
+        return L.engram_forward_noalloc(cfg.ref, ctypes.byref(p), FAKE, hidden, B, T, FAKE, None, None,
+                                        None)
+    assert call(_cfg(eg, orders=(3, 2)), 2, 8) == eg.ENGRAM_E_INVALID
+    assert call(cfg, 2, 8, hidden=None) == eg.ENGRAM_E_INVALID
+    assert call(cfg, 0, 8) == eg.ENGRAM_OK
+    per_tok = eg.engram_workspace_size(cfg, 1, 1024, eg.ENGRAM_OP_FORWARD) / 1024
+    too_many = int(eg.ENGRAM_NOALLOC_SCRATCH_BYTES / per_tok) + 4096
+    assert call(cfg, 1, too_many) == eg.ENGRAM_E_SCRATCH
+    assert "scratch" in eg.engram_status_string(eg.ENGRAM_E_SCRATCH)
 
 
 def test_backward_and_hash_validation(eg):
