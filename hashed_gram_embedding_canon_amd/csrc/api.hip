@@ -29,7 +29,10 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Two 128-byte stages: the four-deep ring of 64-byte stages hides more load
 // latency (fewer cycles per tile) but runs at a lower clock under the power
 // limit and measured slower.
-constexpr int32_t kFwdStageBytes = 128;
+#ifndef ENGRAM_FWD_STAGE_BYTES
+#define ENGRAM_FWD_STAGE_BYTES 128
+#endif
+constexpr int32_t kFwdStageBytes = ENGRAM_FWD_STAGE_BYTES;
 #ifndef ENGRAM_GEMM_PERSISTENT
 #define ENGRAM_GEMM_PERSISTENT 1
 #endif

@@ -91,6 +91,53 @@ struct Stage {
 // Spread the next stage's load instructions between MFMA groups (1) or issue
 // them in one burst at the start of a stage (0).
 constexpr bool kSpreadLoads = ENGRAM_GEMM_SPREAD != 0;
+#ifndef ENGRAM_GEMM_LOAD_GROUPS
+#define ENGRAM_GEMM_LOAD_GROUPS 10
+#endif
+// Spread over the first this many MFMA groups of a stage (the later groups
+// issue no loads), so the last load of the next stage has the rest of the
+// stage to land before the wait at its end.  Of the 16 groups of a 128-byte
+// stage, the first 10 measured best at the 27B shape: 1.540 ms per
+// projection against 1.630 ms with one load after every group (8 and 12:
+// 1.549 and 1.543 ms; 6: 1.575 ms).
+constexpr int kLoadGroups = ENGRAM_GEMM_LOAD_GROUPS;
+
+#ifdef ENGRAM_GEMM_TRACE
+// Measurement build only: shader-clock stamps of workgroups 0..31 (wave 0),
+// per tile: start, K loop done, epilogue done; per stage of their second tile.
+constexpr int kTrWG = 32, kTrTiles = 48, kTrStages = 96;
+__device__ uint64_t g_gemm_trace[kTrWG * kTrTiles * 3 + kTrWG * kTrStages + 2];
+#define ENGRAM_TRACE_TILE(which)                                                          \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < kTrWG && it_ < kTrTiles)                         \
+      g_gemm_trace[(blockIdx.x * kTrTiles + it_) * 3 + (which)] = __builtin_readcyclecounter(); \
+  } while (0)
+#define ENGRAM_TRACE_STAGE(k)                                                             \
+  do {                                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < kTrWG && it_ == 1 && (k) < kTrStages)           \
+      g_gemm_trace[kTrWG * kTrTiles * 3 + blockIdx.x * kTrStages + (k)] =                \
+          __builtin_readcyclecounter();                                                   \
+  } while (0)
+// per wave (lane 0), workgroups 0..7, second tile: stamp w of stage k
+constexpr int kTr2WG = 8, kTr2Stages = 24;
+__device__ uint64_t g_gemm_trace2[kTr2WG * kTr2Stages * 4 * 3];
+#define ENGRAM_TRACE_W(k, w)                                                               \
+  do {                                                                                     \
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < kTr2WG && it_ == 1 && (k) < kTr2Stages)   \
+      g_gemm_trace2[((blockIdx.x * kTr2Stages + (k)) * 4 + (threadIdx.x >> 6)) * 3 + (w)] = \
+          __builtin_readcyclecounter();                                                    \
+  } while (0)
+#else
+#define ENGRAM_TRACE_TILE(which) \
+  do {                           \
+  } while (0)
+#define ENGRAM_TRACE_STAGE(k) \
+  do {                        \
+  } while (0)
+#define ENGRAM_TRACE_W(k, w) \
+  do {                       \
+  } while (0)
+#endif
 // what the load slots of a K stage carry
 constexpr int kSlotNext = 0, kSlotNone = 1, kSlotH = 2;  // kSlotH + X: part X of h
 template <int X>
@@ -132,6 +179,8 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int tx = xcd < tiles_m ? (int)((tiles_m - 1 - xcd) / 8 + 1) : 0;  // token tiles of list x
   const int nslots = tx * tiles_f;
   for (int slot = blockIdx.x >> 3; slot < nslots; slot += slot_step) {
+  [[maybe_unused]] const int it_ = (slot - (int)(blockIdx.x >> 3)) / slot_step;
+  ENGRAM_TRACE_TILE(0);
   const int gm = g.group_m;
   const int per_group = gm * tiles_f;
   const int grp = slot / per_group;
@@ -398,9 +447,11 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kSpreadLoads && SLOTS != kSlotNone) {
-          constexpr int PER = (NI + NG - 1) / NG;
+          // load j goes out after group (j * LG) / NI
+          constexpr int LG = kLoadGroups < NG ? kLoadGroups : NG;
+          const int gi = ss * FB + a;
 #pragma unroll
-          for (int j = (ss * FB + a) * PER; j < (ss * FB + a + 1) * PER && j < NI; ++j) {
+          for (int j = (gi * NI + LG - 1) / LG; gi < LG && j < ((gi + 1) * NI + LG - 1) / LG; ++j) {
             if constexpr (SLOTS == kSlotNext)
               issue_one(bA, bB, nla, j);
             else
@@ -463,8 +514,12 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     issue(0, l0);
 #define ENGRAM_STEP(k, SA, SB_, LN, SLOT) \
   {                                       \
+    ENGRAM_TRACE_W(k, 0);                 \
     ENGRAM_WAIT_VM(0);                    \
+    ENGRAM_TRACE_W(k, 1);                 \
     ENGRAM_BARRIER();                     \
+    ENGRAM_TRACE_W(k, 2);                 \
+    ENGRAM_TRACE_STAGE(k);                \
     compute(SA, SB_, (k) + 1, LN, SLOT{}); \
   }
     int kt = 0;
@@ -479,6 +534,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     ENGRAM_STEP(kt + 1, sA1, sB1, l0, LastSlots);
 #undef ENGRAM_STEP
   }
+  ENGRAM_TRACE_TILE(1);
   // stage buffers are free from here on (the st0 half of h may be in flight)
   if (hov) {
     ENGRAM_BARRIER();
@@ -823,6 +879,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // (its global stores may still be in flight)
   ENGRAM_WAIT_VM_LDS(63);
   ENGRAM_BARRIER();
+  ENGRAM_TRACE_TILE(2);
   }  // slot loop
 }
 
@@ -849,6 +906,21 @@ static hipError_t launch_one(const GemmArgs& g0, hipStream_t s) {
     hipLaunchKernelGGL((gemm_kernel<GT, EPI, GATHER, 64>), dim3((unsigned)blocks), dim3(kNT), 0, s, g);
   return hipGetLastError();
 }
+
+#ifdef ENGRAM_GEMM_TRACE
+extern "C" int engram_debug_gemm_trace(uint64_t* out, int n) {
+  const int total = (int)(sizeof(g_gemm_trace) / sizeof(uint64_t));
+  if (n > total) n = total;
+  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(g_gemm_trace), n * sizeof(uint64_t)) != hipSuccess) return -1;
+  return n;
+}
+extern "C" int engram_debug_gemm_trace2(uint64_t* out, int n) {
+  const int total = (int)(sizeof(g_gemm_trace2) / sizeof(uint64_t));
+  if (n > total) n = total;
+  if (hipMemcpyFromSymbol(out, HIP_SYMBOL(g_gemm_trace2), n * sizeof(uint64_t)) != hipSuccess) return -1;
+  return n;
+}
+#endif
 
 bool gemm_supported(GemmType type, const GemmArgs& g, bool gather) {
   const int es = type == GEMM_F32 ? 4 : (type == GEMM_FP8 ? 1 : 2);
