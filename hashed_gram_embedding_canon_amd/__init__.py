@@ -84,6 +84,7 @@ class engram_compact(ctypes.Structure):
         ("ring_pos", _vp),
         ("ring_head", ctypes.c_int64),
         ("ring_hits", ctypes.c_int64),
+        ("consumed_event", _vp),
     ]
 
 
@@ -117,7 +118,7 @@ EXPORTS = ("engram_workspace_size", "engram_status_string", "engram_hash_indices
            "engram_forward_noalloc",
            "engram_backward_table_grad", "engram_backward", "engram_prefetch_plan",
            "engram_shard_requests", "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce",
-           "engram_quantize_fp8",
+           "engram_quantize_fp8", "engram_device_copy",
            "engram_profile_enable",
            "engram_profile_reset", "engram_profile_read")
 
@@ -149,6 +150,7 @@ def lib():
     L.engram_prefetch_plan.argtypes = [C, _vp, _vp, i64, i64, _vp, K, _vp]
     L.engram_shard_requests.argtypes = [C, i32, _vp, i64, _vp, _vp, _vp, _vp, sz, _vp]
     L.engram_quantize_fp8.argtypes = [_vp, i32, i64, i32, _vp, _vp, _vp]
+    L.engram_device_copy.argtypes = [_vp, _vp, sz, _vp]
     L.engram_shard_serve.argtypes = [C, i32, _vp, _vp, i64, _vp, _vp]
     L.engram_shard_grads.argtypes = [C, i32, _vp, _vp, _vp, i64, _vp, _vp, _vp, _vp, sz, _vp]
     L.engram_shard_reduce.argtypes = [C, i32, _vp, _vp, _vp, _vp, i32, _vp]
@@ -162,7 +164,7 @@ def lib():
                  "engram_backward_table_grad",
                  "engram_backward", "engram_prefetch_plan", "engram_shard_requests",
                  "engram_shard_serve", "engram_shard_grads", "engram_shard_reduce",
-                 "engram_quantize_fp8"):
+                 "engram_quantize_fp8", "engram_device_copy"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -361,6 +363,10 @@ def engram_prefetch_plan(cfg: Config, canon_map_host, tokens_host, *, B: int, T:
     _check(lib().engram_prefetch_plan(cfg.ref, _ptr(canon_map_host), _ptr(tokens_host), B, T,
                                       ctypes.cast(tabs, _vp) if tabs is not None else None,
                                       ctypes.byref(plan), ss), "engram_prefetch_plan")
+
+
+def engram_device_copy(dst, src, nbytes: int, *, stream=None):
+    _check(lib().engram_device_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "engram_device_copy")
 
 
 def engram_profile_enable(on: bool):

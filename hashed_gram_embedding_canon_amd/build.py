@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "engram")
 LIB = os.path.join(HERE, "libengram.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["hash_gather.hip", "gemm.hip", "gemm_tn.hip", "gate_conv.hip", "backward.hip", "scatter.hip", "shard.hip", "quant.hip", "api.hip"]
+SOURCES = ["hash_gather.hip", "gemm.hip", "gemm_tn.hip", "gate_conv.hip", "backward.hip", "scatter.hip", "shard.hip", "quant.hip", "stream.hip", "api.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I" + os.path.join(ROOT, "include"),
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-result"]

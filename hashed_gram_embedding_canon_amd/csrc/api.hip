@@ -501,6 +501,13 @@ static engram_status forward_impl(const engram_config* cfg, const engram_params*
     Timed tm("gather_quant", hs);
     if (launch_gather_quant(idx, N, g, s.d_mem, w.e8, w.se, hs) != hipSuccess) return ENGRAM_E_HIP;
   }
+  // compact mode: the plan's device buffers are read for the last time by
+  // the gather (or, fused, by the projection below)
+  auto consumed = [&]() -> bool {
+    return !compact || !compact->consumed_event ||
+           hipEventRecord((hipEvent_t)compact->consumed_event, hs) == hipSuccess;
+  };
+  if (!fused && !consumed()) return ENGRAM_E_HIP;
   {
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
@@ -535,9 +542,12 @@ static engram_status forward_impl(const engram_config* cfg, const engram_params*
     ga.partials = w.partials;
     ga.k_out = saved ? (uint8_t*)saved->k : nullptr;
     ga.v_out = w.v;
-    Timed tm(fused ? "gather_proj_gemm" : (fp8 ? "proj_gemm_fp8" : "proj_gemm"), hs);
-    const GemmType gt = fp8 ? GEMM_FP8 : (s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32);
-    if (launch_gemm(gt, EPI_KV, ga, hs) != hipSuccess) return ENGRAM_E_HIP;
+    {
+      Timed tm(fused ? "gather_proj_gemm" : (fp8 ? "proj_gemm_fp8" : "proj_gemm"), hs);
+      const GemmType gt = fp8 ? GEMM_FP8 : (s.dtype == ENGRAM_BF16 ? GEMM_BF16 : GEMM_F32);
+      if (launch_gemm(gt, EPI_KV, ga, hs) != hipSuccess) return ENGRAM_E_HIP;
+    }
+    if (fused && !consumed()) return ENGRAM_E_HIP;
   }
   {
     GateConvArgs gc;
@@ -955,6 +965,10 @@ engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* cano
   // 4. the inverse map first, then the rows chunk by chunk: gather a chunk
   //    into pinned staging on the host threads, queue its copy, gather the next
   hipStream_t hs = (hipStream_t)side_stream;
+  // the forward on the previous plan may still be about to read the device
+  // buffers these copies rewrite
+  if (plan->consumed_event && hipStreamWaitEvent(hs, (hipEvent_t)plan->consumed_event, 0) != hipSuccess)
+    return ENGRAM_E_HIP;
   if (N > 0 && hipMemcpyAsync(plan->inverse_dev, plan->inverse_host, (size_t)N * J * 4,
                               hipMemcpyHostToDevice, hs) != hipSuccess)
     return ENGRAM_E_HIP;
@@ -1131,6 +1145,15 @@ engram_status engram_shard_reduce(const engram_config* cfg, int32_t G, float* co
     off += counts_host[b];
   }
   return ENGRAM_OK;
+}
+
+engram_status engram_device_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes % 16 != 0) return ENGRAM_E_INVALID;
+  if (bytes == 0) return ENGRAM_OK;
+  if (!dst || !src || !aligned16(dst) || !aligned16(src)) return ENGRAM_E_INVALID;
+  hipStream_t hs = (hipStream_t)stream;
+  Timed tm("device_copy", hs);
+  return hip_status(launch_stream_copy(dst, src, bytes, hs));
 }
 
 void engram_profile_enable(int32_t on) {

@@ -159,6 +159,9 @@ hipError_t launch_shard_serve(const ShardTables& st, const uint32_t* ids, int64_
 hipError_t launch_shard_grad_add(const ShardGrads& sg, const uint32_t* ids, const float* rows,
                                  int64_t n, int32_t dim, hipStream_t s);
 
+// dst[0..bytes) = src[0..bytes) (bytes % 16 == 0, 16-byte aligned buffers)
+hipError_t launch_stream_copy(void* dst, const void* src, uint64_t bytes, hipStream_t s);
+
 // Weight gradients dW[i][j] = sum_t X[t][i] Y[t][j] over token-major operands.
 constexpr int kTnPadTokens = 64;  // X rows are padded to, and chunks are, multiples of this
 struct GemmTnArgs {

@@ -1,0 +1,36 @@
+// Plain device-to-device copy: the achievable-bandwidth reference that the
+// memory-bound kernels of the path are compared with (each lane moves 16-byte
+// pieces, four loads in flight, then four stores; one pass over the buffer).
+#include "kernels.h"
+
+namespace engram {
+
+constexpr int kCopyPer = 4;
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restrict__ src,
+                                                          u32x4* __restrict__ dst, uint64_t n16) {
+  const uint64_t base = (uint64_t)blockIdx.x * (256 * kCopyPer) + threadIdx.x;
+  u32x4 v[kCopyPer];
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const uint64_t i = base + (uint64_t)u * 256;
+    if (i < n16) v[u] = src[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const uint64_t i = base + (uint64_t)u * 256;
+    if (i < n16) dst[i] = v[u];
+  }
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, uint64_t bytes, hipStream_t s) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const uint64_t blocks = (n16 + 256 * kCopyPer - 1) / (256 * kCopyPer);
+  if (blocks >= (uint64_t(1) << 32)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace engram

@@ -178,14 +178,21 @@ typedef struct {
    * or of the next one can overwrite them, reserves ring positions from
    * ring_head on for the rest, and leaves only those in counts, uniq_host
    * and total_rows; the copying call moves just them.  Each plan must be
-   * copied before the next one is made.  One forward may read the ring while
-   * the next plan copies; a third must wait for that forward. */
+   * copied before the next one is made.  A forward on plan k and the copies
+   * of plan k+1 may be queued together only with consumed_event (below):
+   * the copies rewrite inverse_dev, and without the ring rows_dev too. */
   int64_t ring_rows;      /* R >= 2 * capacity_rows, < 2^31; rows_dev holds R rows */
   int64_t* ring_pos;      /* host [sum_j M_j]: ring position (a count of appended rows) where
                              each table row was last copied, -1 = none; the caller sets all
                              to -1 before the first call and keeps it with the ring */
   int64_t ring_head;      /* in/out: rows appended to the ring so far */
   int64_t ring_hits;      /* out: distinct rows of the last planning call found in the ring */
+  void* consumed_event;   /* NULL, or a hipEvent_t that orders the next plan's copies after
+                             this plan's forward: a compact-mode engram_forward records it on
+                             its stream once it has read rows_dev and inverse_dev for the last
+                             time, and the copies of engram_prefetch_plan wait for it on the
+                             side stream.  With it a forward on plan k may overlap the call
+                             that copies plan k+1. */
 } engram_compact;
 
 /* engram_compact.flags */
@@ -430,6 +437,15 @@ engram_status engram_shard_grads(const engram_config* cfg, int32_t G, const int6
 engram_status engram_shard_reduce(const engram_config* cfg, int32_t G, float* const* shard_grads,
                                   const uint32_t* ids, const float* rows,
                                   const int64_t* counts_host, int32_t nblocks, void* stream);
+
+/*
+ * Measurement reference: a plain device-to-device copy of bytes (a multiple
+ * of 16; both buffers 16-byte aligned, not overlapping) queued on stream.
+ * Its rate is the achievable HBM bandwidth that the memory-bound kernels are
+ * compared with, beside the 8 TB/s peak.  ENGRAM_E_INVALID for bad sizes or
+ * pointers.
+ */
+engram_status engram_device_copy(void* dst, const void* src, size_t bytes, void* stream);
 
 /*
  * Kernel timing for measurement: while enabled, every kernel the library

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(eg):
     names = _declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     L = ctypes.CDLL(eg.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -292,6 +292,14 @@ def test_shard_validation(eg):
     big = _cfg(eg, table_rows=np.array([(1 << 27) + 1] * 8, np.int64))
     assert L.engram_shard_serve(big.ref, 1, FAKE, FAKE, 4, FAKE, None) == eg.ENGRAM_E_UNSUPPORTED
     assert eg.engram_workspace_size(cfg, 2, 100, eg.ENGRAM_OP_SHARD) > 0
+
+
+def test_device_copy_validation(eg):
+    L = eg.lib()
+    assert L.engram_device_copy(FAKE, FAKE + 16, 24, None) == eg.ENGRAM_E_INVALID  # not 16-byte pieces
+    assert L.engram_device_copy(FAKE + 8, FAKE, 32, None) == eg.ENGRAM_E_INVALID   # misaligned
+    assert L.engram_device_copy(None, FAKE, 32, None) == eg.ENGRAM_E_INVALID
+    assert L.engram_device_copy(FAKE, FAKE, 0, None) == eg.ENGRAM_OK
 
 
 def test_profile_api_without_launches(eg):

@@ -100,7 +100,6 @@ def test_engram27b_table_grads_sampled(torch, oracle_lib):
     sparse = dp.backward(bufs, dy, eg.ENGRAM_GRAD_SORTED_SPARSE)
     torch.cuda.synchronize()
     keys, rows = _sparse_to_dict(sparse, wl.dim)
-    del sparse
     p = H.oracle_problem(inp)
     idx = p.hash()
     assert np.array_equal(bufs["idx"].cpu().numpy(), idx)
@@ -126,11 +125,43 @@ def test_engram27b_table_grads_sampled(torch, oracle_lib):
     err = H.rel_l2(got, ref)
     print(f"  rel L2 = {err:.3e}", flush=True)
     assert err <= 1e-3, err
-    # the atomic variant agrees with the sorted one on the same rows
+    # rows hit once or twice, under a bound of their own: the heavy segments
+    # above dominate a pooled norm, so an error confined to the light rows
+    # (most rows of a Zipf stream) would hide there
+    rng_pick = synth.u64_stream(22, 4096)
+    light = []
+    for hits, want_n in ((1, 384), (2, 256)):
+        cand = uk[cnt == hits]
+        sel_i = np.unique(rng_pick % np.uint64(len(cand)))[:want_n]
+        light.append(cand[sel_i.astype(np.int64)])
+    light = np.concatenate(light)
+    lj = (light >> 32).astype(np.int32)
+    lr = (light & 0xFFFFFFFF).astype(np.int32)
+    ref_l, npos_l = p.table_grad_rows(inp.dy, idx, lj, lr)
+    got_l = np.stack([rows[key_pos[int(k)]] for k in light])
+    err_l = H.rel_l2(got_l, ref_l)
+    worst = max(H.rel_l2(got_l[i], ref_l[i]) for i in range(len(light)))
+    print(f"  {len(light)} single/double-hit rows ({npos_l} positions): rel L2 = {err_l:.3e}, "
+          f"worst row {worst:.3e}", flush=True)
+    assert len(light) >= 512 and err_l <= 1e-3, err_l
+    # the atomic variant agrees with the sorted one on every key (on the GPU)
     dense = dp.backward(bufs, dy, eg.ENGRAM_GRAD_ATOMIC_DENSE)["dense"]
     torch.cuda.synchronize()
-    got_a = np.stack([dense[int(j)][int(r)].cpu().numpy().astype(np.float64) for j, r in zip(rj, rr)])
-    assert H.rel_l2(got_a, got) <= 1e-3
+    n = int(sparse["count"].item())
+    skeys = sparse["keys"][:n]
+    srows = sparse["rows"][:n]
+    num = torch.zeros((), dtype=torch.float64, device="cuda")
+    den = torch.zeros((), dtype=torch.float64, device="cuda")
+    for j in range(wl.J):
+        m = (skeys >> 32) == j
+        r = (skeys[m] & 0xFFFFFFFF).long()
+        a = dense[j][r].double()
+        b = srows[m].double()
+        num += ((a - b) ** 2).sum()
+        den += (b ** 2).sum()
+    err_all = float((num / den).sqrt())
+    print(f"  atomic vs sorted over all {n} keys: rel L2 = {err_all:.3e}", flush=True)
+    assert err_all <= 1e-3, err_all
 
 
 def test_training_backward_concurrent_streams(torch):
@@ -149,21 +180,23 @@ def test_training_backward_concurrent_streams(torch):
 
     def run(streams):
         ws = [torch.empty(n_ws, dtype=torch.uint8, device="cuda") for _ in streams]
-        outs = []
-        ev = torch.cuda.Event()
-        ev.record()
-        for st in streams:
-            st.wait_event(ev)
-        for b in range(dp.B):
-            rows = slice(b * T, (b + 1) * T)
-            o = {"keys": torch.empty(T * J, dtype=torch.int64, device="cuda"),
+        # every output exists (and count is zeroed, a kernel on the default
+        # stream) before the event that the side streams wait for
+        outs = [{"keys": torch.empty(T * J, dtype=torch.int64, device="cuda"),
                  "rows": torch.empty(T * J, D, dtype=torch.float32, device="cuda"),
                  "count": torch.zeros(1, dtype=torch.int64, device="cuda"),
                  "w_kv": torch.empty(2 * d, wl.d_mem, dtype=torch.float32, device="cuda"),
                  "conv_w": torch.empty(d, wl.taps, dtype=torch.float32, device="cuda"),
                  "gamma_q": torch.empty(d, dtype=torch.float32, device="cuda"),
                  "gamma_k": torch.empty(d, dtype=torch.float32, device="cuda"),
-                 "hidden": torch.empty(1, T, d, dtype=dp.tdtype, device="cuda")}
+                 "hidden": torch.empty(1, T, d, dtype=dp.tdtype, device="cuda")} for _ in range(dp.B)]
+        ev = torch.cuda.Event()
+        ev.record()
+        for st in streams:
+            st.wait_event(ev)
+        for b in range(dp.B):
+            rows = slice(b * T, (b + 1) * T)
+            o = outs[b]
             tg = eg.engram_table_grad()
             tg.mode = eg.ENGRAM_GRAD_SORTED_SPARSE
             tg.keys, tg.rows, tg.count = o["keys"].data_ptr(), o["rows"].data_ptr(), o["count"].data_ptr()
@@ -172,7 +205,6 @@ def test_training_backward_concurrent_streams(torch):
             eg.engram_backward(dp.cfg, dp.params, dp.hidden[b:b + 1], dy[b:b + 1], B=1, T=T, saved=sv,
                                table_out=tg, param_out=pg, workspace=ws[b % len(streams)],
                                stream=streams[b % len(streams)])
-            outs.append(o)
         torch.cuda.synchronize()
         return outs
 
