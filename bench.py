@@ -113,6 +113,10 @@ def kernel_key(name: str) -> str:
         return "bwd_gate_conv_params" if targs[2] == "true" else "bwd_gate_conv"
     if "quant_rows_kernel" in base:
         return "quant_w"
+    if "bwd_scale_kernel" in base:
+        return "bwd_scale"
+    if "scale_rows_kernel" in base:
+        return "scale_rows"
     for key in ("hash_gather", "gather_quant", "gate_conv", "gather", "hash", "transpose_w",
                 "atomic_scatter"):
         if f"engram::{key}_kernel" in base:
@@ -297,6 +301,8 @@ def backward_units(wl, N):
     # dv per launch: written once (one branch), or fp32 first / add / last over M launches
     dv = N * d * eg_ if M == 1 else (N * d * (4 + 8 * (M - 2) + 4) + N * d * eg_) / M
     return {
+        # bf16: the per-token fp16 range factors from dy (every branch), v and the stats
+        "bwd_scale": {"bound": "hbm", "bytes": (M + 1) * N * d * es + M * N * 16 + N * 4},
         # dy, v, k, h in; stats; dk out, dv
         "bwd_gate_conv": {"bound": "hbm", "bytes": 4 * N * d * es + N * 16 + N * d * eg_ + dv},
         "transpose_w": {"bound": "hbm", "bytes": (M + 1) * d * dm * (es + eg_)},

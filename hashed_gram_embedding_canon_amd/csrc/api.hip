@@ -264,6 +264,7 @@ size_t forward_ws(const Shape& s, int64_t N, const engram_saved* sv, FwdWs* out,
 }
 
 struct BwdWs {
+  float* scale;    // [N] bf16 io: power of two of each token's fp16 [dk | dv] row
   uint8_t* dkv;    // [round_up(N, 64)][2d]: the weight-gradient GEMM reads whole stages
   uint8_t* wt;
   float* de;
@@ -293,6 +294,7 @@ size_t backward_ws(const Shape& s, int64_t B, int64_t T, BwdWs* out, uint8_t* ba
   };
   BwdWs w{};
   const int64_t cols = (int64_t)(s.M + 1) * s.d;  // [dk of each branch | dv]
+  if (s.dtype == ENGRAM_BF16) w.scale = (float*)take((size_t)N * 4);
   w.dkv = take((size_t)round_pad(N) * cols * eg);
   if (s.M > 1) w.dv_acc = (float*)take((size_t)N * s.d * 4);
   if (table) {
@@ -610,7 +612,11 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
   }
   const bool want_w = pg && pg->w_kv;
   const bool want_sums = pg && (pg->conv_w || pg->gamma_q || pg->gamma_k);
-  const bool need_e = want_w && !(saved && saved->e);
+  const bool bf = s.dtype == ENGRAM_BF16;
+  // dW reads e: gathered again unless saved; with bf16 io each row divided by
+  // its token's scale, into the workspace either way
+  const bool regather = want_w && !(saved && saved->e);
+  const bool need_e = want_w && (regather || bf);
   if (pg) {
     if (s.d_mem % 256 != 0) return ENGRAM_E_UNSUPPORTED;  // whole 256-wide dW tiles
     if (pg->hidden && !aligned16(pg->hidden)) return ENGRAM_E_INVALID;
@@ -624,7 +630,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
         !aligned16(saved->stats) || !aligned16(p->w_kv))
       return ENGRAM_E_INVALID;
     if (want_w && saved->e && !aligned16(saved->e)) return ENGRAM_E_INVALID;
-    if (need_e)
+    if (regather)
       for (int j = 0; j < s.J; ++j)
         if (!p->tables[j] || !aligned16(p->tables[j])) return ENGRAM_E_INVALID;
   }
@@ -633,9 +639,25 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
   BwdWs w;
   backward_ws(s, B, T, &w, (uint8_t*)workspace, out != nullptr, pg != nullptr, need_e);
   hipStream_t hs = (hipStream_t)stream;
-  const bool bf = s.dtype == ENGRAM_BF16;
 
   const int64_t nblk = bwd_blocks(B, T);
+  if (bf && N > 0) {
+    BwdScaleArgs sa;
+    sa.B = B;
+    sa.T = T;
+    sa.d = s.d;
+    sa.taps = s.taps;
+    sa.branches = s.M;
+    sa.dy = (const uint8_t*)dy;
+    sa.v = (const uint8_t*)saved->v;
+    sa.stats = saved->stats;
+    sa.conv_w = p->conv_w;
+    sa.gamma_q = p->gamma_q;
+    sa.gamma_k = p->gamma_k;
+    sa.scale = w.scale;
+    Timed tm("bwd_scale", hs);
+    if (launch_bwd_scale(sa, hs) != hipSuccess) return ENGRAM_E_HIP;
+  }
   const int64_t cols = (int64_t)(s.M + 1) * s.d;
   const size_t act = (size_t)N * s.d * s.es;  // bytes of one branch's [N][d] activations
   // one launch per branch; the shared v's gradient gathers over them
@@ -660,6 +682,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
     ba.branch = m;
     ba.dv_acc = w.dv_acc;
     ba.dv_mode = s.M == 1 ? 0 : (m == 0 ? 1 : (m + 1 < s.M ? 2 : 3));
+    ba.scale = w.scale;
     if (pg) {
       ba.pacc = want_sums ? w.pacc + (size_t)m * nblk * s.d * (s.taps + 1) : nullptr;
       ba.dh = pg->hidden ? (uint8_t*)pg->hidden + m * act : nullptr;
@@ -686,6 +709,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
     ga.stage_bytes = kBwdStageBytes;
     ga.persistent = ENGRAM_GEMM_PERSISTENT;
     ga.c_out = w.de;
+    ga.col_scale = w.scale;
     Timed tm("de_gemm", hs);
     if (launch_gemm(bf ? GEMM_F16 : GEMM_F32, EPI_STORE_F32, ga, hs) != hipSuccess)
       return ENGRAM_E_HIP;
@@ -727,12 +751,18 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
     }
     if (want_w) {
       const uint8_t* e = need_e ? w.e : (const uint8_t*)(saved ? saved->e : nullptr);
-      if (need_e && N > 0) {
+      if (need_e && !regather && N > 0) {
+        Timed tm("scale_rows", hs);
+        if (launch_scale_rows_bf16((const uint8_t*)saved->e, w.scale, N, s.d_mem, w.e, hs) != hipSuccess)
+          return ENGRAM_E_HIP;
+      }
+      if (regather && N > 0) {
         GatherArgs g;
         std::memset(&g, 0, sizeof(g));
         g.J = s.J;
         g.row_chunks = s.D * s.es / 16;
         for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
+        g.row_scale = w.scale;  // bf16: e_t / s_t; fp32: null
         Timed tm("gather", hs);
         if (launch_gather(saved->idx, w.e, N, g, hs) != hipSuccess) return ENGRAM_E_HIP;
       }

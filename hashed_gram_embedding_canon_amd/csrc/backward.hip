@@ -259,7 +259,10 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       dv[c] = alpha * acc;
     }
     pb[pslot] = pd;
+    const float sc = a.scale ? a.scale[row0 + t] : 1.f;  // the token's fp16 range factor
     if constexpr (!MULTI) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dv[c] *= sc;
       st4_grad<BF16>(a.dkv, (row0 + t) * ld + dv_col + f, dv);
     } else {
       floatx4* acc = reinterpret_cast<floatx4*>(a.dv_acc + (row0 + t) * d + f);
@@ -269,10 +272,13 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
         const floatx4 prev = *acc;
 #pragma unroll
         for (int c = 0; c < 4; ++c) dv[c] += prev[c];
-        if (a.dv_mode == kDvAdd)
+        if (a.dv_mode == kDvAdd) {
           *acc = floatx4{dv[0], dv[1], dv[2], dv[3]};
-        else
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) dv[c] *= sc;
           st4_grad<BF16>(a.dkv, (row0 + t) * ld + dv_col + f, dv);
+        }
       }
     }
   };
@@ -344,9 +350,13 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       float hv[4], kv[4], dk[4];
       widen4<BF16>(rh[q], hv);
       widen4<BF16>(rk[q], kv);
+      const float sc = a.scale ? a.scale[row0 + t] : 1.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) dk[c] = ca * gqk[c] * hv[c] - cb * kv[c];
-      st4_grad<BF16>(a.dkv, (row0 + t) * ld + dk_col + f, dk);
+      float dks[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dks[c] = dk[c] * sc;
+      st4_grad<BF16>(a.dkv, (row0 + t) * ld + dk_col + f, dks);
       if constexpr (PARAMS) {
         const float cq = rq * rq * rq * ds * rkk * P * inv_sqrt_d * inv_d;
         float dh[4];
@@ -435,6 +445,157 @@ hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s) {
 }
 
 int64_t bwd_blocks(int64_t B, int64_t T) { return B * ((T + kBwTokens - 1) / kBwTokens); }
+
+// ------------------------------------------------------------- fp16 range
+// The de and dW contractions take [dk_t | dv_t] in fp16, whose range (normal
+// numbers from 2^-14 to 65504) the gradients of a loss can leave at either
+// end.  Each token's row is stored times s_t = 2^E_t, chosen from an upper
+// bound b_t of |dk_t|, |dv_t| so that b_t s_t < 2^14, and the factor is
+// taken out again where it is exact (the de epilogue, e_t / s_t in bf16).
+// The bound follows the chain rule of bwd_gate_conv_kernel, with
+// m_u = max |G_u|, M_t = max_{t <= u <= t+taps-1} m_u, W = max_c sum_i |w[c][i]|
+// and |dz| <= 1.1 |G| (SiLU' lies in (-0.1, 1.1)):
+//   |dvt_t|   <= (1 + 1.1 W) M_t
+//   |dv_t|    <= sum over branches of alpha_t (1 + 1.1 W) M_t
+//   |dalpha_t| <= ||dvt_t||_2 ||v_t||_2 <= sqrt(d) (1 + 1.1 W) M_t ||v_t||_2
+//   |ds_t|    = alpha (1 - alpha) |dalpha_t|
+//   |dk_t|    <= |ds_t| rk (Gamma + rk rq |P| / d), Gamma = max_c |g_q g_k|,
+// using |h| <= ||h||_2 <= sqrt(d) / rq and |k| <= sqrt(d) / rk.
+__device__ inline float pow2_scale_for(float bound) {
+  if (!(bound > 0.f) || !(bound <= 3.0e38f)) return 1.f;
+  // bound < 2^e with e = (biased exponent) - 126 (normal bound); subnormal: e = -125
+  const int ex = (int)((__float_as_uint(bound) >> 23) & 0xFFu);
+  const int e = ex > 0 ? ex - 126 : -125;
+  int E = 14 - e;
+  E = E < -96 ? -96 : (E > 96 ? 96 : E);
+  return __uint_as_float((uint32_t)(127 + E) << 23);
+}
+
+__device__ inline float wave_max_all(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline float wave_sum_all(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+constexpr int kScTok = 64;  // tokens of a sequence per workgroup
+__global__ __launch_bounds__(256) void bwd_scale_kernel(BwdScaleArgs a) {
+  constexpr int kMaxHalo = 7;
+  __shared__ float mx[ENGRAM_MAX_BRANCHES][kScTok + kMaxHalo];
+  __shared__ float vn2[kScTok];
+  __shared__ float red[4][1 + ENGRAM_MAX_BRANCHES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t b = blockIdx.y, t0 = (int64_t)blockIdx.x * kScTok, T = a.T;
+  const int d = a.d, taps = a.taps, NH = taps - 1, M = a.branches;
+  const int64_t N = a.B * T, row0 = b * T;
+  // W and Gamma_m over all features
+  float wl = 0.f, gl[ENGRAM_MAX_BRANCHES];
+  for (int m = 0; m < ENGRAM_MAX_BRANCHES; ++m) gl[m] = 0.f;
+  for (int c = tid; c < d; c += 256) {
+    float sw = 0.f;
+    for (int i = 0; i < taps; ++i) sw += fabsf(a.conv_w[(int64_t)c * taps + i]);
+    wl = fmaxf(wl, sw);
+    for (int m = 0; m < M; ++m) {
+      const float g = (a.gamma_q ? a.gamma_q[(int64_t)m * d + c] : 1.f) *
+                      (a.gamma_k ? a.gamma_k[(int64_t)m * d + c] : 1.f);
+      gl[m] = fmaxf(gl[m], fabsf(g));
+    }
+  }
+  wl = wave_max_all(wl);
+  for (int m = 0; m < M; ++m) gl[m] = wave_max_all(gl[m]);
+  if (lane == 0) {
+    red[wave][0] = wl;
+    for (int m = 0; m < M; ++m) red[wave][1 + m] = gl[m];
+  }
+  // per-token maxima of |G| (with the halo after the block) and sums of v^2
+  const int64_t tend = t0 + kScTok < T ? t0 + kScTok : T;
+  const int64_t hend = t0 + kScTok + NH < T ? t0 + kScTok + NH : T;
+  const int nu = (int)(hend - t0), nv = (int)(tend - t0);
+  const int pieces = d / 8;  // 16-byte pieces of a bf16 row
+  for (int it = wave; it < M * nu + nv; it += 4) {
+    const bool is_g = it < M * nu;
+    const int m = is_g ? it / nu : 0;
+    const int u = is_g ? it - m * nu : it - M * nu;
+    const uint8_t* row = is_g ? a.dy + ((int64_t)m * N + row0 + t0 + u) * d * 2
+                              : a.v + (row0 + t0 + u) * d * 2;
+    float acc = 0.f;
+    for (int p = lane; p < pieces; p += 64) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(row + p * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = __uint_as_float(q[i] << 16), x1 = __uint_as_float(q[i] & 0xFFFF0000u);
+        if (is_g)
+          acc = fmaxf(acc, fmaxf(fabsf(x0), fabsf(x1)));
+        else
+          acc += x0 * x0 + x1 * x1;
+      }
+    }
+    if (is_g) {
+      acc = wave_max_all(acc);
+      if (lane == 0) mx[m][u] = acc;
+    } else {
+      acc = wave_sum_all(acc);
+      if (lane == 0) vn2[u] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid >= nv) return;
+  const float W = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+  const float wf = 1.f + 1.1f * W;
+  const float sqd = sqrtf((float)d), inv_d = 1.f / (float)d;
+  const float vn = sqrtf(vn2[tid]);
+  float dvb = 0.f, dkb = 0.f;
+  for (int m = 0; m < M; ++m) {
+    float Mt = 0.f;
+    for (int i = 0; i <= NH && tid + i < nu; ++i) Mt = fmaxf(Mt, mx[m][tid + i]);
+    const float G = fmaxf(fmaxf(red[0][1 + m], red[1][1 + m]), fmaxf(red[2][1 + m], red[3][1 + m]));
+    const floatx4 st = *reinterpret_cast<const floatx4*>(a.stats + ((int64_t)m * N + row0 + t0 + tid) * 4);
+    const float al = st[0], rq = st[1], rk = st[2], P = st[3];
+    dvb += al * wf * Mt;
+    const float dsb = al * (1.f - al) * sqd * wf * Mt * vn;
+    dkb = fmaxf(dkb, dsb * rk * (G + rk * rq * fabsf(P) * inv_d));
+  }
+  // 1.01: rounding in the kernels' fp32 sums stays far inside the 4x left to 65504
+  a.scale[row0 + t0 + tid] = pow2_scale_for(1.01f * fmaxf(dvb, dkb));
+}
+
+hipError_t launch_bwd_scale(const BwdScaleArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.T == 0) return hipSuccess;
+  if (a.d % 8 != 0 || a.taps < 1 || a.taps > 8 || a.branches < 1 || a.branches > ENGRAM_MAX_BRANCHES)
+    return hipErrorInvalidValue;
+  dim3 grid((unsigned)((a.T + kScTok - 1) / kScTok), (unsigned)a.B);
+  hipLaunchKernelGGL(bwd_scale_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// rows of e divided by their token's scale (a power of two: exact in bf16)
+__global__ __launch_bounds__(256) void scale_rows_kernel(const uint8_t* __restrict__ e,
+                                                         const float* __restrict__ scale,
+                                                         uint64_t pieces, int32_t row_pieces,
+                                                         uint8_t* __restrict__ out) {
+  const uint64_t c = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= pieces) return;
+  const float inv = pow2_inverse(scale[c / (uint64_t)row_pieces]);
+  u32x4 q = *(reinterpret_cast<const u32x4*>(e) + c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q[i] = pack_bf16x2(__uint_as_float(q[i] << 16) * inv, __uint_as_float(q[i] & 0xFFFF0000u) * inv);
+  *(reinterpret_cast<u32x4*>(out) + c) = q;
+}
+
+hipError_t launch_scale_rows_bf16(const uint8_t* e, const float* scale, int64_t N, int32_t cols,
+                                  uint8_t* out, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (cols % 8 != 0) return hipErrorInvalidValue;
+  const uint64_t pieces = (uint64_t)N * (cols / 8);
+  hipLaunchKernelGGL(scale_rows_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, e,
+                     scale, pieces, cols / 8, out);
+  return hipGetLastError();
+}
 
 // ------------------------------------------------------------- parameter sums
 // dst[c][e] = sum of src rows c*64 .. c*64+63 (< rows) in column e, in order

@@ -859,18 +859,21 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       }
     }
   } else {
+    // a column (token) scaled by a power of two in its operand row comes back
+    // to scale here, exactly
 #pragma unroll
     for (int b = 0; b < TB; ++b) {
       const int64_t m = m0 + (wt * TB + b) * 32 + l32;
       if (m < g.M) {
+        const float inv = g.col_scale ? pow2_inverse(g.col_scale[m]) : 1.f;
 #pragma unroll
         for (int a = 0; a < FB; ++a)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int f = f0 + (wf * FB + a) * 32 + q * 8 + lhalf * 4;
             *reinterpret_cast<floatx4*>(g.c_out + m * g.F + f) =
-                floatx4{acc[a][b][q * 4], acc[a][b][q * 4 + 1], acc[a][b][q * 4 + 2],
-                        acc[a][b][q * 4 + 3]};
+                floatx4{acc_read(acc[a][b][q * 4]) * inv, acc_read(acc[a][b][q * 4 + 1]) * inv,
+                        acc_read(acc[a][b][q * 4 + 2]) * inv, acc_read(acc[a][b][q * 4 + 3]) * inv};
           }
       }
     }

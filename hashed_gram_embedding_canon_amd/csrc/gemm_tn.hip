@@ -8,8 +8,10 @@
 // fragments, which hold 8 consecutive K values per lane, are read across the
 // rows with the 16-bit transposing LDS read (ds_read_b64_tr_b16: in each
 // group of 16 lanes, lane 4r+c supplies 4 values of row r and lane j receives
-// column j of the 4 rows; two reads give a lane its 8 K values).  e arrives
-// in bf16 and is widened to fp16 in registers (exact in fp16's normal range).
+// column j of the 4 rows; two reads give a lane its 8 K values).  X arrives
+// in fp16 (each token's row times a power of two that keeps it inside fp16's
+// range) and is rounded to bf16 in registers; Y is e in bf16 with each row
+// divided by the same power of two, so the product needs no other factor.
 // fp32 operands (small shapes) read their 4 K values with 4 LDS reads.
 //
 // Tiles are 256 x 256 outputs per workgroup of 4 wavefronts (128 x 128 each,
@@ -68,12 +70,11 @@ __device__ inline u32x2 read_tr16(const lds_u8* base, uint32_t byte) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// two bf16 (bits in a 32-bit word) -> two fp16, round to nearest even
-__device__ inline uint32_t bf16x2_to_f16x2(uint32_t u) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
+// two fp16 (bits in a 32-bit word) -> two bf16, round to nearest even
+__device__ inline uint32_t f16x2_to_bf16x2(uint32_t u) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  const f2 f = {__uint_as_float(u << 16), __uint_as_float(u & 0xFFFF0000u)};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, h2));
+  const h2 h = __builtin_bit_cast(h2, u);
+  return pack_bf16x2((float)h[0], (float)h[1]);
 }
 
 template <int GT>
@@ -196,18 +197,22 @@ __global__ __launch_bounds__(256, 1) void gemm_tn_kernel(GemmTnArgs g) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) b4[b] = frag(tx + kTnOperand, wt * 128 + b * 32, ss);
   };
-  // bf16 Y is widened to fp16 a fragment at a time, each feeding 4 MFMAs, so
-  // the conversions overlap the matrix pipe instead of preceding it
+  // fp16 X is rounded to bf16 (Y, the bf16 rows of e divided by the tokens'
+  // scales, may lie outside fp16's range) a fragment at a time, each feeding
+  // 4 MFMAs, so the conversions overlap the matrix pipe instead of preceding it
   auto mfma_step = [&](const u32x4* a4, const u32x4* b4) __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      u32x4 y = b4[b];
+    for (int a = 0; a < 4; ++a) {
+      u32x4 x = a4[a];
       if constexpr (GT == GEMM_F16) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) y[c] = bf16x2_to_f16x2(y[c]);
-      }
+        for (int c = 0; c < 4; ++c) x[c] = f16x2_to_bf16x2(x[c]);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) Mma<GT>::run(a4[a], y, acc[a][b]);
+        for (int b = 0; b < 4; ++b) Mma<GEMM_BF16>::run(x, b4[b], acc[a][b]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Mma<GT>::run(x, b4[b], acc[a][b]);
+      }
     }
   };
   if (nst > 0) {

@@ -84,6 +84,19 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
       v[u] = *(reinterpret_cast<const u32x4*>(base_s[j] + row * rc * 16) + part);
     }
   }
+  if (g.row_scale) {  // bf16 rows of token n divided by row_scale[n] (a power of two: exact)
+#pragma unroll
+    for (int u = 0; u < kGatherPer; ++u) {
+      const uint32_t c = c0 + u * 256u;
+      if (c < pieces) {
+        const float inv = pow2_inverse(g.row_scale[c / rc / J]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[u][i] = pack_bf16x2(__uint_as_float(v[u][i] << 16) * inv,
+                                __uint_as_float(v[u][i] & 0xFFFF0000u) * inv);
+      }
+    }
+  }
 #pragma unroll
   for (int u = 0; u < kGatherPer; ++u) {
     const uint32_t c = c0 + u * 256u;

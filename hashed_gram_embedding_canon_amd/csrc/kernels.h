@@ -15,6 +15,7 @@ struct GatherArgs {
   const uint8_t* base[ENGRAM_MAX_TABLES];
   int32_t J;
   int32_t row_chunks;  // row_bytes / 16
+  const float* row_scale;  // launch_gather only: null, or [N] (bf16 rows): e[n] /= row_scale[n]
 };
 hipError_t launch_gather(const int32_t* idx, uint8_t* e, int64_t N, const GatherArgs& g,
                          hipStream_t s);
@@ -52,6 +53,7 @@ struct GemmArgs {
   uint8_t* v_out;      // [M][d]
   // EPI_STORE_F32
   float* c_out;        // [M][F]
+  const float* col_scale;  // null, or [M]: C[m][:] is divided by col_scale[m] (a power of two)
   // B gathered from tables (forward only): B[m][j*D + c] = tables[j][idx[m][j]][c]
   const int32_t* idx;  // [M][J] or null (then B is read as a dense matrix)
   const uint8_t* tables[ENGRAM_MAX_TABLES];
@@ -102,8 +104,34 @@ struct BwdArgs {
                           // sum_t (ds rq rk / sqrt d) h_t k_t (the RMSNorm scales' shared sum)
   uint8_t* dh;            // [N][d] io dtype: the gate's part of dL/dh
   int32_t pad_rows;       // zero rows N .. N+pad_rows-1 of dkv are written too
+  const float* scale;     // [N] power-of-two factor of each token's dkv row, or null (1)
 };
 hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s);
+
+// Per-token power-of-two scale s_t of the fp16 [dk | dv] rows (bf16 io): an
+// upper bound of |dk_t|, |dv_t| from the upstream gradient, v and the saved
+// gate statistics, times s_t, stays below 2^14.
+struct BwdScaleArgs {
+  int64_t B, T;
+  int32_t d, taps, branches;
+  const uint8_t* dy;      // [M][N][d] bf16
+  const uint8_t* v;       // [N][d] bf16
+  const float* stats;     // [M][N][4]
+  const float* conv_w;    // [d][taps]
+  const float* gamma_q;   // [M][d] or null
+  const float* gamma_k;   // [M][d] or null
+  float* scale;           // [N] out
+};
+hipError_t launch_bwd_scale(const BwdScaleArgs& a, hipStream_t s);
+// out[n][:] = rows of e (bf16, [N][cols]) divided by scale[n] (exact: powers of two)
+hipError_t launch_scale_rows_bf16(const uint8_t* e, const float* scale, int64_t N, int32_t cols,
+                                  uint8_t* out, hipStream_t s);
+
+// power-of-two helpers of the backward's per-token scales
+__host__ __device__ inline float pow2_inverse(float s) {
+  // s = 2^E (normal): 2^-E, exactly
+  return __uint_as_float(0x7F000000u - __float_as_uint(s));
+}
 int64_t bwd_blocks(int64_t B, int64_t T);  // workgroups of the backward, rows of pacc
 // pacc -> dconv [d][taps] and the RMSNorm scale gradients dgq = g_k S, dgk =
 // g_q S (each output may be null); tmp holds bwd_param_tmp_floats() floats

@@ -327,8 +327,12 @@ engram_status engram_backward_table_grad(const engram_config* cfg, const engram_
  *   forward over device tables, not a compact plan);
  *   workspace: >= engram_workspace_size(cfg, B, T, ENGRAM_OP_BACKWARD_PARAMS)
  *   when param_out is given, else ENGRAM_OP_BACKWARD.
- * dW_KV takes its operands in fp16 (bf16 io) like the de contraction and sums
- * in fp32 over token chunks, the chunks in a fixed order (deterministic).
+ * With bf16 io the contractions take [dk_t | dv_t] in fp16, each token's
+ * row times a power of two s_t chosen from a bound of its values so that
+ * any scale of dy stays inside fp16's range (the factor comes out exactly:
+ * de_t / s_t; dW_KV from the rows rounded to bf16 and e_t / s_t in bf16).
+ * dW_KV sums in fp32 over token chunks, the chunks in a fixed order
+ * (deterministic).
  * With M branches (the loss is the sum over the branches' outputs): hidden,
  * dy, saved->k and saved->stats hold every branch ([M][...] as in
  * engram_forward); the table, W_V and conv gradients sum the branches;

@@ -3,7 +3,7 @@ the hidden state (dW_KV, conv taps, RMSNorm scales, dh) against the oracle.
 
 Bars: fp32 io computes in fp32 throughout, so relative L2 <= 1e-5.  With
 bf16 io the forward keeps k and v in bf16 (relative rounding up to 2^-9)
-and the weight-gradient contraction takes fp16 operands (2^-11), so a
+and the weight-gradient contraction takes bf16 operands (2^-9), so a
 gradient that is a sum of products of these carries relative errors of a
 few times 2^-9: relative L2 <= 5e-3; dh is stored in bf16 as well, and is
 held to max |err| / max |ref| <= 1e-2.  At the Engram-27B shapes G is
