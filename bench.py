@@ -46,6 +46,9 @@ def kernel_units(wl, N):
         "gather": {"bound": "hbm", "bytes": N * J * 4 + 2 * N * dm * es},
         # hash and gather in one kernel: token ids in, rows in, e out (no indices)
         "hash_gather": {"bound": "hbm", "bytes": N * 4 + 2 * N * dm * es},
+        # the same with rows repeated inside a 16-token tile read once (the
+        # algorithmic bytes count every token's rows, as for hash_gather)
+        "dedup_gather": {"bound": "hbm", "bytes": N * 4 + 2 * N * dm * es},
         "proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * (M + 1) * d, "bytes": proj_bytes},
         # the same projection reading the table rows itself (row gather fused)
         "gather_proj_gemm": {"bound": "mfma", "flops": 2 * N * dm * (M + 1) * d,
@@ -117,8 +120,8 @@ def kernel_key(name: str) -> str:
         return "bwd_scale"
     if "scale_rows_kernel" in base:
         return "scale_rows"
-    for key in ("hash_gather", "gather_quant", "gate_conv", "gather", "hash", "transpose_w",
-                "atomic_scatter"):
+    for key in ("hash_gather", "dedup_gather", "gather_quant", "gate_conv", "gather", "hash",
+                "transpose_w", "atomic_scatter"):
         if f"engram::{key}_kernel" in base:
             return key
     # the per-GPU steps of the sharded exchange
@@ -842,6 +845,10 @@ def main():
     ap.add_argument("--calibration-bytes", type=int, default=1 << 30)
     ap.add_argument("--branches", type=int, default=1,
                     help="M branches sharing the tables and W_V (own W_K, hidden state, gate, Y)")
+    ap.add_argument("--dedup", action="store_true",
+                    help="read rows repeated inside a 16-token gather tile once (ENGRAM_FLAG_GATHER_DEDUP)")
+    ap.add_argument("--token-stream", choices=("zipf", "repeat"), default="zipf",
+                    help="i.i.d. Zipf tokens, or the Zipf stream with local repetition of short segments")
     ap.add_argument("--fp8", action="store_true",
                     help="the projection as one E4M3 matmul (ENGRAM_FLAG_FP8_PROJ); not the headline")
     ap.add_argument("--shard-gpus", type=int, default=8,
@@ -894,7 +901,9 @@ def main():
         f"table params={wl.table_params / 1e9:.2f}B; generating inputs")
     t = time.perf_counter()
     inp = synth.Inputs(wl)
-    flags = (eg.ENGRAM_FLAG_FUSED_GATHER if args.fused_gather else 0) | (eg.ENGRAM_FLAG_FP8_PROJ if args.fp8 else 0)
+    flags = ((eg.ENGRAM_FLAG_FUSED_GATHER if args.fused_gather else 0) |
+             (eg.ENGRAM_FLAG_FP8_PROJ if args.fp8 else 0) |
+             (eg.ENGRAM_FLAG_GATHER_DEDUP if args.dedup else 0))
     dp = H.DeviceProblem(inp, flags=flags)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM after {time.perf_counter() - t:.1f} s")
@@ -905,9 +914,9 @@ def main():
     # one distinct token batch per timed step (consecutive stretches of the
     # seeded Zipf stream), all resident in HBM before timing: a step never
     # finds the previous step's rows in the caches
-    batches = [dp.tokens] + [
-        H.to_dev(synth.zipf_tokens(synth.seed_of(wl.cfg, synth.S_TOKENS), N, wl.vocab, wl.zipf_s,
-                                   offset=k * N).reshape(wl.B, wl.T)) for k in range(1, args.steps)]
+    draw = synth.repeat_tokens if args.token_stream == "repeat" else synth.zipf_tokens
+    batches = [H.to_dev(draw(synth.seed_of(wl.cfg, synth.S_TOKENS), N, wl.vocab, wl.zipf_s,
+                             offset=k * N).reshape(wl.B, wl.T)) for k in range(args.steps)]
 
     def step(i):
         dp.tokens = batches[i % len(batches)]
@@ -960,7 +969,8 @@ def main():
         kernels[name] = ent
     # the counters were taken on the default configuration (one branch, bf16
     # projection, rows gathered first): other configurations report none
-    traffic = traffic_from_profile(wl.name) if wl.branches == 1 and flags == 0 else {}
+    traffic = (traffic_from_profile(wl.name)
+               if wl.branches == 1 and flags == 0 and args.token_stream == "zipf" else {})
     for name, ent in kernels.items():
         if name in traffic:
             ent["counter_bytes"] = int(traffic[name])
@@ -982,7 +992,8 @@ def main():
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                     "traffic": int(traffic[dom]) if dom in traffic else None}
-    mem_names = [k for k in ("hash_gather", "gather", "gather_quant", "gate_conv") if k in prof]
+    mem_names = [k for k in ("hash_gather", "dedup_gather", "gather", "gather_quant", "gate_conv")
+                 if k in prof]
     mem_ms = sum(prof[k][1] / prof[k][0] for k in mem_names)
     mem_bytes = sum(units[k]["bytes"] for k in mem_names)
     es = 2 if wl.dtype == "bf16" else 4
@@ -1018,7 +1029,8 @@ def main():
         "dtype": ("fp8 e4m3 projection, bf16 elsewhere" if args.fp8 else
                   "bf16" if wl.dtype == "bf16" else "f32"),
         "data": "synthetic",
-        "config": {"workload": wl.name, "branches": wl.branches, "row_gather": "fused into projection" if args.fused_gather else "gathered into workspace", "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
+        "config": {"workload": wl.name, "token_stream": args.token_stream,
+                   "gather": "lds dedup" if args.dedup else "plain", "branches": wl.branches, "row_gather": "fused into projection" if args.fused_gather else "gathered into workspace", "batch": wl.B, "seq_len": wl.T, "tables": wl.J,
                    "rows_per_table": list(wl.rows[:1]) + ["..."], "dim": wl.dim,
                    "d_mem": wl.d_mem, "hidden": wl.hidden, "table_params": wl.table_params,
                    "zipf_s": wl.zipf_s, "vocab": wl.vocab, "canon_vocab": wl.canon_vocab},

@@ -24,6 +24,7 @@ ENGRAM_MAX_BRANCHES = 8
 ENGRAM_FLAG_FUSED_GATHER = 1
 ENGRAM_FLAG_FP8_PROJ = 2
 ENGRAM_FLAG_CHECK_IDS = 4
+ENGRAM_FLAG_GATHER_DEDUP = 8
 ENGRAM_PLAN_REUSE = 1
 ENGRAM_GRAD_SORTED_SPARSE, ENGRAM_GRAD_SORTED_DENSE, ENGRAM_GRAD_ATOMIC_DENSE = 0, 1, 2
 ENGRAM_OP_FORWARD, ENGRAM_OP_BACKWARD, ENGRAM_OP_BACKWARD_PARAMS, ENGRAM_OP_SHARD = 0, 1, 2, 3

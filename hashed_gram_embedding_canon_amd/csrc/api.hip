@@ -57,7 +57,8 @@ engram_status check_config(const engram_config* c, Shape* s) {
   if (c->dim < 1 || c->hidden < 1) return ENGRAM_E_INVALID;
   if (c->conv_kernel < 1 || c->conv_kernel > 8) return ENGRAM_E_UNSUPPORTED;
   if (!(c->rms_eps >= 0.f)) return ENGRAM_E_INVALID;
-  if (c->flags & ~(uint32_t)(ENGRAM_FLAG_FUSED_GATHER | ENGRAM_FLAG_FP8_PROJ | ENGRAM_FLAG_CHECK_IDS))
+  if (c->flags & ~(uint32_t)(ENGRAM_FLAG_FUSED_GATHER | ENGRAM_FLAG_FP8_PROJ | ENGRAM_FLAG_CHECK_IDS |
+                             ENGRAM_FLAG_GATHER_DEDUP))
     return ENGRAM_E_INVALID;
   if ((c->flags & ENGRAM_FLAG_CHECK_IDS) && (!c->bad_ids || ((uintptr_t)c->bad_ids & 3u)))
     return ENGRAM_E_INVALID;
@@ -71,6 +72,8 @@ engram_status check_config(const engram_config* c, Shape* s) {
   const int d_mem = J * c->dim;
   if (d_mem % kGemmBF != 0) return ENGRAM_E_UNSUPPORTED;
   if ((c->flags & ENGRAM_FLAG_FP8_PROJ) && d_mem > kQuantMaxDmem) return ENGRAM_E_UNSUPPORTED;
+  if ((c->flags & ENGRAM_FLAG_GATHER_DEDUP) && dedup_gather_lds_bytes(J, c->dim * es / 16) == 0)
+    return ENGRAM_E_UNSUPPORTED;
   if (c->hidden % kGemmBF != 0) return ENGRAM_E_UNSUPPORTED;
   if (c->hidden / (c->dtype == ENGRAM_BF16 ? 8 : 4) > 1024) return ENGRAM_E_UNSUPPORTED;
   int64_t max_rows = 1;
@@ -478,7 +481,12 @@ static engram_status forward_impl(const engram_config* cfg, const engram_params*
     const HashArgs ha = make_hash_args(cfg, s);
     if ((st = id_check_begin(cfg, hs)) != ENGRAM_OK) return st;
     for (int j = 0; j < s.J; ++j) g.base[j] = (const uint8_t*)p->tables[j];
-    if (hash_in_gather) {
+    if (hash_in_gather && (s.flags & ENGRAM_FLAG_GATHER_DEDUP)) {
+      Timed tm("dedup_gather", hs);
+      if (launch_dedup_gather(tokens, p->canon_map, N, (int32_t)T, ha, g, w.e,
+                              saved && saved->idx ? saved->idx : nullptr, hs) != hipSuccess)
+        return ENGRAM_E_HIP;
+    } else if (hash_in_gather) {
       Timed tm("hash_gather", hs);
       if (launch_hash_gather(tokens, p->canon_map, N, (int32_t)T, ha, g, w.e,
                              saved && saved->idx ? saved->idx : nullptr, hs) != hipSuccess)

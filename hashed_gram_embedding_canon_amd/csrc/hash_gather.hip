@@ -183,6 +183,121 @@ hipError_t launch_hash_gather(const int32_t* tokens, const int32_t* canon, int64
   return hipGetLastError();
 }
 
+// Hash + gather with the repeats of a tile served from LDS: a block owns
+// kDdTok consecutive tokens.  It hashes their J indices into LDS, marks each
+// (table, row) pair's first occurrence in the tile as its leader, reads only
+// the leaders' rows from the tables into LDS, and writes every token's pieces
+// of e from there.  N-grams recur in text, often within a few tokens, so a
+// tile can hold the same (table, row) more than once; each such row then
+// costs one read instead of several.
+#ifndef ENGRAM_DEDUP_TOKENS
+#define ENGRAM_DEDUP_TOKENS 16
+#endif
+constexpr int kDdTok = ENGRAM_DEDUP_TOKENS;
+constexpr int kDdPer = 8;  // leader-row loads in flight per thread
+__global__ __launch_bounds__(256) void dedup_gather_kernel(const int32_t* __restrict__ tokens,
+                                                           const int32_t* __restrict__ canon,
+                                                           int64_t N, int32_t T, GatherArgs g,
+                                                           HashArgs a, uint8_t* __restrict__ e,
+                                                           int32_t* __restrict__ idx_out) {
+  extern __shared__ __attribute__((aligned(16))) u32x4 rows_s[];  // [kDdTok * J][rc]
+  __shared__ const uint8_t* base_s[ENGRAM_MAX_TABLES];
+  __shared__ uint32_t c_s[kDdTok + ENGRAM_MAX_ORDERS - 1];
+  __shared__ int32_t key_s[kDdTok * ENGRAM_MAX_TABLES];
+  __shared__ int16_t lead_s[kDdTok * ENGRAM_MAX_TABLES];
+  __shared__ int16_t list_s[kDdTok * ENGRAM_MAX_TABLES];
+  __shared__ int nlead_s;
+  const int tid = threadIdx.x;
+  const int J = g.J, rc = g.row_chunks;
+  const int64_t n0 = (int64_t)blockIdx.x * kDdTok;
+  const int ntok = N - n0 < kDdTok ? (int)(N - n0) : kDdTok;
+  const int H = a.max_order - 1;
+  if (tid < J) base_s[tid] = g.base[tid];
+  if (tid == 0) nlead_s = 0;
+  for (int i = tid; i < ntok + H; i += 256) {
+    const int64_t n = n0 - H + i;
+    c_s[i] = n >= 0 ? canon_of(canon, tokens[n], a, i >= H) : 0u;  // n < 0 is never read
+  }
+  __syncthreads();
+  const int np = ntok * J;  // pairs (token k, table j), q = k * J + j
+  for (int q = tid; q < np; q += 256) {
+    const int k = q / J, j = q - k * J;
+    const int64_t n = n0 + k;
+    const int t = (int)(n % T);
+    uint32_t c[ENGRAM_MAX_ORDERS];
+#pragma unroll
+    for (int i = 0; i < ENGRAM_MAX_ORDERS; ++i)
+      c[i] = i < a.max_order ? (t - i < 0 ? (uint32_t)a.pad_id : c_s[k + H - i]) : 0u;
+    const int32_t r = (int32_t)hash_one(a, j, a.orders[j / a.heads], c);
+    key_s[q] = r;
+    if (idx_out) idx_out[n * J + j] = r;
+  }
+  __syncthreads();
+  // leader of pair (k, j): the first token of the tile with the same row of table j
+  for (int q = tid; q < np; q += 256) {
+    const int k = q / J, j = q - k * J;
+    const int32_t key = key_s[q];
+    int kl = k;
+    for (int k2 = 0; k2 < k; ++k2)
+      if (key_s[k2 * J + j] == key) {
+        kl = k2;
+        break;
+      }
+    lead_s[q] = (int16_t)(kl * J + j);
+    if (kl == k) list_s[atomicAdd(&nlead_s, 1)] = (int16_t)q;
+  }
+  __syncthreads();
+  // the leaders' rows into LDS, kDdPer loads in flight per thread
+  const int nl = nlead_s;
+  for (int c0 = tid; c0 < nl * rc; c0 += 256 * kDdPer) {
+    u32x4 v[kDdPer];
+    int dst[kDdPer];
+#pragma unroll
+    for (int u = 0; u < kDdPer; ++u) {
+      const int c = c0 + u * 256;
+      dst[u] = -1;
+      if (c < nl * rc) {
+        const int li = c / rc, part = c - li * rc;
+        const int q = list_s[li];
+        const int j = q % J;
+        v[u] = *(reinterpret_cast<const u32x4*>(base_s[j] + (int64_t)key_s[q] * rc * 16) + part);
+        dst[u] = q * rc + part;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDdPer; ++u)
+      if (dst[u] >= 0) rows_s[dst[u]] = v[u];
+  }
+  __syncthreads();
+  // every pair's pieces of e from its leader's row
+  u32x4* eo = reinterpret_cast<u32x4*>(e) + (uint64_t)n0 * J * rc;
+  for (int c = tid; c < np * rc; c += 256) {
+    const int q = c / rc, part = c - q * rc;
+    eo[c] = rows_s[lead_s[q] * rc + part];
+  }
+}
+
+hipError_t launch_dedup_gather(const int32_t* tokens, const int32_t* canon, int64_t N, int32_t T,
+                               const HashArgs& a, const GatherArgs& g, uint8_t* e, int32_t* idx_out,
+                               hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  const size_t lds = dedup_gather_lds_bytes(g.J, g.row_chunks);
+  if (lds == 0) return hipErrorInvalidValue;
+  const int64_t blocks = (N + kDdTok - 1) / kDdTok;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const hipError_t at = hipFuncSetAttribute((const void*)dedup_gather_kernel,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (at != hipSuccess) return at;
+  hipLaunchKernelGGL(dedup_gather_kernel, dim3((unsigned)blocks), dim3(256), lds, s, tokens, canon,
+                     N, T, g, a, e, idx_out);
+  return hipGetLastError();
+}
+
+size_t dedup_gather_lds_bytes(int32_t J, int32_t row_chunks) {
+  const size_t b = (size_t)kDdTok * J * row_chunks * 16;
+  return b <= (size_t(64) << 10) ? b : 0;  // the rest of the 160 KB is the block's own arrays
+}
+
 hipError_t launch_gather(const int32_t* idx, uint8_t* e, int64_t N, const GatherArgs& g,
                          hipStream_t s) {
   if (N == 0) return hipSuccess;

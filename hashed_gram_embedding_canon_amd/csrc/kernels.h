@@ -19,6 +19,12 @@ struct GatherArgs {
 };
 hipError_t launch_gather(const int32_t* idx, uint8_t* e, int64_t N, const GatherArgs& g,
                          hipStream_t s);
+// hash + gather with the rows repeated inside a tile of tokens read once (LDS);
+// lds bytes per block, 0 when a tile's rows exceed what it may stage
+size_t dedup_gather_lds_bytes(int32_t J, int32_t row_chunks);
+hipError_t launch_dedup_gather(const int32_t* tokens, const int32_t* canon, int64_t N, int32_t T,
+                               const HashArgs& a, const GatherArgs& g, uint8_t* e, int32_t* idx_out,
+                               hipStream_t s);
 // hash + gather in one launch; idx_out [N][J] (may be null) receives the indices
 hipError_t launch_hash_gather(const int32_t* tokens, const int32_t* canon, int64_t N, int32_t T,
                               const HashArgs& a, const GatherArgs& g, uint8_t* e, int32_t* idx_out,

@@ -100,7 +100,16 @@ enum {
    * returns ENGRAM_E_INVALID when *bad_ids > 0.  The outputs are still
    * written in full (with pad_id in place of the bad ids).  Costs one
    * stream synchronisation per call; compact-mode forwards read no ids. */
-  ENGRAM_FLAG_CHECK_IDS = 4u
+  ENGRAM_FLAG_CHECK_IDS = 4u,
+  /* Forward over device tables: the hash + gather reads a (table, row) that
+   * repeats inside a tile of 16 consecutive tokens once, into LDS, and writes
+   * every token's copy from there ("DeepSeek AI II", system-efficiency part:
+   * N-gram use is Zipf-distributed, so a few rows take most of the reads).
+   * Same results as without the flag.  ENGRAM_E_UNSUPPORTED when a tile's
+   * rows (16 * J * D * sizeof(dtype) bytes) exceed 64 KB.  Ignored in
+   * compact mode (the plan already holds each row once), with
+   * ENGRAM_FLAG_FUSED_GATHER and with ENGRAM_FLAG_FP8_PROJ. */
+  ENGRAM_FLAG_GATHER_DEDUP = 8u
 };
 
 /* Shapes and addressing constants.  Host struct, read during the call only. */

@@ -103,6 +103,27 @@ def zipf_tokens(seed: int, n: int, vocab: int, s: float, offset: int = 0) -> np.
     return out
 
 
+def repeat_tokens(seed: int, n: int, vocab: int, s: float, offset: int = 0, p_copy: float = 0.5,
+                  seg: int = 4, reach: int = 8) -> np.ndarray:
+    """A token stream with local repetition: the Zipf stream cut into segments
+    of `seg` tokens, each of which (with probability p_copy) is replaced by a
+    copy of one of the `reach` segments before it, so short N-grams recur
+    within a few dozen tokens, as phrases do in text.  Segments are counted
+    from the stream start, so consecutive batches (offsets that are multiples
+    of seg) continue one stream."""
+    assert offset % seg == 0
+    out = zipf_tokens(seed, n, vocab, s, offset=offset)
+    nseg = n // seg
+    s0 = offset // seg
+    u = unit_stream(seed + 7919, nseg, offset=s0)
+    r = (u64_stream(seed + 7920, nseg, offset=s0) % np.uint64(reach)).astype(np.int64)
+    for i in range(nseg):
+        src = i - 1 - int(r[i])
+        if u[i] < p_copy and src >= 0:
+            out[i * seg:(i + 1) * seg] = out[src * seg:(src + 1) * seg]
+    return out
+
+
 def random_surjection(seed: int, vocab: int, canon_vocab: int) -> np.ndarray:
     """Seeded surjection [0,vocab) -> [0,canon_vocab).
 

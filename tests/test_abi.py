@@ -122,7 +122,14 @@ def test_id_check_validation(eg):
     assert eg.engram_workspace_size(ok, 2, 8, eg.ENGRAM_OP_FORWARD) == \
         eg.engram_workspace_size(_cfg(eg), 2, 8, eg.ENGRAM_OP_FORWARD)
     assert _fwd(eg, ok, B=0) == eg.ENGRAM_OK  # no tokens: nothing queued, no sync
-    assert _fwd(eg, _cfg(eg, flags=8)) == eg.ENGRAM_E_INVALID  # unknown flag bit
+    assert _fwd(eg, _cfg(eg, flags=16)) == eg.ENGRAM_E_INVALID  # unknown flag bit
+
+
+def test_gather_dedup_shape_limit(eg):
+    """The LDS dedup gather stages a 16-token tile's rows (at most 64 KB)."""
+    dd = eg.ENGRAM_FLAG_GATHER_DEDUP
+    assert eg.engram_workspace_size(_cfg(eg, flags=dd), 2, 8, eg.ENGRAM_OP_FORWARD) > 0  # 16 KB
+    assert _fwd(eg, _cfg(eg, flags=dd, dim=256)) == eg.ENGRAM_E_UNSUPPORTED  # 128 KB
 
 
 def test_noalloc_forward_host_checks(eg):
