@@ -101,6 +101,18 @@ constexpr bool kSpreadLoads = ENGRAM_GEMM_SPREAD != 0;
 // projection against 1.630 ms with one load after every group (8 and 12:
 // 1.549 and 1.543 ms; 6: 1.575 ms).
 constexpr int kLoadGroups = ENGRAM_GEMM_LOAD_GROUPS;
+#ifndef ENGRAM_GEMM_EARLY_BARRIER
+#define ENGRAM_GEMM_EARLY_BARRIER 1
+#endif
+#ifndef ENGRAM_GEMM_LATE
+#define ENGRAM_GEMM_LATE 6
+#endif
+#ifndef ENGRAM_GEMM_EARLY_PER
+#define ENGRAM_GEMM_EARLY_PER 2
+#endif
+#ifndef ENGRAM_GEMM_H1_LATE
+#define ENGRAM_GEMM_H1_LATE 0
+#endif
 
 #ifdef ENGRAM_GEMM_TRACE
 // Measurement build only: shader-clock stamps of workgroups 0..31 (wave 0),
@@ -465,6 +477,117 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   using SlotNext = std::integral_constant<int, kSlotNext>;
   using SlotNone = std::integral_constant<int, kSlotNone>;
 
+  // ---- early-barrier schedule (two 128-byte stages, bf16 / fp16 operands).
+  // Stage k's barrier sits after the first group of its last K step instead
+  // of before its first: by then every wave has read all of stage k's
+  // fragments (their reads ended with the step before), so stage k's buffer
+  // is free, and stage k+1's data has landed.  The rest of stage k then
+  // reads stage k+1's step-0 fragments while its last MFMAs run (the MFMAs of
+  // a stage start without an LDS wait) and issues the first kLate loads of
+  // stage k+2 into the freed buffer; stage k+1 issues the other loads of
+  // stage k+2 in its first groups.  Buffer k % 2 holds stage k, and after the
+  // last stage the virtual stages nk, nk+1 are the two parts of the h tile
+  // (value tiles and the de contraction: placeholders or nothing).
+  constexpr bool kEarlyBarrier =
+      ENGRAM_GEMM_EARLY_BARRIER && NS == 2 && (GT == GEMM_BF16 || GT == GEMM_F16) && !GATHER;
+  constexpr int kLate = ENGRAM_GEMM_LATE;  // slots issued after the barrier two stages ahead
+  constexpr int kBarGroup = 12;  // the barrier follows this group (first of step 3)
+  Frag af2[2][FB], bf2[2][TB];   // fragments carried across stages
+  auto slot_issue = [&](auto kSlots, const void* bA, const void* bB, uint32_t la, int j)
+                        __attribute__((always_inline)) {
+    constexpr int SL = decltype(kSlots)::value;
+    if constexpr (SL == kSlotNext)
+      issue_one(bA, bB, la, j);
+    else if constexpr (SL >= kSlotH)
+      issue_h(SL - kSlotH, j);
+  };
+  // sa, sb: this stage; na, nb: the next one (step-0 fragments, with kNext);
+  // kEarlyS: slots kLate.. of the stage after this one (ekl at ela) in
+  // groups 0..4; kLateS: slots 0..kLate-1 (all with kLateAll) of the stage
+  // two ahead (lkl at lla) after the barrier.
+  auto compute2 = [&](const uint8_t* sa, const uint8_t* sb, const uint8_t* na, const uint8_t* nb,
+                      auto kEarlyS, int ekl, uint32_t ela, auto kLateS, int lkl, uint32_t lla,
+                      auto kNext, auto kLateAll, [[maybe_unused]] int kid)
+                      __attribute__((always_inline)) {
+    constexpr int ESL = decltype(kEarlyS)::value;
+    constexpr int LSL = decltype(kLateS)::value;
+    constexpr bool NEXT = decltype(kNext)::value;
+    constexpr int NI = 2 * NL;
+    constexpr int KS = S::kKSteps;
+    constexpr int NLATE = decltype(kLateAll)::value ? NI : kLate;
+    constexpr int NAFTER = KS * FB - 1 - kBarGroup;  // groups after the barrier
+    static_assert(KS == 4 && FB == 4 && NI == 16 && NAFTER == 3, "early-barrier stage shape");
+    // every early slot goes out before the barrier that waits for it
+    static_assert(kLate + ENGRAM_GEMM_EARLY_PER * (kBarGroup + 1) >= NI, "early loads after the barrier");
+    const void* ebA = ESL == kSlotNext ? stage_base(tileA, ekl) : nullptr;
+    const void* ebB = ESL == kSlotNext ? stage_base(tileB, ekl) : nullptr;
+    const void* lbA = LSL == kSlotNext ? stage_base(tileA, lkl) : nullptr;
+    const void* lbB = LSL == kSlotNext ? stage_base(tileB, lkl) : nullptr;
+#pragma unroll
+    for (int ss = 0; ss < KS; ++ss) {
+      const int cur = ss & 1, nx = (ss + 1) & 1;
+#pragma unroll
+      for (int a = 0; a < FB; ++a) {
+        const int gi = ss * FB + a;
+#pragma unroll
+        for (int b = 0; b < TB; ++b) Mma<GT>::run(af2[cur][a], bf2[cur][b], acc[a][b]);
+        if (ss + 1 < KS) {
+          frag_one(sa, sb, ss + 1, a, af2[nx][a], bf2[nx][a]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, TB / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        } else if (NEXT && gi > kBarGroup) {
+          // next stage's step 0: pairs 0 and 1 in group 13, 2 and 3 in 14 and 15
+          if (gi == kBarGroup + 1) {
+            frag_one(na, nb, 0, 0, af2[nx][0], bf2[nx][0]);
+            frag_one(na, nb, 0, 1, af2[nx][1], bf2[nx][1]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, TB - 1, 0);
+          } else {
+            const int pr = gi - kBarGroup;
+            frag_one(na, nb, 0, pr, af2[nx][pr], bf2[nx][pr]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, TB - 1, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, TB, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ESL != kSlotNone) {
+          constexpr int EP = ENGRAM_GEMM_EARLY_PER;  // early slots per group
+#pragma unroll
+          for (int j = kLate + EP * gi; j < kLate + EP * (gi + 1) && j < NI; ++j)
+            slot_issue(kEarlyS, ebA, ebB, ela, j);
+        }
+        if constexpr (LSL != kSlotNone) {
+          if (gi > kBarGroup) {
+            const int g3 = gi - kBarGroup - 1;
+#pragma unroll
+            for (int j = g3 * NLATE / NAFTER; j < (g3 + 1) * NLATE / NAFTER; ++j)
+              slot_issue(kLateS, lbA, lbB, lla, j);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (gi == kBarGroup) {
+          // this wave's loads of the next stage and its reads of this one are
+          // done; then every wave's are
+          ENGRAM_TRACE_W(kid, 0);
+          if constexpr (NEXT)
+            ENGRAM_WAIT_VM_LDS(0);
+          else
+            ENGRAM_WAIT_VM_LDS(63);
+          ENGRAM_TRACE_W(kid, 1);
+          ENGRAM_BARRIER();
+          ENGRAM_TRACE_W(kid, 2);
+        }
+      }
+    }
+  };
+
   // ---- ring: stage k lives in buffer k % NS; loads run NS-1 stages ahead.
   // Each wave issues 2*NL loads per stage, so "stage k landed" is
   // vmcnt <= 2*NL * (stages issued after k).  nk is a multiple of NS
@@ -475,7 +598,37 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   uint8_t* const sA1 = st1;
   uint8_t* const sB1 = st1 + kTS;
   const uint32_t l0 = lds_addr(st0), l1 = lds_addr(st1);
-  if constexpr (NS == 4) {
+  if constexpr (kEarlyBarrier) {
+    using True_ = std::true_type;
+    using False_ = std::false_type;
+    issue(0, l0);
+    {
+      const void* bA = stage_base(tileA, 1);
+      const void* bB = stage_base(tileB, 1);
+#pragma unroll
+      for (int j = 0; j < kLate; ++j) issue_one(bA, bB, l1, j);
+    }
+    ENGRAM_WAIT_VM(kLate);  // this wave's stage-0 loads landed
+    ENGRAM_BARRIER();
+    frag(sA0, sB0, 0, af2[0], bf2[0]);
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+      compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, SlotNext{}, kt + 2, l0, True_{}, False_{},
+               kt);
+      compute2(sA1, sB1, sA0, sB0, SlotNext{}, kt + 2, l0, SlotNext{}, kt + 3, l1, True_{}, False_{},
+               kt + 1);
+    }
+    // part 0 of the h tile (placeholder reads in value tiles) as stage nk;
+    // part 1 goes out after the loop, where a burst of loads holds up no MFMA
+    using H0 = std::conditional_t<kHOverlap, SlotHPart<0>, SlotNone>;
+#if ENGRAM_GEMM_H1_LATE
+    using H1 = std::conditional_t<kHOverlap, SlotHPart<1>, SlotNone>;
+#else
+    using H1 = SlotNone;
+#endif
+    compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, H0{}, 0, 0u, True_{}, False_{}, kt);
+    compute2(sA1, sB1, sA1, sB1, H0{}, 0, 0u, H1{}, 0, 0u, False_{}, True_{}, kt + 1);
+  } else if constexpr (NS == 4) {
     uint8_t* const sA2 = st2;
     uint8_t* const sB2 = st2 + kTS;
     uint8_t* const sA3 = st3;
@@ -557,8 +710,10 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     if (key_tile) {
       if (hov) {
         // the last part of h (the others went out in the last K stages)
+        if constexpr (!kEarlyBarrier || !ENGRAM_GEMM_H1_LATE) {
 #pragma unroll
-        for (int j = 0; j < 2 * NL; ++j) issue_h(NS - 1, j);
+          for (int j = 0; j < 2 * NL; ++j) issue_h(NS - 1, j);
+        }
       } else {
         // whole h tile: instruction i of wave w fills rows t0, t0+1 (t0 = 2(32w+i))
 #pragma unroll 4
