@@ -16,12 +16,29 @@
 namespace engram {
 
 constexpr int kGcTokens = 64;   // R (32 and 128 measured slower)
+// 1: issue the first v loads before the gates are formed (measured 45 %
+// slower; kept off)
+#ifndef ENGRAM_GC_EARLY
+#define ENGRAM_GC_EARLY 0
+#endif
+// Non-temporal stores of Y (bit 2; bit 1 would make the v loads
+// non-temporal): Y is not read again here, and keeping it out of the 256 MB
+// Infinity Cache leaves the table rows of the Zipf head there for the next
+// batch's gather (0.170 -> 0.150 ms on distinct batches) at the cost of 3 %
+// in this kernel (0.286 -> 0.294 ms).
+#ifndef ENGRAM_GC_NT
+#define ENGRAM_GC_NT 2
+#endif
 constexpr int kMaxTaps = 8;
 
 // raw 16 bytes of VEC features (8 bf16 or 4 fp32), widened at use
 template <int VEC, bool BF16>
 __device__ inline u32x4 load_raw(const uint8_t* base, int64_t elem) {
-  return *reinterpret_cast<const u32x4*>(base + elem * (BF16 ? 2 : 4));
+  const u32x4* p = reinterpret_cast<const u32x4*>(base + elem * (BF16 ? 2 : 4));
+  if constexpr ((ENGRAM_GC_NT & 1) != 0)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
 }
 template <int VEC, bool BF16>
 __device__ inline void widen(const u32x4 u, float* out) {
@@ -46,13 +63,20 @@ __device__ inline void store_vec(uint8_t* base, int64_t elem, const float* v) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       u[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(base + elem * 2) = u;
+    u32x4* p = reinterpret_cast<u32x4*>(base + elem * 2);
+    if constexpr ((ENGRAM_GC_NT & 2) != 0)
+      __builtin_nontemporal_store(u, p);
+    else
+      *p = u;
   } else {
     *reinterpret_cast<floatx4*>(base + elem * 4) = floatx4{v[0], v[1], v[2], v[3]};
   }
 }
 
-template <int VEC, bool BF16, int TAPS>
+// SINGLE: one branch.  Its window then holds the gated values
+// vt = alpha v themselves, so a token's conv is taps multiply-adds per
+// feature instead of a product per tap and a gate-weighted sum of them.
+template <int VEC, bool BF16, int TAPS, bool SINGLE>
 __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   constexpr int R = kGcTokens;
   constexpr int NW = TAPS > 1 ? TAPS - 1 : 1;  // window length
@@ -67,6 +91,23 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   const int64_t N = a.B * a.T;
   const float inv_d = 1.0f / (float)d;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
+
+  // the first PD rows of v go out before the gates are formed (they do not
+  // depend on them), so the stream starts with its loads in flight
+  const int f = threadIdx.x * VEC;
+  const int64_t tbeg = t0 - nh > 0 ? t0 - nh : 0;
+  const int64_t tend = (t0 + R < a.T) ? t0 + R : a.T;
+  const uint8_t* __restrict__ vsrc = a.v;
+  const int64_t row0 = b * a.T;
+  constexpr int PD = 4;  // 8 measured slower (fewer waves fit)
+  u32x4 ring[PD];
+#if ENGRAM_GC_EARLY
+  if (f < d) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u)
+      if (tbeg + u < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + tbeg + u) * d + f);
+  }
+#endif
 
   // ---- gate of tokens t0-nh .. t0+R-1 of each branch (zero before the
   // sequence start); branch m has its own partial sums and stats
@@ -100,32 +141,27 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   // conv weights, so one pass over v serves all of them: the lane keeps the
   // last taps-1 raw v values, and branch m's conv input at t-i is
   // alpha_m(t-i) v(t-i), i.e. z_m = sum_i alpha_m(t-i) (w_i v(t-i)).
-  const int f = threadIdx.x * VEC;
   if (f >= d) return;
   float w[VEC][TAPS];
 #pragma unroll
   for (int c = 0; c < VEC; ++c)
 #pragma unroll
     for (int i = 0; i < TAPS; ++i) w[c][i] = a.conv_w[(f + c) * TAPS + i];
-  float win[NW][VEC];  // win[i] = raw v at t-1-i
+  float win[NW][VEC];  // win[i] = raw v (SINGLE: alpha v) at t-1-i
 #pragma unroll
   for (int i = 0; i < NW; ++i)
 #pragma unroll
     for (int c = 0; c < VEC; ++c) win[i][c] = 0.f;
 
-  const int64_t tbeg = t0 - nh > 0 ? t0 - nh : 0;
-  const int64_t tend = (t0 + R < a.T) ? t0 + R : a.T;
-  const uint8_t* __restrict__ vsrc = a.v;
   const int64_t ystride = N * d * (BF16 ? 2 : 4);  // bytes between branch outputs
-  const int64_t row0 = b * a.T;
   // v rows stream through a ring of PD tokens loaded ahead (each wave keeps
   // PD 1 KB loads in flight; HBM latency, not bandwidth, bounds a shallower
   // ring at this occupancy)
-  constexpr int PD = 4;  // 8 measured slower (fewer waves fit)
-  u32x4 ring[PD];
+#if !ENGRAM_GC_EARLY
 #pragma unroll
   for (int u = 0; u < PD; ++u)
     if (tbeg + u < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + tbeg + u) * d + f);
+#endif
   for (int64_t tb = tbeg; tb < tend; tb += PD) {
 #pragma unroll
     for (int u = 0; u < PD; ++u) {
@@ -134,6 +170,32 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
         float cur[VEC];
         widen<VEC, BF16>(ring[u], cur);
         if (t + PD < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + t + PD) * d + f);
+        if constexpr (SINGLE) {
+          const int li = (int)(t - (t0 - nh));
+          const float al0 = alpha_s[li];
+          float vt[VEC];
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) vt[c] = al0 * cur[c];
+          if (t >= t0) {
+            float out[VEC];
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+              float z = w[c][0] * vt[c];
+#pragma unroll
+              for (int i = 1; i < TAPS; ++i) z += w[c][i] * win[i - 1][c];
+              // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
+              out[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) + vt[c];
+            }
+            store_vec<VEC, BF16>(a.y, (row0 + t) * d + f, out);
+          }
+#pragma unroll
+          for (int i = NW - 1; i > 0; --i)
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) win[i][c] = win[i - 1][c];
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) win[0][c] = vt[c];
+          continue;
+        }
         if (t >= t0) {
           // weighted taps, shared by the branches
           float p[TAPS][VEC];
@@ -178,13 +240,18 @@ hipError_t launch_gate_conv(const GateConvArgs& a, hipStream_t s) {
   if (threads > 1024) return hipErrorInvalidValue;
   if (a.branches > ENGRAM_MAX_BRANCHES) return hipErrorInvalidValue;
   dim3 grid((unsigned)((a.T + kGcTokens - 1) / kGcTokens), (unsigned)a.B);
+  const bool single = a.branches <= 1;
   switch (a.taps) {
 #define ENGRAM_TAPS_CASE(K)                                                                      \
   case K:                                                                                        \
-    if (bf)                                                                                      \
-      hipLaunchKernelGGL((gate_conv_kernel<8, true, K>), grid, dim3(threads), 0, s, a);         \
+    if (bf && single)                                                                            \
+      hipLaunchKernelGGL((gate_conv_kernel<8, true, K, true>), grid, dim3(threads), 0, s, a);   \
+    else if (bf)                                                                                 \
+      hipLaunchKernelGGL((gate_conv_kernel<8, true, K, false>), grid, dim3(threads), 0, s, a);  \
+    else if (single)                                                                             \
+      hipLaunchKernelGGL((gate_conv_kernel<4, false, K, true>), grid, dim3(threads), 0, s, a);  \
     else                                                                                         \
-      hipLaunchKernelGGL((gate_conv_kernel<4, false, K>), grid, dim3(threads), 0, s, a);        \
+      hipLaunchKernelGGL((gate_conv_kernel<4, false, K, false>), grid, dim3(threads), 0, s, a); \
     break;
     ENGRAM_TAPS_CASE(1)
     ENGRAM_TAPS_CASE(2)

@@ -113,6 +113,9 @@ constexpr int kLoadGroups = ENGRAM_GEMM_LOAD_GROUPS;
 #ifndef ENGRAM_GEMM_H1_LATE
 #define ENGRAM_GEMM_H1_LATE 0
 #endif
+#ifndef ENGRAM_GEMM_V_NT
+#define ENGRAM_GEMM_V_NT 0
+#endif
 
 #ifdef ENGRAM_GEMM_TRACE
 // Measurement build only: shader-clock stamps of workgroups 0..31 (wave 0),
@@ -896,7 +899,11 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         const int64_t m = m0 + t;
         if (m < g.M) {
           const u32x4 x = *reinterpret_cast<const u32x4*>(trow(t) + ((c16 ^ (t & 31)) << 4));
-          *reinterpret_cast<u32x4*>(g.v_out + (m * d + fk + c16 * 8) * 2) = x;
+          u32x4* vp = reinterpret_cast<u32x4*>(g.v_out + (m * d + fk + c16 * 8) * 2);
+          if constexpr (ENGRAM_GEMM_V_NT != 0)
+            __builtin_nontemporal_store(x, vp);
+          else
+            *vp = x;
         }
       }
     }

@@ -62,7 +62,13 @@ hipError_t launch_hash(const int32_t* tokens, const int32_t* canon, int64_t N, i
 // (c / rc) % J: e is written front to back and idx read in order.  Each
 // thread moves kGatherPer pieces, kGatherPer * 256 apart, with all its row
 // loads in flight together.  32-bit piece numbers (the host checks the size).
-constexpr int kGatherPer = 4;
+#ifndef ENGRAM_GATHER_PER
+#define ENGRAM_GATHER_PER 4
+#endif
+#ifndef ENGRAM_GATHER_NT
+#define ENGRAM_GATHER_NT 0
+#endif
+constexpr int kGatherPer = ENGRAM_GATHER_PER;
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ idx,
                                                      uint8_t* __restrict__ e, uint32_t pieces,
                                                      GatherArgs g) {
@@ -166,7 +172,13 @@ __global__ __launch_bounds__(256) void hash_gather_kernel(const int32_t* __restr
 #pragma unroll
   for (int u = 0; u < kGatherPer; ++u) {
     const uint32_t c = c0 + u * 256u;
-    if (c < c_end) *(reinterpret_cast<u32x4*>(e) + c) = v[u];
+    if (c < c_end) {
+      u32x4* p = reinterpret_cast<u32x4*>(e) + c;
+      if constexpr (ENGRAM_GATHER_NT != 0)
+        __builtin_nontemporal_store(v[u], p);
+      else
+        *p = v[u];
+    }
   }
 }
 
