@@ -165,7 +165,7 @@ def csrc_digest(root: str | None = None) -> str:
 
 
 # bench names made of several dispatches per call: the kernel that runs once per call
-GROUP_LEADER = {"sorted_scatter": "sort_init_kernel", "dw_gemm": "gemm_tn_kernel",
+GROUP_LEADER = {"sorted_scatter": "sort_hist_kernel<true>", "dw_gemm": "gemm_tn_kernel",
                 "bwd_param_sums": "param_finish_kernel", "shard_pack": "owner_bounds_kernel"}
 # names whose leader is the last dispatch of a call (the others' is the first)
 GROUP_LEADER_LAST = {"bwd_param_sums"}

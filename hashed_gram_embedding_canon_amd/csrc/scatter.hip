@@ -12,11 +12,37 @@
 // order varies run to run).
 #include "kernels.h"
 
+// 1: the segmented reduce reads the per-token gradient rows with
+// non-temporal loads (each is read once).
+#ifndef ENGRAM_SCATTER_NT
+#define ENGRAM_SCATTER_NT 1
+#endif
+// 1: the groups of the whole grid take the short segments in a grid-stride
+// walk (all of them in one window of the output at a time); 0: each block
+// takes the segments of its own range
+#ifndef ENGRAM_RED_GRID_STRIDE
+#define ENGRAM_RED_GRID_STRIDE 1
+#endif
+// segments per group and batch
+#ifndef ENGRAM_RED_BATCH
+#define ENGRAM_RED_BATCH 4
+#endif
+// 1: the next batch's bounds, keys and tokens load behind the current rows
+#ifndef ENGRAM_RED_PREFETCH
+#define ENGRAM_RED_PREFETCH 1
+#endif
+
 namespace engram {
 
 constexpr int kSortThreads = 256;
+constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortThreads * kSortItems;  // keys per block
+constexpr int kWaveRange = 64 * kSortItems;            // keys per wave
+// Up to this many blocks per table, each scatter block derives its digit
+// offsets from the per-block histograms itself (one cache line per digit);
+// beyond it a separate scan kernel writes them.
+constexpr int kFusedScanBlocks = 64;
 
 static inline int64_t sort_blocks(int64_t N) { return (N + kSortTile - 1) / kSortTile; }
 
@@ -49,37 +75,62 @@ void carve_sort(uint8_t* base, int64_t N, int32_t J, SortBufs* b) {
   b->total = (uint32_t*)take(4);
 }
 
-// keys[j][n] = idx[n][j], vals[j][n] = n
-__global__ __launch_bounds__(256) void sort_init_kernel(const int32_t* __restrict__ idx,
-                                                        uint32_t* __restrict__ keys,
-                                                        uint32_t* __restrict__ vals, int64_t N,
-                                                        int J) {
-  const int j = blockIdx.y;
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  keys[j * N + n] = (uint32_t)idx[n * J + j];
-  vals[j * N + n] = (uint32_t)n;
+// Position of item r of a lane inside table j's key array: a block takes
+// kSortTile consecutive keys, each of its waves kWaveRange of them, one
+// coalesced row of 64 per item.  Key order inside a block is (wave, item,
+// lane), which is input order.
+__device__ __forceinline__ int64_t tile_pos(int blk, int wave, int r, int lane) {
+  return (int64_t)blk * kSortTile + wave * kWaveRange + r * 64 + lane;
+}
+
+// Key and token of position p of table j.  The first pass reads the row ids
+// straight from idx [N][J] (the token is the position); later passes read the
+// previous pass's output.
+template <bool FIRST>
+__device__ __forceinline__ void load_pair(const int32_t* __restrict__ idx,
+                                          const uint32_t* __restrict__ kin,
+                                          const uint32_t* __restrict__ vin, int64_t N, int J, int j,
+                                          int64_t p, uint32_t& key, uint32_t& val) {
+  if (p >= N) {
+    key = 0u;
+    val = 0u;
+  } else if (FIRST) {
+    key = (uint32_t)idx[p * J + j];
+    val = (uint32_t)p;
+  } else {
+    key = kin[j * N + p];
+    val = vin[j * N + p];
+  }
 }
 
 // hist[j][digit][blk] for one 8-bit digit
-__global__ __launch_bounds__(kSortThreads) void sort_hist_kernel(const uint32_t* __restrict__ keys,
+template <bool FIRST>
+__global__ __launch_bounds__(kSortThreads) void sort_hist_kernel(const int32_t* __restrict__ idx,
+                                                                 const uint32_t* __restrict__ keys,
                                                                  uint32_t* __restrict__ hist,
-                                                                 int64_t N, int shift, int nb) {
+                                                                 int64_t N, int J, int shift, int nb) {
   __shared__ uint32_t cnt[256];
   const int j = blockIdx.y;
   const int blk = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  uint32_t key[kSortItems];
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    uint32_t v;
+    load_pair<FIRST>(idx, keys, keys, N, J, j, tile_pos(blk, wave, r, lane), key[r], v);
+  }
   cnt[threadIdx.x] = 0;
   __syncthreads();
-  const uint32_t* k = keys + j * N;
-  for (int r = 0; r < kSortItems; ++r) {
-    const int64_t p = (int64_t)blk * kSortTile + r * kSortThreads + threadIdx.x;
-    if (p < N) atomicAdd(&cnt[(k[p] >> shift) & 255u], 1u);
-  }
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r)
+    if (tile_pos(blk, wave, r, lane) < N) atomicAdd(&cnt[(key[r] >> shift) & 255u], 1u);
   __syncthreads();
   hist[((int64_t)j * 256 + threadIdx.x) * nb + blk] = cnt[threadIdx.x];
 }
 
-// exclusive scan of hist[j][*][*] in (digit, block) order; thread = digit
+// Exclusive scan of hist[j][*][*] in (digit, block) order, thread = digit;
+// used when a table has more than kFusedScanBlocks blocks.
 __global__ __launch_bounds__(256) void sort_scan_kernel(uint32_t* __restrict__ hist, int nb) {
   __shared__ uint32_t sums[256];
   const int j = blockIdx.x;
@@ -103,60 +154,139 @@ __global__ __launch_bounds__(256) void sort_scan_kernel(uint32_t* __restrict__ h
   }
 }
 
-// Stable scatter by digit.  Keys of a block are taken in rounds of 256
-// (round-major, then thread order = input order); inside a round the rank of
-// a key among equal digits comes from wave ballots and per-wave digit counts.
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Stable scatter by one 8-bit digit.  All keys of the block are loaded
+// first.  Each wave ranks its own kWaveRange keys in order with ballots and a
+// per-wave digit count in LDS (no block barrier between items).  The block
+// then orders its keys by digit in LDS (digit start in the block + counts of
+// the waves before + rank) and writes them out in that order, so that each
+// digit's keys form one run of consecutive output positions starting at the
+// digit's block base (this block's share of the table-wide exclusive scan).
+template <bool FIRST, bool FUSED>
 __global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(
-    const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
-    uint32_t* __restrict__ vout, const uint32_t* __restrict__ hist, int64_t N, int shift, int nb) {
-  constexpr int NW = kSortThreads / 64;
-  __shared__ uint32_t running[256];
-  __shared__ uint32_t wcount[NW][256];
+    const int32_t* __restrict__ idx, const uint32_t* __restrict__ kin,
+    const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout, uint32_t* __restrict__ vout,
+    const uint32_t* __restrict__ hist, int64_t N, int J, int shift, int nb) {
+  __shared__ uint32_t wcount[kSortWaves][256];
+  __shared__ uint32_t wtot[kSortWaves], wtot2[kSortWaves];
+  __shared__ uint32_t dstart[256], dshift[256];
+  __shared__ uint32_t ks[kSortTile], vs[kSortTile];
   const int j = blockIdx.y;
   const int blk = blockIdx.x;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  running[threadIdx.x] = hist[((int64_t)j * 256 + threadIdx.x) * nb + blk];
+  uint32_t key[kSortItems], val[kSortItems];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) wcount[w][threadIdx.x] = 0;
+  for (int r = 0; r < kSortItems; ++r)
+    load_pair<FIRST>(idx, kin, vin, N, J, j, tile_pos(blk, wave, r, lane), key[r], val[r]);
+  // this block's output offset of digit threadIdx.x
+  uint32_t base;
+  if (FUSED) {
+    const uint32_t* h = hist + ((int64_t)j * 256 + threadIdx.x) * nb;
+    uint32_t pre = 0, tot = 0;
+    for (int b0 = 0; b0 < nb; b0 += 16) {  // 16 loads in flight at a time
+      uint32_t c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = b0 + u < nb ? h[b0 + u] : 0u;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        tot += c[u];
+        pre += b0 + u < blk ? c[u] : 0u;
+      }
+    }
+    uint32_t incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    uint32_t wb = 0;
+    for (int w = 0; w < wave; ++w) wb += wtot[w];
+    base = wb + incl - tot + pre;
+  } else {
+    base = hist[((int64_t)j * 256 + threadIdx.x) * nb + blk];
+  }
+#pragma unroll
+  for (int w = 0; w < kSortWaves; ++w) wcount[w][threadIdx.x] = 0;
   __syncthreads();
-  const uint32_t* ki = kin + j * N;
-  const uint32_t* vi = vin + j * N;
-  uint32_t* ko = kout + j * N;
-  uint32_t* vo = vout + j * N;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t lt = lanes_below(lane);
+  uint32_t rank[kSortItems];
+#pragma unroll
   for (int r = 0; r < kSortItems; ++r) {
-    const int64_t p = (int64_t)blk * kSortTile + r * kSortThreads + threadIdx.x;
-    const bool valid = p < N;
-    const uint32_t key = valid ? ki[p] : 0u;
-    const uint32_t val = valid ? vi[p] : 0u;
-    const uint32_t dg = (key >> shift) & 255u;
+    const bool valid = tile_pos(blk, wave, r, lane) < N;
+    const uint32_t dg = (key[r] >> shift) & 255u;
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
       const uint64_t bal = __ballot((dg >> bit) & 1u);
       peers &= ((dg >> bit) & 1u) ? bal : ~bal;
     }
-    const uint32_t rank = (uint32_t)__popcll(peers & lt_mask);
-    if (valid && rank == 0) wcount[wave][dg] = (uint32_t)__popcll(peers);
-    __syncthreads();
-    if (valid) {
-      uint32_t base = running[dg];
-      for (int w = 0; w < wave; ++w) base += wcount[w][dg];
-      ko[base + rank] = key;
-      vo[base + rank] = val;
-    }
-    __syncthreads();
-    uint32_t add = 0;
+    const uint32_t below = (uint32_t)__popcll(peers & lt);
+    // One wave's LDS accesses complete in issue order: every peer reads the
+    // count before its first peer writes the new one.
+    const uint32_t before = wcount[wave][dg];
+    rank[r] = before + below;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && below == 0) wcount[wave][dg] = before + (uint32_t)__popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // Digit d of this block: its keys' offsets among themselves (per wave), the
+  // start of its run in the block's digit order, and the shift from there to
+  // its output position.
+  {
+    uint32_t cnt = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      add += wcount[w][threadIdx.x];
-      wcount[w][threadIdx.x] = 0;
+    for (int w = 0; w < kSortWaves; ++w) {
+      const uint32_t c = wcount[w][threadIdx.x];
+      wcount[w][threadIdx.x] = cnt;
+      cnt += c;
     }
-    running[threadIdx.x] += add;
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wtot2[wave] = incl;
     __syncthreads();
+    uint32_t loc = incl - cnt;
+    for (int w = 0; w < wave; ++w) loc += wtot2[w];
+    dstart[threadIdx.x] = loc;
+    dshift[threadIdx.x] = base - loc;  // mod 2^32
+  }
+  __syncthreads();
+  // the block's keys in digit order in LDS, then written out in that order:
+  // each digit's keys go to consecutive output positions
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    if (tile_pos(blk, wave, r, lane) < N) {
+      const uint32_t dg = (key[r] >> shift) & 255u;
+      const uint32_t lp = dstart[dg] + wcount[wave][dg] + rank[r];
+      ks[lp] = key[r];
+      vs[lp] = val[r];
+    }
+  }
+  __syncthreads();
+  const int64_t left = N - (int64_t)blk * kSortTile;
+  const int nvalid = left < kSortTile ? (int)left : kSortTile;
+  uint32_t* ko = kout + j * N;
+  uint32_t* vo = vout + j * N;
+  for (int i = threadIdx.x; i < nvalid; i += kSortThreads) {
+    const uint32_t k = ks[i];
+    const uint32_t pos = dshift[(k >> shift) & 255u] + (uint32_t)i;
+    ko[pos] = k;
+    vo[pos] = vs[i];
   }
 }
+
+// Heads of segments: the first key of a table and every key that differs
+// from the one before it.
 
 // number of segment heads per block of sorted keys
 __global__ __launch_bounds__(256) void seg_count_kernel(const uint32_t* __restrict__ keys,
@@ -165,15 +295,23 @@ __global__ __launch_bounds__(256) void seg_count_kernel(const uint32_t* __restri
   __shared__ uint32_t tot;
   const int j = blockIdx.y;
   const int blk = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   if (threadIdx.x == 0) tot = 0;
-  __syncthreads();
   const uint32_t* k = keys + j * N;
-  uint32_t c = 0;
+  uint32_t kv[kSortItems], pv[kSortItems];  // all loads in flight together
+#pragma unroll
   for (int r = 0; r < kSortItems; ++r) {
-    const int64_t p = (int64_t)blk * kSortTile + r * 256 + threadIdx.x;
-    if (p < N && (p == 0 || k[p] != k[p - 1])) ++c;
+    const int64_t p = tile_pos(blk, wave, r, lane);
+    kv[r] = p < N ? k[p] : 0u;
+    pv[r] = p > 0 && p < N ? k[p - 1] : ~kv[r];
   }
-  atomicAdd(&tot, c);
+  uint32_t c = 0;
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r)
+    c += (uint32_t)__popcll(__ballot(tile_pos(blk, wave, r, lane) < N && kv[r] != pv[r]));
+  __syncthreads();
+  if (lane == 0) atomicAdd(&tot, c);
   __syncthreads();
   if (threadIdx.x == 0) seg_count[j * nb + blk] = tot;
 }
@@ -207,38 +345,74 @@ __global__ __launch_bounds__(1024) void seg_scan_kernel(uint32_t* __restrict__ s
   }
 }
 
-// seg_start / seg_key of every head, in sorted order
-__global__ __launch_bounds__(256) void seg_write_kernel(const uint32_t* __restrict__ keys,
-                                                        const uint32_t* __restrict__ seg_count,
-                                                        uint32_t* __restrict__ seg_start,
-                                                        uint64_t* __restrict__ seg_key, int64_t N,
-                                                        int nb) {
-  __shared__ uint32_t wsum[4];
-  __shared__ uint32_t base_s;
+// Keys and head flags of a wave's positions, and the number of heads before
+// the wave's first position (block's scanned count plus the heads of the
+// waves before it).
+__device__ __forceinline__ uint32_t seg_wave_base(const uint32_t* __restrict__ k,
+                                                  const uint32_t* __restrict__ seg_count,
+                                                  int64_t N, int nb, uint32_t (&kv)[kSortItems],
+                                                  uint64_t (&bal)[kSortItems], uint32_t* wtot) {
   const int j = blockIdx.y;
   const int blk = blockIdx.x;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  if (threadIdx.x == 0) base_s = seg_count[j * nb + blk];
-  __syncthreads();
-  const uint32_t* k = keys + j * N;
+  bool h[kSortItems];
+#pragma unroll
   for (int r = 0; r < kSortItems; ++r) {
-    const int64_t p = (int64_t)blk * kSortTile + r * 256 + threadIdx.x;
-    const bool head = p < N && (p == 0 || k[p] != k[p - 1]);
-    const uint64_t bal = __ballot(head);
-    if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
-    __syncthreads();
-    uint32_t base = base_s;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    if (head) {
-      const uint32_t s = base + (uint32_t)__popcll(bal & lt_mask);
-      seg_start[s] = (uint32_t)(j * N + p);
-      seg_key[s] = ((uint64_t)j << 32) | k[p];
+    const int64_t p = tile_pos(blk, wave, r, lane);
+    kv[r] = p < N ? k[p] : 0u;
+    h[r] = p < N && (p == 0 || kv[r] != k[p - 1]);
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    bal[r] = __ballot(h[r]);
+    c += (uint32_t)__popcll(bal[r]);
+  }
+  if (lane == 0) wtot[wave] = c;
+  __syncthreads();
+  uint32_t base = seg_count[j * nb + blk];
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  return base;
+}
+
+// seg_start / seg_key of every head, in sorted order, and (when seg_tok is
+// given) the token of its first element
+__global__ __launch_bounds__(256) void seg_write_kernel(const uint32_t* __restrict__ keys,
+                                                        const uint32_t* __restrict__ vals,
+                                                        const uint32_t* __restrict__ seg_count,
+                                                        uint32_t* __restrict__ seg_start,
+                                                        uint64_t* __restrict__ seg_key,
+                                                        uint32_t* __restrict__ seg_tok, int64_t N,
+                                                        int nb) {
+  __shared__ uint32_t wtot[kSortWaves];
+  const int j = blockIdx.y;
+  const int blk = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const uint32_t* k = keys + j * N;
+  uint32_t tv[kSortItems];
+  if (seg_tok) {
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+      const int64_t p = tile_pos(blk, wave, r, lane);
+      tv[r] = p < N ? vals[j * N + p] : 0u;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) base_s += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
+  }
+  uint32_t kv[kSortItems];
+  uint64_t bal[kSortItems];
+  uint32_t base = seg_wave_base(k, seg_count, N, nb, kv, bal, wtot);
+  const uint64_t lt = lanes_below(lane);
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const int64_t p = tile_pos(blk, wave, r, lane);
+    if ((bal[r] >> lane) & 1ull) {
+      const uint32_t s = base + (uint32_t)__popcll(bal[r] & lt);
+      seg_start[s] = (uint32_t)(j * N + p);
+      seg_key[s] = ((uint64_t)j << 32) | kv[r];
+      if (seg_tok) seg_tok[s] = tv[r];
+    }
+    base += (uint32_t)__popcll(bal[r]);
   }
 }
 
@@ -250,105 +424,246 @@ __global__ __launch_bounds__(256) void seg_inverse_kernel(const uint32_t* __rest
                                                           const uint32_t* __restrict__ seg_count,
                                                           int32_t* __restrict__ inverse, int64_t N,
                                                           int nb, int J) {
-  __shared__ uint32_t wsum[4];
-  __shared__ uint32_t base_s;
+  __shared__ uint32_t wtot[kSortWaves];
   const int j = blockIdx.y;
   const int blk = blockIdx.x;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const uint64_t le_mask = ~0ull >> (63 - lane);
-  if (threadIdx.x == 0) base_s = seg_count[j * nb + blk];
-  __syncthreads();
   const uint32_t* k = keys + j * N;
   const uint32_t* v = vals + j * N;
+  uint32_t tv[kSortItems];
+#pragma unroll
   for (int r = 0; r < kSortItems; ++r) {
-    const int64_t p = (int64_t)blk * kSortTile + r * 256 + threadIdx.x;
-    const bool head = p < N && (p == 0 || k[p] != k[p - 1]);
-    const uint64_t bal = __ballot(head);
-    if (lane == 0) wsum[wave] = (uint32_t)__popcll(bal);
-    __syncthreads();
-    uint32_t base = base_s;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    if (p < N) inverse[(int64_t)v[p] * J + j] = (int32_t)(base + (uint32_t)__popcll(bal & le_mask) - 1);
-    __syncthreads();
-    if (threadIdx.x == 0) base_s += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
+    const int64_t p = tile_pos(blk, wave, r, lane);
+    tv[r] = p < N ? v[p] : 0u;
+  }
+  uint32_t kv[kSortItems];
+  uint64_t bal[kSortItems];
+  uint32_t base = seg_wave_base(k, seg_count, N, nb, kv, bal, wtot);
+  const uint64_t le = ~0ull >> (63 - lane);
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const int64_t p = tile_pos(blk, wave, r, lane);
+    if (p < N) inverse[(int64_t)tv[r] * J + j] = (int32_t)(base + (uint32_t)__popcll(bal[r] & le) - 1);
+    base += (uint32_t)__popcll(bal[r]);
   }
 }
 
-// Segmented reduce.  A wave holds S = 64 / (D/4) lane groups of D/4 lanes
-// (one 16-byte column piece per lane); each group sums whole segments in a
-// grid-stride walk and writes their rows.  Most segments have one element,
-// so the cost is the chain segment start -> token -> de row; a group runs two
-// segments side by side (two independent chains) and sums each segment's
-// elements in sorted order with two accumulators (a fixed order).
-constexpr int kSegBlocksMax = 4096;
+// Segmented reduce.  Block b owns segments [b*kSegsPerBlock, ...).  A wave
+// holds S = 64 / (D/4) lane groups of D/4 lanes (one 16-byte column piece per
+// lane), a block G = 4*S groups.  A Zipf-heavy row can have hundreds of
+// elements: segments of kLongSeg or more are summed first, by the whole
+// block, group g taking elements g, g+G, ... in order, and the G partial
+// sums are then added in group order.  Nearly every other segment has one
+// element; a group takes kRedBatch consecutive segments at a time, with the
+// first rows of all of them in flight together and the bounds, keys and
+// first tokens of its next batch loading behind them, and sums the rest of a
+// segment's elements in sorted order.  Both orders depend only on D, so
+// results repeat run to run.
+constexpr int kSegsPerBlock = 1024;
+constexpr int kLongSeg = 32;
+constexpr int kRedBatch = ENGRAM_RED_BATCH;
+
+__device__ __forceinline__ floatx4 load_row_piece(const float* p) {
+#if ENGRAM_SCATTER_NT
+  return __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+#else
+  return *reinterpret_cast<const floatx4*>(p);
+#endif
+}
+
 template <int MODE>
-__global__ __launch_bounds__(256) void seg_reduce_kernel(ScatterArgs a, const uint32_t* __restrict__ vals,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void seg_reduce_kernel(ScatterArgs a, const uint32_t* __restrict__ vals,
                                                          const uint32_t* __restrict__ seg_start,
                                                          const uint64_t* __restrict__ seg_key,
+                                                         const uint32_t* __restrict__ seg_tok,
                                                          const uint32_t* __restrict__ total) {
+  constexpr int kScan = kSegsPerBlock / 256;
+  __shared__ floatx4 part[256];  // G * D/4 = 4 * S * D/4 <= 256
+  __shared__ uint32_t lst[kSegsPerBlock];
+  __shared__ uint32_t nl;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int D4 = a.D / 4;               // <= 64 (D <= 256)
+  const int D4 = a.D / 4;  // <= 64 (D <= 256)
   const int S = 64 / D4;
+  const int G = 4 * S;
   const int grp = lane / D4;
   const int col = lane - grp * D4;
-  if (grp >= S) return;
-  const int64_t U = total[0];
-  const int64_t NJ = a.N * a.J;
+  const bool act = grp < S;
+  const int gi = wave * S + grp;
+  const uint32_t U = total[0];
+  const uint32_t s0 = blockIdx.x * (uint32_t)kSegsPerBlock;
+#if !ENGRAM_RED_GRID_STRIDE
+  if (s0 >= U) return;  // block-uniform
+#endif
+  const uint32_t s1 = min(s0 + (uint32_t)kSegsPerBlock, U);
+  const uint32_t NJ = (uint32_t)(a.N * a.J);
   const int64_t dm = (int64_t)a.J * a.D;
-  const int64_t stride = (int64_t)gridDim.x * 4 * S;
-  auto bounds = [&](int64_t seg, int64_t& beg, int64_t& end, uint64_t& key) {
-    beg = seg_start[seg];
-    end = (seg + 1 < U) ? (int64_t)seg_start[seg + 1] : NJ;
-    key = seg_key[seg];
+  auto start_of = [&](uint32_t s) -> uint32_t { return s < U ? seg_start[s] : NJ; };
+  auto row = [&](uint64_t key, uint32_t t) -> floatx4 {
+    return load_row_piece(a.de + (int64_t)t * dm + (int64_t)(key >> 32) * a.D + col * 4);
   };
-  auto row_src = [&](uint64_t key) -> const float* {
-    return a.de + (int64_t)(key >> 32) * a.D + col * 4;
-  };
-  // the rest of a segment after its first element
-  auto tail = [&](const float* src, int64_t p, int64_t end, floatx4 acc0) -> floatx4 {
-    floatx4 acc1 = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (; p + 1 < end; p += 2) {
-      const int64_t t0 = vals[p], t1 = vals[p + 1];
-      acc0 += *reinterpret_cast<const floatx4*>(src + t0 * dm);
-      acc1 += *reinterpret_cast<const floatx4*>(src + t1 * dm);
-    }
-    if (p < end) acc0 += *reinterpret_cast<const floatx4*>(src + (int64_t)vals[p] * dm);
-    return acc0 + acc1;
-  };
-  auto emit = [&](int64_t seg, uint64_t key, floatx4 acc) {
+  auto emit = [&](uint32_t seg, uint64_t key, floatx4 acc) {
     const int j = (int)(key >> 32);
-    const int64_t row = (int64_t)(key & 0xFFFFFFFFu);
+    const int64_t r = (int64_t)(key & 0xFFFFFFFFu);
     if (MODE == ENGRAM_GRAD_SORTED_SPARSE) {
-      *reinterpret_cast<floatx4*>(a.rows_out + seg * a.D + col * 4) = acc;
+      *reinterpret_cast<floatx4*>(a.rows_out + (int64_t)seg * a.D + col * 4) = acc;
       if (col == 0) a.keys_out[seg] = (int64_t)key;
     } else {
-      floatx4* dst = reinterpret_cast<floatx4*>(a.dense[j] + row * a.D + col * 4);
+      floatx4* dst = reinterpret_cast<floatx4*>(a.dense[j] + r * a.D + col * 4);
       *dst = *dst + acc;
     }
   };
-  for (int64_t sa = ((int64_t)blockIdx.x * 4 + wave) * S + grp; sa < U; sa += 2 * stride) {
-    const int64_t sb = sa + stride;
-    const bool hb = sb < U;
-    int64_t ba, ea, bb = 0, eb = 0;
-    uint64_t ka, kb = 0;
-    bounds(sa, ba, ea, ka);
-    if (hb) bounds(sb, bb, eb, kb);
-    const float* srca = row_src(ka);
-    const float* srcb = row_src(kb);
-    const int64_t ta = vals[ba];
-    const int64_t tb = hb ? (int64_t)vals[bb] : 0;
-    floatx4 xa = *reinterpret_cast<const floatx4*>(srca + ta * dm);
-    floatx4 xb = hb ? *reinterpret_cast<const floatx4*>(srcb + tb * dm) : floatx4{};
-    if (ea - ba > 1) xa = tail(srca, ba + 1, ea, xa);
-    emit(sa, ka, xa);
-    if (hb) {
-      if (eb - bb > 1) xb = tail(srcb, bb + 1, eb, xb);
-      emit(sb, kb, xb);
+  const floatx4 zero = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // long segments of the block's range, whole block
+  if (threadIdx.x == 0) nl = 0;
+  __syncthreads();
+  {
+    uint32_t len[kScan];
+#pragma unroll
+    for (int c = 0; c < kScan; ++c) {
+      const uint32_t s = s0 + c * 256 + threadIdx.x;
+      len[c] = s < s1 ? start_of(s + 1) - seg_start[s] : 0u;
     }
+#pragma unroll
+    for (int c = 0; c < kScan; ++c)
+      if (len[c] >= (uint32_t)kLongSeg) lst[atomicAdd(&nl, 1u)] = s0 + c * 256 + threadIdx.x;
   }
+  __syncthreads();
+  const uint32_t n_long = nl;
+  for (uint32_t i = 0; i < n_long; ++i) {
+    const uint32_t sl = lst[i];
+    const uint32_t beg = seg_start[sl];
+    const uint32_t end = start_of(sl + 1);
+    const uint64_t key = seg_key[sl];
+    if (act) {
+      floatx4 acc = zero;
+      for (uint32_t p = beg + gi; p < end; p += (uint32_t)(G * kRedBatch)) {
+        uint32_t t[kRedBatch];
+#pragma unroll
+        for (int u = 0; u < kRedBatch; ++u) {
+          const uint32_t q = p + (uint32_t)(u * G);
+          t[u] = q < end ? vals[q] : 0u;
+        }
+        floatx4 x[kRedBatch];
+#pragma unroll
+        for (int u = 0; u < kRedBatch; ++u)
+          x[u] = p + (uint32_t)(u * G) < end ? row(key, t[u]) : zero;
+#pragma unroll
+        for (int u = 0; u < kRedBatch; ++u) acc += x[u];
+      }
+      part[gi * D4 + col] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < D4) {  // wave 0, group 0: col == threadIdx.x
+      floatx4 sum = part[threadIdx.x];
+      for (int g = 1; g < G; ++g) sum += part[g * D4 + threadIdx.x];
+      emit(sl, key, sum);
+    }
+    __syncthreads();
+  }
+
+  // the other segments, kRedBatch consecutive ones per group
+  if (!act) return;
+#if ENGRAM_RED_GRID_STRIDE
+  const uint32_t b_end = U;
+  const uint32_t b_first = (blockIdx.x * (uint32_t)G + (uint32_t)gi) * kRedBatch;
+  const uint32_t b_step = gridDim.x * (uint32_t)G * kRedBatch;
+#else
+  const uint32_t b_end = s1;
+  const uint32_t b_first = s0 + (uint32_t)(gi * kRedBatch);
+  const uint32_t b_step = (uint32_t)(G * kRedBatch);
+#endif
+  uint32_t st[kRedBatch + 1];
+  uint64_t key[kRedBatch];
+  uint32_t tok[kRedBatch];
+  auto load_meta = [&](uint32_t sb) {
+#pragma unroll
+    for (int u = 0; u <= kRedBatch; ++u) st[u] = start_of(sb + u);
+#pragma unroll
+    for (int u = 0; u < kRedBatch; ++u) {
+      const bool in = sb + u < b_end;
+      key[u] = in ? seg_key[sb + u] : 0ull;
+      tok[u] = in ? seg_tok[sb + u] : 0u;
+    }
+  };
+  uint32_t sb = b_first;
+  if (sb < b_end) load_meta(sb);
+  for (; sb < b_end; sb += b_step) {
+    bool ok[kRedBatch];
+    floatx4 x[kRedBatch];
+    uint32_t cst[kRedBatch + 1];
+    uint64_t ckey[kRedBatch];
+#pragma unroll
+    for (int u = 0; u < kRedBatch; ++u) {
+      ok[u] = sb + u < b_end && st[u + 1] - st[u] < (uint32_t)kLongSeg;
+      x[u] = ok[u] ? row(key[u], tok[u]) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u <= kRedBatch; ++u) cst[u] = st[u];
+#pragma unroll
+    for (int u = 0; u < kRedBatch; ++u) ckey[u] = key[u];
+    const uint32_t next = sb + b_step;
+#if ENGRAM_RED_PREFETCH
+    if (next < b_end) load_meta(next);
+#endif
+#pragma unroll
+    for (int u = 0; u < kRedBatch; ++u) {
+      if (!ok[u]) continue;
+      for (uint32_t p = cst[u] + 1; p < cst[u + 1]; p += 4) {
+        uint32_t tt[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tt[v] = p + v < cst[u + 1] ? vals[p + v] : 0u;
+        floatx4 y[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) y[v] = p + v < cst[u + 1] ? row(ckey[u], tt[v]) : zero;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[u] += y[v];
+      }
+      emit(sb + u, ckey[u], x[u]);
+    }
+#if !ENGRAM_RED_PREFETCH
+    if (next < b_end) load_meta(next);
+#endif
+  }
+}
+
+// Stable sort of every table's (row id, token) pairs by row id: one digit
+// pass per 8 bits of the largest row id, the first reading idx itself.
+// Returns the ping-pong buffer that holds the result.
+static int sort_pairs(const int32_t* idx, int64_t N, int J, int key_bits, const SortBufs& b,
+                      hipStream_t s) {
+  const int nb = (int)sort_blocks(N);
+  const bool fused = nb <= kFusedScanBlocks;
+  const int passes = key_bits > 8 ? (key_bits + 7) / 8 : 1;
+  const dim3 grid(nb, J);
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = pass * 8;
+    const int in = (pass - 1) & 1, out = pass & 1;
+    if (pass == 0)
+      hipLaunchKernelGGL(sort_hist_kernel<true>, grid, dim3(kSortThreads), 0, s, idx, nullptr, b.hist,
+                         N, J, shift, nb);
+    else
+      hipLaunchKernelGGL(sort_hist_kernel<false>, grid, dim3(kSortThreads), 0, s, idx, b.keys[in],
+                         b.hist, N, J, shift, nb);
+    if (!fused) hipLaunchKernelGGL(sort_scan_kernel, dim3(J), dim3(256), 0, s, b.hist, nb);
+    const uint32_t* kin = pass ? b.keys[in] : nullptr;
+    const uint32_t* vin = pass ? b.vals[in] : nullptr;
+    if (pass == 0 && fused)
+      hipLaunchKernelGGL((sort_scatter_kernel<true, true>), grid, dim3(kSortThreads), 0, s, idx, kin,
+                         vin, b.keys[out], b.vals[out], b.hist, N, J, shift, nb);
+    else if (pass == 0)
+      hipLaunchKernelGGL((sort_scatter_kernel<true, false>), grid, dim3(kSortThreads), 0, s, idx, kin,
+                         vin, b.keys[out], b.vals[out], b.hist, N, J, shift, nb);
+    else if (fused)
+      hipLaunchKernelGGL((sort_scatter_kernel<false, true>), grid, dim3(kSortThreads), 0, s, idx, kin,
+                         vin, b.keys[out], b.vals[out], b.hist, N, J, shift, nb);
+    else
+      hipLaunchKernelGGL((sort_scatter_kernel<false, false>), grid, dim3(kSortThreads), 0, s, idx,
+                         kin, vin, b.keys[out], b.vals[out], b.hist, N, J, shift, nb);
+  }
+  return (passes - 1) & 1;
 }
 
 hipError_t launch_sorted_scatter(const ScatterArgs& a, const SortBufs& b, int32_t mode,
@@ -361,35 +676,23 @@ hipError_t launch_sorted_scatter(const ScatterArgs& a, const SortBufs& b, int32_
     return hipGetLastError();
   }
   const int nb = (int)sort_blocks(N);
-  hipLaunchKernelGGL(sort_init_kernel, dim3((unsigned)((N + 255) / 256), J), dim3(256), 0, s, a.idx,
-                     b.keys[0], b.vals[0], N, J);
-  int cur = 0;
-  const int passes = (a.key_bits + 7) / 8;
-  for (int pass = 0; pass < passes; ++pass) {
-    const int shift = pass * 8;
-    hipLaunchKernelGGL(sort_hist_kernel, dim3(nb, J), dim3(kSortThreads), 0, s, b.keys[cur], b.hist,
-                       N, shift, nb);
-    hipLaunchKernelGGL(sort_scan_kernel, dim3(J), dim3(256), 0, s, b.hist, nb);
-    hipLaunchKernelGGL(sort_scatter_kernel, dim3(nb, J), dim3(kSortThreads), 0, s, b.keys[cur],
-                       b.vals[cur], b.keys[cur ^ 1], b.vals[cur ^ 1], b.hist, N, shift, nb);
-    cur ^= 1;
-  }
+  const int cur = sort_pairs(a.idx, N, J, a.key_bits, b, s);
   hipLaunchKernelGGL(seg_count_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.seg_count, N, nb);
   hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(1024), 0, s, b.seg_count, nb * J, b.total,
                      mode == ENGRAM_GRAD_SORTED_SPARSE ? a.count_out : nullptr);
-  hipLaunchKernelGGL(seg_write_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.seg_count,
-                     b.seg_start, b.seg_key, N, nb);
-  // grid-stride over at most N*J segments, S per wave
+  // the first token of every segment goes to the spare ping-pong buffer
+  uint32_t* seg_tok = b.vals[cur ^ 1];
+  hipLaunchKernelGGL(seg_write_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.vals[cur],
+                     b.seg_count, b.seg_start, b.seg_key, seg_tok, N, nb);
+  // at most N*J segments; blocks past the actual count return at once
   const int64_t max_segs = N * J;
-  const int S = 64 / (a.D / 4);
-  const int64_t want = (max_segs + 4 * S - 1) / (4 * S);
-  const unsigned blocks = (unsigned)(want < kSegBlocksMax ? want : kSegBlocksMax);
+  const unsigned blocks = (unsigned)((max_segs + kSegsPerBlock - 1) / kSegsPerBlock);
   if (mode == ENGRAM_GRAD_SORTED_SPARSE)
     hipLaunchKernelGGL(seg_reduce_kernel<ENGRAM_GRAD_SORTED_SPARSE>, dim3(blocks), dim3(256), 0, s, a,
-                       b.vals[cur], b.seg_start, b.seg_key, b.total);
+                       b.vals[cur], b.seg_start, b.seg_key, seg_tok, b.total);
   else
     hipLaunchKernelGGL(seg_reduce_kernel<ENGRAM_GRAD_SORTED_DENSE>, dim3(blocks), dim3(256), 0, s, a,
-                       b.vals[cur], b.seg_start, b.seg_key, b.total);
+                       b.vals[cur], b.seg_start, b.seg_key, seg_tok, b.total);
   return hipGetLastError();
 }
 
@@ -400,23 +703,11 @@ hipError_t launch_dedup(const int32_t* idx, int64_t N, int32_t J, int32_t key_bi
     return hipGetLastError();
   }
   const int nb = (int)sort_blocks(N);
-  hipLaunchKernelGGL(sort_init_kernel, dim3((unsigned)((N + 255) / 256), J), dim3(256), 0, s, idx,
-                     b.keys[0], b.vals[0], N, J);
-  int cur = 0;
-  const int passes = (key_bits + 7) / 8;
-  for (int pass = 0; pass < passes; ++pass) {
-    const int shift = pass * 8;
-    hipLaunchKernelGGL(sort_hist_kernel, dim3(nb, J), dim3(kSortThreads), 0, s, b.keys[cur], b.hist,
-                       N, shift, nb);
-    hipLaunchKernelGGL(sort_scan_kernel, dim3(J), dim3(256), 0, s, b.hist, nb);
-    hipLaunchKernelGGL(sort_scatter_kernel, dim3(nb, J), dim3(kSortThreads), 0, s, b.keys[cur],
-                       b.vals[cur], b.keys[cur ^ 1], b.vals[cur ^ 1], b.hist, N, shift, nb);
-    cur ^= 1;
-  }
+  const int cur = sort_pairs(idx, N, J, key_bits, b, s);
   hipLaunchKernelGGL(seg_count_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.seg_count, N, nb);
   hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(1024), 0, s, b.seg_count, nb * J, b.total, nullptr);
-  hipLaunchKernelGGL(seg_write_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.seg_count,
-                     b.seg_start, b.seg_key, N, nb);
+  hipLaunchKernelGGL(seg_write_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.vals[cur],
+                     b.seg_count, b.seg_start, b.seg_key, nullptr, N, nb);
   hipLaunchKernelGGL(seg_inverse_kernel, dim3(nb, J), dim3(256), 0, s, b.keys[cur], b.vals[cur],
                      b.seg_count, inverse, N, nb, J);
   return hipGetLastError();

@@ -32,7 +32,8 @@ import synth  # noqa: E402
     ("engram::gather_quant_kernel(int const*, long, engram::GatherArgs, int, unsigned char*, float*)",
      "gather_quant"),
     ("void engram::quant_rows_kernel<true>(unsigned char const*, long, int, unsigned char*, float*)", "quant_w"),
-    ("engram::sort_init_kernel(int const*, unsigned int*, unsigned int*, long, int)", "sorted_scatter"),
+    ("void engram::sort_hist_kernel<true>(int const*, unsigned int const*, unsigned int*, long, int, int, int)",
+     "sorted_scatter"),
     ("void engram::seg_reduce_kernel<0>(engram::ScatterArgs)", "sorted_scatter"),
     ("engram::owner_bounds_kernel(x)", "shard_pack"),
     ("engram::serve_kernel(x)", "shard_serve"),

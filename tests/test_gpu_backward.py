@@ -85,6 +85,81 @@ def test_sorted_path_is_deterministic(torch):
     assert torch.equal(r1["keys"][:n], r2["keys"][:n]) and torch.equal(r1["rows"][:n], r2["rows"][:n])
 
 
+def test_table_grads_one_long_segment_per_table(torch, oracle_lib):
+    """A constant token stream: past the first few positions every table's
+    keys are one segment of nearly N elements, summed by a whole block of lane
+    groups.  Every key exact, every row against the oracle."""
+    import hashed_gram_embedding_canon_amd as eg
+    wl = synth.get_workload("tiny").with_shape(1, 20000)
+    print("[tiny bwd] constant tokens B=1 T=20000", flush=True)
+    inp = synth.Inputs(wl)
+    tok = np.full((wl.B, wl.T), 7, np.int32)
+    dp = H.DeviceProblem(inp, tokens=tok)
+    bufs = dp.alloc_saved(("idx", "stats", "k", "v"))
+    dp.forward(bufs)
+    dy = H.to_dev(inp.dy)
+    sparse = dp.backward(bufs, dy, eg.ENGRAM_GRAD_SORTED_SPARSE)
+    dense = dp.backward(bufs, dy, eg.ENGRAM_GRAD_SORTED_DENSE)["dense"]
+    torch.cuda.synchronize()
+    keys, rows = _sparse_to_dict(sparse, wl.dim)
+    p = H.oracle_problem(inp, tokens=tok)
+    idx = p.hash()
+    want = np.unique(np.concatenate([(np.int64(j) << 32) | idx[:, j].astype(np.int64)
+                                     for j in range(wl.J)]))
+    assert np.array_equal(keys, want)
+    longest = max(np.unique(idx[:, j], return_counts=True)[1].max() for j in range(wl.J))
+    assert longest >= wl.T - 4, longest
+    ref = p.table_grad_dense(inp.dy)
+    ref_rows = np.stack([ref[int(k >> 32)][int(k & 0xFFFFFFFF)] for k in keys])
+    err = H.rel_l2(rows, ref_rows)
+    worst = max(H.rel_l2(rows[i], ref_rows[i]) for i in range(len(keys)))
+    print(f"  {len(keys)} keys, longest segment {longest}: rel L2 {err:.2e}, worst row {worst:.2e}",
+          flush=True)
+    assert err <= 1e-3 and worst <= 1e-3, (err, worst)
+    got = np.concatenate([d.cpu().numpy().astype(np.float64).ravel() for d in dense])
+    assert H.rel_l2(got, np.concatenate([r.ravel() for r in ref])) <= 1e-3
+
+
+def test_table_grads_many_sort_blocks(torch, oracle_lib):
+    """270000 tokens: more than 64 sort blocks per table, where a separate
+    scan kernel writes the digit offsets.  Every key exact; every row against
+    the atomic scatter; sampled rows (the 8 most-hit keys and 200 seeded
+    random ones) against the oracle."""
+    import hashed_gram_embedding_canon_amd as eg
+    wl = synth.get_workload("tiny").with_shape(1, 270000)
+    print("[tiny bwd] B=1 T=270000", flush=True)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp)
+    bufs = dp.alloc_saved(("idx", "stats", "k", "v"))
+    dp.forward(bufs)
+    dy = H.to_dev(inp.dy)
+    sparse = dp.backward(bufs, dy, eg.ENGRAM_GRAD_SORTED_SPARSE)
+    atomic = dp.backward(bufs, dy, eg.ENGRAM_GRAD_ATOMIC_DENSE)["dense"]
+    torch.cuda.synchronize()
+    keys, rows = _sparse_to_dict(sparse, wl.dim)
+    p = H.oracle_problem(inp)
+    idx = p.hash()
+    all_keys = np.concatenate([(np.int64(j) << 32) | idx[:, j].astype(np.int64) for j in range(wl.J)])
+    uk, cnt = np.unique(all_keys, return_counts=True)
+    assert np.array_equal(keys, uk)
+    kj = (keys >> 32).astype(np.int64)
+    kr = (keys & 0xFFFFFFFF).astype(np.int64)
+    a = np.concatenate([atomic[j].cpu().numpy().astype(np.float64)[kr[kj == j]] for j in range(wl.J)])
+    err_a = H.rel_l2(rows, a)
+    picked = set(int(k) for k in uk[np.argsort(-cnt, kind="stable")[:8]])
+    picked.update(int(keys[int(q)]) for q in synth.u64_stream(23, 200) % np.uint64(len(keys)))
+    sel = sorted(picked)
+    rj = np.array([k >> 32 for k in sel], np.int32)
+    rr = np.array([k & 0xFFFFFFFF for k in sel], np.int32)
+    ref, npos = p.table_grad_rows(inp.dy, idx, rj, rr)
+    key_pos = {int(k): i for i, k in enumerate(keys)}
+    got = np.stack([rows[key_pos[k]] for k in sel])
+    err = H.rel_l2(got, ref)
+    print(f"  {len(keys)} keys; sorted vs atomic rel L2 {err_a:.2e}; {len(sel)} sampled rows "
+          f"({npos} positions) vs oracle {err:.2e}", flush=True)
+    assert err_a <= 1e-3 and err <= 1e-3, (err_a, err)
+
+
 def test_engram27b_table_grads_sampled(torch, oracle_lib):
     """27B-scale shapes: every key exact; against the oracle, the rows of the
     64 most-hit keys (the longest segments), the most-hit row of every table

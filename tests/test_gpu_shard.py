@@ -31,9 +31,9 @@ def _shard_rows(table_rows, G):
     return [(int(m) + G - 1) // G for m in table_rows]
 
 
-def _requests(torch, dp, idx, G):
+def _requests(torch, dp, idx, G, N=None):
     import hashed_gram_embedding_canon_amd as eg
-    N, J = dp.N, dp.wl.J
+    N, J = dp.N if N is None else N, dp.wl.J
     send_ids = torch.empty(max(N * J, 1), dtype=torch.int32, device="cuda")
     counts = torch.empty(G, dtype=torch.int64, device="cuda")
     inverse = torch.empty(N, J, dtype=torch.int32, device="cuda")
@@ -72,6 +72,27 @@ def test_requests_match_definition(torch, name, B, T, G):
     send_ids, counts, inverse = _requests(torch, dp, idx, G)
     torch.cuda.synchronize()
     ids_ref, counts_ref, inv_ref = _reference_order(idx.cpu().numpy(), inp.table_rows, G)
+    assert np.array_equal(counts.cpu().numpy(), counts_ref)
+    assert np.array_equal(send_ids[: ids_ref.size].cpu().numpy().view(np.uint32), ids_ref)
+    assert np.array_equal(inverse.cpu().numpy(), inv_ref)
+
+
+def test_requests_many_sort_blocks(torch):
+    """300001 tokens of seeded row ids (more than 64 sort blocks per table):
+    send order, counts and inverse map exact."""
+    wl = synth.get_workload("tiny").with_shape(1, 300)
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp)
+    N, J, G = 300_001, wl.J, 3
+    rows = np.asarray(inp.table_rows, np.uint64)
+    u = synth.u64_stream(31, N * J).reshape(N, J)
+    # half the tokens on 64 rows per table, half anywhere: long and short segments
+    hot = (u >> np.uint64(40)) % np.uint64(2) == 0
+    idx = np.where(hot, u % np.uint64(64), u % rows[None, :]).astype(np.int32)
+    print(f"[shard requests] N={N} J={J} G={G}", flush=True)
+    send_ids, counts, inverse = _requests(torch, dp, H.to_dev(idx), G, N)
+    torch.cuda.synchronize()
+    ids_ref, counts_ref, inv_ref = _reference_order(idx, inp.table_rows, G)
     assert np.array_equal(counts.cpu().numpy(), counts_ref)
     assert np.array_equal(send_ids[: ids_ref.size].cpu().numpy().view(np.uint32), ids_ref)
     assert np.array_equal(inverse.cpu().numpy(), inv_ref)
