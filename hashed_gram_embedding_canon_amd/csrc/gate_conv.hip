@@ -15,11 +15,16 @@
 
 namespace engram {
 
-constexpr int kGcTokens = 64;   // R (32 and 128 measured slower)
-// 1: issue the first v loads before the gates are formed (measured 45 %
-// slower; kept off)
-#ifndef ENGRAM_GC_EARLY
-#define ENGRAM_GC_EARLY 0
+// R tokens per workgroup and v rows loaded ahead per lane.  Measured at the
+// 27B shape (d = 2560): R = 24 with 8 rows ahead 0.255 ms; R = 16, 32 and 48
+// 0.260-0.264; R = 64 with 2, 4, 8 and 12 rows ahead 0.290, 0.269, 0.265 and
+// 0.277; R = 128 0.282.
+#ifndef ENGRAM_GC_TOKENS
+#define ENGRAM_GC_TOKENS 24
+#endif
+constexpr int kGcTokens = ENGRAM_GC_TOKENS;
+#ifndef ENGRAM_GC_RING
+#define ENGRAM_GC_RING 8
 #endif
 // Non-temporal stores of Y (bit 2; bit 1 would make the v loads
 // non-temporal): Y is not read again here, and keeping it out of the 256 MB
@@ -30,6 +35,11 @@ constexpr int kGcTokens = 64;   // R (32 and 128 measured slower)
 #define ENGRAM_GC_NT 2
 #endif
 constexpr int kMaxTaps = 8;
+// feature tiles of partial sums loaded in one burst (d <= 16 * 256)
+#ifndef ENGRAM_GC_MAX_TILES
+#define ENGRAM_GC_MAX_TILES 16
+#endif
+constexpr int kGcMaxTiles = ENGRAM_GC_MAX_TILES;
 
 // raw 16 bytes of VEC features (8 bf16 or 4 fp32), widened at use
 template <int VEC, bool BF16>
@@ -92,22 +102,12 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
   const float inv_d = 1.0f / (float)d;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
 
-  // the first PD rows of v go out before the gates are formed (they do not
-  // depend on them), so the stream starts with its loads in flight
   const int f = threadIdx.x * VEC;
-  const int64_t tbeg = t0 - nh > 0 ? t0 - nh : 0;
   const int64_t tend = (t0 + R < a.T) ? t0 + R : a.T;
   const uint8_t* __restrict__ vsrc = a.v;
   const int64_t row0 = b * a.T;
-  constexpr int PD = 4;  // 8 measured slower (fewer waves fit)
+  constexpr int PD = ENGRAM_GC_RING;
   u32x4 ring[PD];
-#if ENGRAM_GC_EARLY
-  if (f < d) {
-#pragma unroll
-    for (int u = 0; u < PD; ++u)
-      if (tbeg + u < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + tbeg + u) * d + f);
-  }
-#endif
 
   // ---- gate of tokens t0-nh .. t0+R-1 of each branch (zero before the
   // sequence start); branch m has its own partial sums and stats
@@ -119,10 +119,25 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
     if (t >= 0 && t < a.T) {
       const float* p = a.partials + (m * N + b * a.T + t) * a.nkt * 3;
       float skk = 0.f, shk = 0.f, shh = 0.f;
-      for (int q = 0; q < a.nkt; ++q) {
-        skk += p[3 * q];
-        shk += p[3 * q + 1];
-        shh += p[3 * q + 2];
+      if (a.nkt <= kGcMaxTiles) {
+        // all of the token's partial sums in flight at once, added in tile order
+        float pv[kGcMaxTiles * 3];
+#pragma unroll
+        for (int q = 0; q < kGcMaxTiles * 3; ++q) pv[q] = q < a.nkt * 3 ? p[q] : 0.f;
+#pragma unroll
+        for (int q = 0; q < kGcMaxTiles; ++q) {
+          if (q < a.nkt) {
+            skk += pv[3 * q];
+            shk += pv[3 * q + 1];
+            shh += pv[3 * q + 2];
+          }
+        }
+      } else {
+        for (int q = 0; q < a.nkt; ++q) {
+          skk += p[3 * q];
+          shk += p[3 * q + 1];
+          shh += p[3 * q + 2];
+        }
       }
       const float rq = 1.0f / sqrtf(shh * inv_d + a.eps);
       const float rk = 1.0f / sqrtf(skk * inv_d + a.eps);
@@ -154,80 +169,123 @@ __global__ __launch_bounds__(1024) void gate_conv_kernel(GateConvArgs a) {
     for (int c = 0; c < VEC; ++c) win[i][c] = 0.f;
 
   const int64_t ystride = N * d * (BF16 ? 2 : 4);  // bytes between branch outputs
-  // v rows stream through a ring of PD tokens loaded ahead (each wave keeps
-  // PD 1 KB loads in flight; HBM latency, not bandwidth, bounds a shallower
-  // ring at this occupancy)
-#if !ENGRAM_GC_EARLY
+  // The window starts with the taps-1 tokens before t0 (zero gate before the
+  // sequence start); v rows then stream through a ring of PD tokens loaded
+  // ahead (each wave keeps PD 1 KB loads in flight).  Every load is
+  // unconditional, its row clamped into the tile, so the compiler can count
+  // the loads in flight instead of draining them at the loop's back edge.
+  // Load order: conv weights, halo, ring.  Waiting for the halo then also
+  // completes the weights, so no load from before the loop is still pending
+  // at its head (a pending one would make every iteration drain the ring).
+  const int64_t last = tend - 1;
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 halo[NW];
+  if constexpr (TAPS > 1) {
 #pragma unroll
-  for (int u = 0; u < PD; ++u)
-    if (tbeg + u < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + tbeg + u) * d + f);
-#endif
-  for (int64_t tb = tbeg; tb < tend; tb += PD) {
+    for (int i = 0; i < NW; ++i) {
+      const int64_t th = t0 - NW + i;
+      halo[i] = load_raw<VEC, BF16>(vsrc, (row0 + (th > 0 ? th : 0)) * d + f);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PD; ++u) {
+    const int64_t t = t0 + u < last ? t0 + u : last;
+    ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + t) * d + f);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (TAPS > 1) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int64_t th = t0 - NW + i;  // gate 0 before the sequence start
+      float cur[VEC];
+      widen<VEC, BF16>(halo[i], cur);
+      const float al0 = SINGLE ? alpha_s[(int)(th - (t0 - nh))] : 1.f;
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) win[NW - 1 - i][c] = th >= 0 ? al0 * cur[c] : 0.f;
+    }
+  }
+  const int n_out = (int)(tend - t0);
+  // conv, SiLU and residual of token t from its raw v, then the window shift
+  auto token = [&](int64_t t, const float* cur) __attribute__((always_inline)) {
+    const int li = (int)(t - (t0 - nh));
+    if constexpr (SINGLE) {
+      const float al0 = alpha_s[li];
+      float vt[VEC];
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) vt[c] = al0 * cur[c];
+      float out[VEC];
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        float z = w[c][0] * vt[c];
+#pragma unroll
+        for (int k = 1; k < TAPS; ++k) z += w[c][k] * win[k - 1][c];
+        // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
+        out[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) + vt[c];
+      }
+      store_vec<VEC, BF16>(a.y, (row0 + t) * d + f, out);
+#pragma unroll
+      for (int k = NW - 1; k > 0; --k)
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) win[k][c] = win[k - 1][c];
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) win[0][c] = vt[c];
+    } else {
+      // weighted taps, shared by the branches
+      float p[TAPS][VEC];
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        p[0][c] = w[c][0] * cur[c];
+#pragma unroll
+        for (int k = 1; k < TAPS; ++k) p[k][c] = w[c][k] * win[k - 1][c];
+      }
+      uint8_t* ydst = a.y;
+      for (int m = 0; m < nbr; ++m, ydst += ystride) {
+        const float* al = alpha_s + m * RH + li;  // al[-k] = alpha_m(t-k)
+        float out[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) {
+          float z = al[0] * p[0][c];
+#pragma unroll
+          for (int k = 1; k < TAPS; ++k) z += al[-k] * p[k][c];
+          // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
+          out[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) + al[0] * cur[c];
+        }
+        store_vec<VEC, BF16>(ydst, (row0 + t) * d + f, out);
+      }
+#pragma unroll
+      for (int k = NW - 1; k > 0; --k)
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) win[k][c] = win[k - 1][c];
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) win[0][c] = cur[c];
+    }
+  };
+  // whole groups of PD tokens: one path, no branch inside
+  const int n_full = n_out - n_out % PD;
+  for (int i = 0; i < n_full; i += PD) {
 #pragma unroll
     for (int u = 0; u < PD; ++u) {
-      const int64_t t = tb + u;
-      if (t < tend) {
-        float cur[VEC];
-        widen<VEC, BF16>(ring[u], cur);
-        if (t + PD < tend) ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + t + PD) * d + f);
-        if constexpr (SINGLE) {
-          const int li = (int)(t - (t0 - nh));
-          const float al0 = alpha_s[li];
-          float vt[VEC];
-#pragma unroll
-          for (int c = 0; c < VEC; ++c) vt[c] = al0 * cur[c];
-          if (t >= t0) {
-            float out[VEC];
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-              float z = w[c][0] * vt[c];
-#pragma unroll
-              for (int i = 1; i < TAPS; ++i) z += w[c][i] * win[i - 1][c];
-              // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
-              out[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) + vt[c];
-            }
-            store_vec<VEC, BF16>(a.y, (row0 + t) * d + f, out);
-          }
-#pragma unroll
-          for (int i = NW - 1; i > 0; --i)
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) win[i][c] = win[i - 1][c];
-#pragma unroll
-          for (int c = 0; c < VEC; ++c) win[0][c] = vt[c];
-          continue;
-        }
-        if (t >= t0) {
-          // weighted taps, shared by the branches
-          float p[TAPS][VEC];
-#pragma unroll
-          for (int c = 0; c < VEC; ++c) {
-            p[0][c] = w[c][0] * cur[c];
-#pragma unroll
-            for (int i = 1; i < TAPS; ++i) p[i][c] = w[c][i] * win[i - 1][c];
-          }
-          const int li = (int)(t - (t0 - nh));
-          uint8_t* ydst = a.y;
-          for (int m = 0; m < nbr; ++m, ydst += ystride) {
-            const float* al = alpha_s + m * RH + li;  // al[-i] = alpha_m(t-i)
-            float out[VEC];
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-              float z = al[0] * p[0][c];
-#pragma unroll
-              for (int i = 1; i < TAPS; ++i) z += al[-i] * p[i][c];
-              // SiLU with the hardware exp2 and reciprocal (about 1 ulp each)
-              out[c] = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) + al[0] * cur[c];
-            }
-            store_vec<VEC, BF16>(ydst, (row0 + t) * d + f, out);
-          }
-        }
-#pragma unroll
-        for (int i = NW - 1; i > 0; --i)
-#pragma unroll
-          for (int c = 0; c < VEC; ++c) win[i][c] = win[i - 1][c];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) win[0][c] = cur[c];
+      const int64_t t = t0 + i + u;
+      float cur[VEC];
+      widen<VEC, BF16>(ring[u], cur);
+      // the slot's next load after its value is read, into the same registers
+      // (hoisted above the read, it would need others and a copy that waits
+      // for it at the loop's back edge)
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int64_t tn = t + PD < last ? t + PD : last;
+        ring[u] = load_raw<VEC, BF16>(vsrc, (row0 + tn) * d + f);
       }
+      token(t, cur);
+    }
+  }
+  // the rest of a tile at the end of a sequence: already in the ring
+#pragma unroll
+  for (int u = 0; u < PD; ++u) {
+    if (n_full + u < n_out) {
+      float cur[VEC];
+      widen<VEC, BF16>(ring[u], cur);
+      token(t0 + n_full + u, cur);
     }
   }
 }
