@@ -124,6 +124,7 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   __shared__ floatx4 st_s[R + 2 * NH + PD];
   __shared__ float pdw[R][kBwMaxWaves];
   __shared__ float dal_s[R];
+  __shared__ float sc_s[R];  // the tokens' fp16 range factors (1 without)
   const int64_t b = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * R;
   const int d = a.d;
@@ -135,6 +136,8 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
     st_s[i] = (u >= 0 && u < T) ? *reinterpret_cast<const floatx4*>(a.stats + (b * T + u) * 4)
                                 : floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  for (int i = threadIdx.x; i < R; i += blockDim.x)
+    sc_s[i] = a.scale && t0 + i < T ? a.scale[b * T + t0 + i] : 1.f;
   __syncthreads();
 
   const int f = threadIdx.x * 4;  // blockDim.x * 4 == d
@@ -152,6 +155,9 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int i = 0; i < TAPS; ++i) w[c][i] = a.conv_w[(f + c) * TAPS + i];
+  // the weights' loads before the ring's, so that none of them is pending at
+  // the loop head (one would make every iteration wait for the whole ring)
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- pass A
   float vtw[NW][4];  // gated value at u-1-i
@@ -165,18 +171,17 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   }
   const int64_t ubeg = t0 - NH;
   // Ring of raw v / G rows: token u sits in slot (u - ubeg) % RS from its
-  // load at step u - PD until finish at step u + NH (RS > PD + NH); zero
-  // outside [0, T), and G zero before t0.
+  // load at step u - PD until finish at step u + NH (RS > PD + NH).  The
+  // loads are unconditional, the row clamped into [0, T), so that the
+  // compiler counts them in flight instead of draining the ring: outside
+  // [0, T) the gate is zero, and G enters only tokens in [t0, T).
   constexpr int RS = (PD + NH + 1 <= 8) ? 8 : 16;
   static_assert(RS % kBwBatch == 0 && R % RS == 0, "");
   raw4_t<BF16> rv[RS], rg[RS];
   auto fetch = [&](int64_t u, raw4_t<BF16>& v, raw4_t<BF16>& g) __attribute__((always_inline)) {
-    v = raw4_t<BF16>{};
-    g = raw4_t<BF16>{};
-    if (u >= 0 && u < T) {
-      v = ld4_raw<BF16>(a.v, (row0 + u) * d + f);
-      if (u >= t0) g = ld4_raw<BF16>(a.dy, (row0 + u) * d + f);
-    }
+    const int64_t uc = u < 0 ? 0 : (u < T ? u : T - 1);
+    v = ld4_raw<BF16>(a.v, (row0 + uc) * d + f);
+    g = ld4_raw<BF16>(a.dy, (row0 + uc) * d + f);
   };
 #pragma unroll
   for (int k = 0; k < PD; ++k) fetch(ubeg + k, rv[k], rg[k]);
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       dv[c] = alpha * acc;
     }
     pb[pslot] = pd;
-    const float sc = a.scale ? a.scale[row0 + t] : 1.f;  // the token's fp16 range factor
+    const float sc = sc_s[t - t0];  // the token's fp16 range factor
     if constexpr (!MULTI) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) dv[c] *= sc;
@@ -332,11 +337,9 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
     raw4_t<BF16> rh[UB], rk[UB];
 #pragma unroll
     for (int q = 0; q < UB; ++q) {
-      const int64_t t = t0 + i0 + q;
-      if (t < tend) {
-        rh[q] = ld4_raw<BF16>(a.h, (row0 + t) * d + f);
-        rk[q] = ld4_raw<BF16>(a.k, (row0 + t) * d + f);
-      }
+      const int64_t t = t0 + i0 + q < tend ? t0 + i0 + q : tend - 1;  // unconditional, clamped
+      rh[q] = ld4_raw<BF16>(a.h, (row0 + t) * d + f);
+      rk[q] = ld4_raw<BF16>(a.k, (row0 + t) * d + f);
     }
 #pragma unroll
     for (int q = 0; q < UB; ++q) {
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       float hv[4], kv[4], dk[4];
       widen4<BF16>(rh[q], hv);
       widen4<BF16>(rk[q], kv);
-      const float sc = a.scale ? a.scale[row0 + t] : 1.f;
+      const float sc = sc_s[i0 + q];
 #pragma unroll
       for (int c = 0; c < 4; ++c) dk[c] = ca * gqk[c] * hv[c] - cb * kv[c];
       float dks[4];
@@ -429,7 +432,8 @@ hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s) {
       return narrow ? launch_bwd_taps<true, true, 768, true>(a, grid, threads, s)
                     : launch_bwd_taps<true, true, 1024, true>(a, grid, threads, s);
     }
-    if (!params) return launch_bwd_taps<true, false, 1024, false>(a, grid, threads, s);
+    if (!params) return narrow ? launch_bwd_taps<true, false, 768, false>(a, grid, threads, s)
+                               : launch_bwd_taps<true, false, 1024, false>(a, grid, threads, s);
     return narrow ? launch_bwd_taps<true, true, 768, false>(a, grid, threads, s)
                   : launch_bwd_taps<true, true, 1024, false>(a, grid, threads, s);
   }
@@ -439,7 +443,8 @@ hipError_t launch_bwd_gate_conv(const BwdArgs& a, hipStream_t s) {
     return narrow ? launch_bwd_taps<false, true, 768, true>(a, grid, threads, s)
                   : launch_bwd_taps<false, true, 1024, true>(a, grid, threads, s);
   }
-  if (!params) return launch_bwd_taps<false, false, 1024, false>(a, grid, threads, s);
+  if (!params) return narrow ? launch_bwd_taps<false, false, 768, false>(a, grid, threads, s)
+                             : launch_bwd_taps<false, false, 1024, false>(a, grid, threads, s);
   return narrow ? launch_bwd_taps<false, true, 768, false>(a, grid, threads, s)
                 : launch_bwd_taps<false, true, 1024, false>(a, grid, threads, s);
 }
