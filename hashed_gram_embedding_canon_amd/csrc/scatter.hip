@@ -12,10 +12,14 @@
 // order varies run to run).
 #include "kernels.h"
 
-// 1: the segmented reduce reads the per-token gradient rows with
-// non-temporal loads (each is read once).
+// bit 1: the segmented reduce reads the per-token gradient rows with
+// non-temporal loads (each is read once); bit 2: it writes the sparse rows
+// with non-temporal stores
 #ifndef ENGRAM_SCATTER_NT
 #define ENGRAM_SCATTER_NT 1
+#endif
+#ifndef ENGRAM_RED_SEGS
+#define ENGRAM_RED_SEGS 256
 #endif
 // 1: the groups of the whole grid take the short segments in a grid-stride
 // walk (all of them in one window of the output at a time); 0: each block
@@ -460,12 +464,12 @@ __global__ __launch_bounds__(256) void seg_inverse_kernel(const uint32_t* __rest
 // first tokens of its next batch loading behind them, and sums the rest of a
 // segment's elements in sorted order.  Both orders depend only on D, so
 // results repeat run to run.
-constexpr int kSegsPerBlock = 1024;
+constexpr int kSegsPerBlock = ENGRAM_RED_SEGS;
 constexpr int kLongSeg = 32;
 constexpr int kRedBatch = ENGRAM_RED_BATCH;
 
 __device__ __forceinline__ floatx4 load_row_piece(const float* p) {
-#if ENGRAM_SCATTER_NT
+#if (ENGRAM_SCATTER_NT & 1) != 0
   return __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
 #else
   return *reinterpret_cast<const floatx4*>(p);
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
                                                          const uint64_t* __restrict__ seg_key,
                                                          const uint32_t* __restrict__ seg_tok,
                                                          const uint32_t* __restrict__ total) {
-  constexpr int kScan = kSegsPerBlock / 256;
+  constexpr int kScan = (kSegsPerBlock + 255) / 256;
   __shared__ floatx4 part[256];  // G * D/4 = 4 * S * D/4 <= 256
   __shared__ uint32_t lst[kSegsPerBlock];
   __shared__ uint32_t nl;
@@ -507,7 +511,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     const int j = (int)(key >> 32);
     const int64_t r = (int64_t)(key & 0xFFFFFFFFu);
     if (MODE == ENGRAM_GRAD_SORTED_SPARSE) {
-      *reinterpret_cast<floatx4*>(a.rows_out + (int64_t)seg * a.D + col * 4) = acc;
+      floatx4* p = reinterpret_cast<floatx4*>(a.rows_out + (int64_t)seg * a.D + col * 4);
+      if constexpr ((ENGRAM_SCATTER_NT & 2) != 0)
+        __builtin_nontemporal_store(acc, p);
+      else
+        *p = acc;
       if (col == 0) a.keys_out[seg] = (int64_t)key;
     } else {
       floatx4* dst = reinterpret_cast<floatx4*>(a.dense[j] + r * a.D + col * 4);
@@ -524,7 +532,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 #pragma unroll
     for (int c = 0; c < kScan; ++c) {
       const uint32_t s = s0 + c * 256 + threadIdx.x;
-      len[c] = s < s1 ? start_of(s + 1) - seg_start[s] : 0u;
+      len[c] = s < s1 && c * 256 + (int)threadIdx.x < kSegsPerBlock ? start_of(s + 1) - seg_start[s] : 0u;
     }
 #pragma unroll
     for (int c = 0; c < kScan; ++c)
