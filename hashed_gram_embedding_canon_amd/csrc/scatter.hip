@@ -40,7 +40,10 @@ namespace engram {
 
 constexpr int kSortThreads = 256;
 constexpr int kSortWaves = kSortThreads / 64;
-constexpr int kSortItems = 16;
+#ifndef ENGRAM_SORT_ITEMS
+#define ENGRAM_SORT_ITEMS 16
+#endif
+constexpr int kSortItems = ENGRAM_SORT_ITEMS;  // keys per thread
 constexpr int kSortTile = kSortThreads * kSortItems;  // keys per block
 constexpr int kWaveRange = 64 * kSortItems;            // keys per wave
 // Up to this many blocks per table, each scatter block derives its digit
