@@ -85,6 +85,32 @@ def test_sorted_path_is_deterministic(torch):
     assert torch.equal(r1["keys"][:n], r2["keys"][:n]) and torch.equal(r1["rows"][:n], r2["rows"][:n])
 
 
+def test_table_grads_one_digit_sort(torch, oracle_lib):
+    """Tables of 251 rows: one 8-bit digit pass sorts the row ids (the first
+    pass, which reads idx itself, is also the last).  Every key exact, every
+    row against the oracle; most rows are hit by several tokens."""
+    import hashed_gram_embedding_canon_amd as eg
+    wl = dataclasses.replace(synth.get_workload("tiny"), rows=(251,) * 8).with_shape(2, 512)
+    print("[tiny bwd] 8 tables of 251 rows, B=2 T=512", flush=True)
+    modes = (eg.ENGRAM_GRAD_SORTED_SPARSE, eg.ENGRAM_GRAD_SORTED_DENSE)
+    inp, dp, bufs, out = _fwd_bwd(torch, wl, modes)
+    p = H.oracle_problem(inp)
+    ref = p.table_grad_dense(inp.dy)
+    idx = p.hash()
+    assert idx.max() < 251
+    keys, rows = _sparse_to_dict(out[eg.ENGRAM_GRAD_SORTED_SPARSE], wl.dim)
+    want = np.unique(np.concatenate([(np.int64(j) << 32) | idx[:, j].astype(np.int64)
+                                     for j in range(wl.J)]))
+    assert np.array_equal(keys, want)
+    ref_rows = np.stack([ref[int(k >> 32)][int(k & 0xFFFFFFFF)] for k in keys])
+    err = H.rel_l2(rows, ref_rows)
+    dense = out[eg.ENGRAM_GRAD_SORTED_DENSE]["dense"]
+    err_d = H.rel_l2(np.concatenate([d.cpu().numpy().astype(np.float64).ravel() for d in dense]),
+                     np.concatenate([r.ravel() for r in ref]))
+    print(f"  {len(keys)} keys for {idx.size} lookups: rel L2 {err:.2e} (dense {err_d:.2e})", flush=True)
+    assert err <= 1e-3 and err_d <= 1e-3, (err, err_d)
+
+
 def test_table_grads_one_long_segment_per_table(torch, oracle_lib):
     """A constant token stream: past the first few positions every table's
     keys are one segment of nearly N elements, summed by a whole block of lane

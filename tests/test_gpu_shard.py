@@ -63,9 +63,12 @@ def _reference_order(idx, table_rows, G):
     return ids, counts, inverse
 
 
-@pytest.mark.parametrize("name,B,T,G", [("tiny", 2, 300, 1), ("tiny", 2, 300, 3), ("small", 2, 2048, 8)])
-def test_requests_match_definition(torch, name, B, T, G):
+@pytest.mark.parametrize("name,B,T,G,rows", [("tiny", 2, 300, 1, None), ("tiny", 2, 300, 3, None),
+                                              ("small", 2, 2048, 8, None), ("tiny", 2, 300, 3, 251)])
+def test_requests_match_definition(torch, name, B, T, G, rows):
     wl = synth.get_workload(name).with_shape(B, T)
+    if rows is not None:  # one 8-bit digit pass sorts the row ids
+        wl = dataclasses.replace(wl, rows=(rows,) * wl.J)
     inp = synth.Inputs(wl)
     dp = H.DeviceProblem(inp)
     idx = dp.hash()
