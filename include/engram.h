@@ -374,8 +374,9 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* par
  * buffers before the copies end).  With ENGRAM_PLAN_REUSE in plan->flags the plan fields are
  * taken as given (a plan-only call made them) and only gather and copy run.
  *   canon_map_host: host [vocab]; tokens_host: host [B][T];
- *   host_tables: NULL (plan only) or host [J] pointers to [M_j][D] dtype
- *   (pinned memory makes the copy a true async DMA).
+ *   host_tables: NULL (plan only) or host [J] pointers to [M_j][D] dtype, in
+ *   any host memory (pageable is fine: host threads gather the rows from them
+ *   into the pinned staging buffer, which is what the async copy reads).
  */
 engram_status engram_prefetch_plan(const engram_config* cfg, const int32_t* canon_map_host,
                                    const int32_t* tokens_host, int64_t B, int64_t T,
