@@ -822,6 +822,80 @@ def copy_calibration(nbytes: int):
                       "GBps_read_plus_write": r["GBps"]}), flush=True)
 
 
+def bench_library_gemm(args):
+    """The three contractions of the 27B shape as plain library products
+    (torch.matmul on hipBLASLt, no epilogue work) beside this library's
+    kernels, in one process, rounds alternated: the projection e W_KV
+    (bf16 out; ours adds the gate sums and reads h), de = [dk|dv] W_KV^T
+    (fp16 operands, fp16 out; ours writes fp32) and dW = [dk|dv]^T e over the
+    tokens (bf16; ours sums token chunks in fp32)."""
+    import statistics
+
+    import torch
+
+    import hashed_gram_embedding_canon_amd as eg
+    import synth
+    from tests import harness as H
+    wl = synth.get_workload("engram27b")
+    N, dm, d = wl.n_tokens, wl.d_mem, wl.hidden
+    inp = synth.Inputs(wl)
+    dp = H.DeviceProblem(inp)
+    bufs = dp.alloc_saved(("idx", "stats", "k", "v"))
+    dp.forward(bufs)
+    dy = H.to_dev(inp.dy)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    e = torch.randn(N, dm, device="cuda", dtype=torch.bfloat16, generator=g)
+    w = torch.randn(dm, 2 * d, device="cuda", dtype=torch.bfloat16, generator=g)
+    x16 = torch.randn(N, 2 * d, device="cuda", dtype=torch.float16, generator=g)
+    wt16 = torch.randn(2 * d, dm, device="cuda", dtype=torch.float16, generator=g)
+    xt = torch.randn(2 * d, N, device="cuda", dtype=torch.bfloat16, generator=g)  # contiguous
+    lib = {"projection": lambda: torch.matmul(e, w), "de": lambda: torch.matmul(x16, wt16),
+           "dW": lambda: torch.matmul(xt, e)}
+    y = torch.empty(wl.B, wl.T, d, dtype=dp.tdtype, device="cuda")
+    ws_f = dp.workspace(eg.ENGRAM_OP_FORWARD)
+    ws_b = dp.workspace(eg.ENGRAM_OP_BACKWARD_PARAMS)
+    res = {f"hipblaslt_{k}": [] for k in lib}
+    res.update({"ours_proj_gemm": [], "ours_de_gemm": [], "ours_dw_gemm": []})
+    tg = eg.engram_table_grad()
+    tg.mode = eg.ENGRAM_GRAD_SORTED_SPARSE
+    cap = N * wl.J
+    kb = torch.empty(cap, dtype=torch.int64, device="cuda")
+    rb = torch.empty(cap, wl.dim, dtype=torch.float32, device="cuda")
+    cb = torch.empty(1, dtype=torch.int64, device="cuda")
+    tg.keys, tg.rows, tg.count = kb.data_ptr(), rb.data_ptr(), cb.data_ptr()
+    pres = {"w_kv": torch.empty(2 * d, dm, device="cuda")}
+    pg = eg.make_param_grad(**pres)
+    sv = eg.make_saved(**bufs)
+    for r in range(args.steps if args.steps < 20 else 5):
+        for k, fn in lib.items():
+            for _ in range(2):
+                fn()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            for _ in range(5):
+                fn()
+            a1.record()
+            torch.cuda.synchronize()
+            res[f"hipblaslt_{k}"].append(a0.elapsed_time(a1) / 5)
+        eg.engram_profile_reset()
+        eg.engram_profile_enable(True)
+        for _ in range(5):
+            dp.forward(ws=ws_f, y=y)
+            eg.engram_backward(dp.cfg, dp.params, dp.hidden, dy, B=dp.B, T=dp.T, saved=sv, table_out=tg,
+                               param_out=pg, workspace=ws_b)
+        torch.cuda.synchronize()
+        eg.engram_profile_enable(False)
+        prof = eg.engram_profile_read()
+        for k in ("proj_gemm", "de_gemm", "dw_gemm"):
+            n, tot = prof[k]
+            res[f"ours_{k}"].append(tot / n)
+        log(f"[bench-lib] round {r}: " + ", ".join(f"{k} {v[-1]:.3f}" for k, v in res.items()))
+    med = {k: round(statistics.median(v), 4) for k, v in res.items()}
+    print(json.dumps({"metric": "27B-shape contractions: hipBLASLt plain products beside this library's kernels",
+                      "shapes": {"projection": [N, dm, 2 * d], "de": [N, 2 * d, dm], "dW": [2 * d, N, dm]},
+                      "median_ms": med, "rounds": len(res["ours_proj_gemm"])}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -836,6 +910,8 @@ def main():
     ap.add_argument("--fused-gather", action="store_true",
                     help="let the projection read the table rows itself (ENGRAM_FLAG_FUSED_GATHER) "
                          "instead of gathering e into the workspace first")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the three 27B-shape contractions as hipBLASLt products beside ours")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -888,6 +964,9 @@ def main():
         return
     if args.workload == "host100b":
         bench_host(args)
+        return
+    if args.library_gemm:
+        bench_library_gemm(args)
         return
 
     import torch
