@@ -43,11 +43,13 @@ def _sparse_to_dict(res, D):
     return keys, rows
 
 
-@pytest.mark.parametrize("dtype,B,T", [("f32", 1, 512), ("f32", 3, 77), ("bf16", 2, 300)])
-def test_tiny_table_grads(torch, oracle_lib, dtype, B, T):
+@pytest.mark.parametrize("dtype,B,T,hidden", [("f32", 1, 512, 256), ("f32", 3, 77, 256), ("bf16", 2, 300, 256),
+                                              ("bf16", 1, 200, 4096)])
+def test_tiny_table_grads(torch, oracle_lib, dtype, B, T, hidden):
+    """hidden 4096: 1024 lanes per workgroup in the elementwise backward."""
     import hashed_gram_embedding_canon_amd as eg
-    wl = dataclasses.replace(synth.get_workload("tiny"), dtype=dtype).with_shape(B, T)
-    print(f"[tiny bwd {dtype}] B={B} T={T}", flush=True)
+    wl = dataclasses.replace(synth.get_workload("tiny"), dtype=dtype, hidden=hidden).with_shape(B, T)
+    print(f"[tiny bwd {dtype}] B={B} T={T} d={hidden}", flush=True)
     modes = (eg.ENGRAM_GRAD_SORTED_SPARSE, eg.ENGRAM_GRAD_SORTED_DENSE, eg.ENGRAM_GRAD_ATOMIC_DENSE)
     inp, dp, bufs, out = _fwd_bwd(torch, wl, modes)
     p = H.oracle_problem(inp)

@@ -83,6 +83,8 @@ def _check(res, ref, bf16, rows=None, tag=""):
     ("f32", 3, 77, 32, 256, True),
     ("bf16", 2, 300, 32, 256, False),
     ("bf16", 2, 700, 64, 512, True),   # 4 x 2 output tiles of dW
+    ("bf16", 1, 200, 32, 4096, True),  # 1024 lanes per workgroup in the elementwise backward
+    ("f32", 1, 130, 32, 4096, False),
 ])
 def test_param_grads_dense(torch, oracle_lib, dtype, B, T, dim, hidden, gammas):
     wl = dataclasses.replace(synth.get_workload("tiny"), dtype=dtype, dim=dim,
