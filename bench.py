@@ -901,6 +901,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="untimed forward steps for this long before the warmup steps, so that "
+                         "the GPU clock is past its power-management transient (0: none)")
     ap.add_argument("--workload", default="engram27b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1006,10 +1009,23 @@ def main():
         dp.tokens = batches[i % len(batches)]
         dp.forward(saved, ws=ws, y=y)
 
+    # After any idle period of 0.1 s or more the GPU's power management first
+    # boosts, then throttles below its steady clock and settles within ~15
+    # steps (~30 ms): the first steps after idle run up to 25 % slower.  Forward
+    # steps over the same batches run untimed for --settle-ms first, so the
+    # timed steps measure the steady state of a running job.
+    settle_steps = 0
+    t = time.perf_counter()
+    while (time.perf_counter() - t) * 1e3 < args.settle_ms:
+        for _ in range(5):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps); {len(batches)} distinct token batches resident")
+    log(f"[bench] settle ({settle_steps} steps) and warmup ({args.warmup} steps) done; "
+        f"{len(batches)} distinct token batches resident")
 
     # headline: no library timing events inside; one event between steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -1100,6 +1116,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms, 4),
         "ms_per_step_median": round(statistics.median(step_ms), 4),
         "ms_per_step_min": round(min(step_ms), 4),
