@@ -825,7 +825,7 @@ def copy_calibration(nbytes: int):
 def bench_library_gemm(args):
     """The three contractions of the 27B shape as plain library products
     (torch.matmul on hipBLASLt, no epilogue work) beside this library's
-    kernels, in one process, rounds alternated: the projection e W_KV
+    kernels, in one process, passes alternated: the projection e W_KV
     (bf16 out; ours adds the gate sums and reads h), de = [dk|dv] W_KV^T
     (fp16 operands, fp16 out; ours writes fp32) and dW = [dk|dv]^T e over the
     tokens (bf16; ours sums token chunks in fp32)."""
@@ -889,11 +889,11 @@ def bench_library_gemm(args):
         for k in ("proj_gemm", "de_gemm", "dw_gemm"):
             n, tot = prof[k]
             res[f"ours_{k}"].append(tot / n)
-        log(f"[bench-lib] round {r}: " + ", ".join(f"{k} {v[-1]:.3f}" for k, v in res.items()))
+        log(f"[bench-lib] pass {r}: " + ", ".join(f"{k} {v[-1]:.3f}" for k, v in res.items()))
     med = {k: round(statistics.median(v), 4) for k, v in res.items()}
     print(json.dumps({"metric": "27B-shape contractions: hipBLASLt plain products beside this library's kernels",
                       "shapes": {"projection": [N, dm, 2 * d], "de": [N, 2 * d, dm], "dW": [2 * d, N, dm]},
-                      "median_ms": med, "rounds": len(res["ours_proj_gemm"])}), flush=True)
+                      "median_ms": med, "passes": len(res["ours_proj_gemm"])}), flush=True)
 
 
 def main():
