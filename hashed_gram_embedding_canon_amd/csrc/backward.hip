@@ -37,6 +37,13 @@
 
 namespace engram {
 
+// Where the conv weights and the tap sums live: 0 registers; 1 LDS in the
+// 1024-lane variants; 2 also in the 768-lane multi-branch variants (the
+// shapes whose registers run out; the others keep them in registers)
+#ifndef ENGRAM_BW_LDS
+#define ENGRAM_BW_LDS 2
+#endif
+
 constexpr int kBwTokens = 64;   // R
 constexpr int kBwBatch = 8;     // tokens per dalpha reduction batch
 constexpr int kBwMaxWaves = 16; // d / 4 / 64
@@ -125,6 +132,15 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   __shared__ float pdw[R][kBwMaxWaves];
   __shared__ float dal_s[R];
   __shared__ float sc_s[R];  // the tokens' fp16 range factors (1 without)
+  // With 1024 lanes (128 registers each), and in the multi-branch variants,
+  // the conv weights and the tap sums live in LDS, one slot per lane, read
+  // and updated where they are used: held in registers they made the kernel
+  // spill, and every reload from scratch waited for the whole ring of v / G
+  // loads.  Same arithmetic in the same order, so the same results.
+  constexpr bool kLdsW = ENGRAM_BW_LDS && (MAXT > 768 || (ENGRAM_BW_LDS > 1 && MULTI)) &&
+                         TAPS * 4 * MAXT * 4 * (PARAMS ? 2 : 1) <= 136 * 1024;
+  __shared__ float w_s[kLdsW ? TAPS * 4 * MAXT : 1];               // [i][c][lane]
+  __shared__ float dcw_s[kLdsW && PARAMS ? TAPS * 4 * MAXT : 1];   // [i][c][lane]
   const int64_t b = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * R;
   const int d = a.d;
@@ -150,11 +166,27 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   const int64_t ld = MULTI ? (int64_t)(a.branches + 1) * d : 2 * (int64_t)d;
   const int dk_col = MULTI ? a.branch * d : 0;
   const int dv_col = MULTI ? a.branches * d : d;
-  float w[4][TAPS];
+  float w[kLdsW ? 1 : 4][kLdsW ? 1 : TAPS];
+  // a lane's own LDS slot (written and read by that lane only)
+  auto lslot = [&](float* arr, int c, int i) __attribute__((always_inline)) -> float* {
+    return reinterpret_cast<float*>(arr) + (i * 4 + c) * MAXT + threadIdx.x;
+  };
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int i = 0; i < TAPS; ++i) w[c][i] = a.conv_w[(f + c) * TAPS + i];
+    for (int i = 0; i < TAPS; ++i) {
+      const float x = a.conv_w[(f + c) * TAPS + i];
+      if constexpr (kLdsW)
+        *lslot(w_s, c, i) = x;
+      else
+        w[c][i] = x;
+    }
+  auto W = [&](int c, int i) __attribute__((always_inline)) -> float {
+    if constexpr (kLdsW)
+      return *lslot(w_s, c, i);
+    else
+      return w[c][i];
+  };
   // the weights' loads before the ring's, so that none of them is pending at
   // the loop head (one would make every iteration wait for the whole ring)
   __builtin_amdgcn_sched_barrier(0);
@@ -190,13 +222,26 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
   for (int k = 0; k < kBwBatch; ++k) pb[k] = 0.f;
   // PARAMS: sum over this block's tokens of dz_u vt_{u-i} (tap i); written
   // out after pass A
-  float dcw[PARAMS ? 4 : 1][PARAMS ? TAPS : 1];
+  float dcw[PARAMS && !kLdsW ? 4 : 1][PARAMS && !kLdsW ? TAPS : 1];
   if constexpr (PARAMS) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int i = 0; i < TAPS; ++i) dcw[c][i] = 0.f;
+      for (int i = 0; i < TAPS; ++i) {
+        if constexpr (kLdsW)
+          *lslot(dcw_s, c, i) = 0.f;
+        else
+          dcw[c][i] = 0.f;
+      }
   }
+  auto dcw_add = [&](int c, int i, float x) __attribute__((always_inline)) {
+    if constexpr (kLdsW) {
+      float* q = lslot(dcw_s, c, i);
+      *q = *q + x;
+    } else {
+      dcw[c][i] += x;
+    }
+  };
   float* const pdst = PARAMS && a.pacc ? a.pacc + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) *
                                                       d * (TAPS + 1) + (int64_t)f * (TAPS + 1)
                                        : nullptr;
@@ -214,9 +259,9 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
     const bool live = u >= t0 && u < T;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float z = w[c][0] * vt[c];
+      float z = W(c, 0) * vt[c];
 #pragma unroll
-      for (int i = 1; i < TAPS; ++i) z += w[c][i] * vtw[i - 1][c];
+      for (int i = 1; i < TAPS; ++i) z += W(c, i) * vtw[i - 1][c];
       const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
       dz[c] = live ? G[c] * sg * (1.0f + z * (1.0f - sg)) : 0.f;
     }
@@ -225,9 +270,9 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
       if (u < tend) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          dcw[c][0] += dz[c] * vt[c];
+          dcw_add(c, 0, dz[c] * vt[c]);
 #pragma unroll
-          for (int i = 1; i < TAPS; ++i) dcw[c][i] += dz[c] * vtw[i - 1][c];
+          for (int i = 1; i < TAPS; ++i) dcw_add(c, i, dz[c] * vtw[i - 1][c]);
         }
       }
     }
@@ -259,7 +304,7 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
     for (int c = 0; c < 4; ++c) {
       float acc = G[c];
 #pragma unroll
-      for (int i = 0; i < TAPS; ++i) acc += w[c][i] * dzw[NH - i][c];
+      for (int i = 0; i < TAPS; ++i) acc += W(c, i) * dzw[NH - i][c];
       pd += acc * v[c];
       dv[c] = alpha * acc;
     }
@@ -311,7 +356,12 @@ __global__ __launch_bounds__(MAXT) void bwd_gate_conv_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int i = 0; i < TAPS; ++i) pdst[c * (TAPS + 1) + i] = dcw[c][i];
+        for (int i = 0; i < TAPS; ++i) {
+          if constexpr (kLdsW)
+            pdst[c * (TAPS + 1) + i] = *lslot(dcw_s, c, i);
+          else
+            pdst[c * (TAPS + 1) + i] = dcw[c][i];
+        }
     }
   }
   __syncthreads();
