@@ -37,6 +37,11 @@ constexpr int32_t kFwdStageBytes = ENGRAM_FWD_STAGE_BYTES;
 #define ENGRAM_GEMM_PERSISTENT 1
 #endif
 constexpr int32_t kBwdStageBytes = 128;
+// token tiles per group in the de contraction's tile walk (its five f-tiles
+// per token tile): 2 measured 2-3.5 % faster than the projection's 4
+#ifndef ENGRAM_DE_GROUP_M
+#define ENGRAM_DE_GROUP_M 2
+#endif
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 engram_status check_config(const engram_config* c, Shape* s) {
@@ -713,7 +718,7 @@ engram_status engram_backward(const engram_config* cfg, const engram_params* p,
     ga.M = N;
     ga.F = s.d_mem;
     ga.K = (int32_t)cols;
-    ga.group_m = 4;
+    ga.group_m = ENGRAM_DE_GROUP_M;
     ga.stage_bytes = kBwdStageBytes;
     ga.persistent = ENGRAM_GEMM_PERSISTENT;
     ga.c_out = w.de;
