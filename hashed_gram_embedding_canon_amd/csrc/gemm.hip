@@ -116,21 +116,36 @@ constexpr int kLoadGroups = ENGRAM_GEMM_LOAD_GROUPS;
 #ifndef ENGRAM_GEMM_V_NT
 #define ENGRAM_GEMM_V_NT 0
 #endif
+// Row stores of a value tile's epilogue unrolled this far (all 16 LDS reads
+// of a round in flight): 1.485 ms per projection against 1.494 ms with 4.
+#ifndef ENGRAM_GEMM_VSTORE_UNROLL
+#define ENGRAM_GEMM_VSTORE_UNROLL 16
+#endif
+constexpr int kVStoreUnroll = ENGRAM_GEMM_VSTORE_UNROLL;
+#ifndef ENGRAM_GEMM_PREFETCH_TILE
+#define ENGRAM_GEMM_PREFETCH_TILE 1
+#endif
+// Load stage 0 of a workgroup's next tile while this one finishes (bf16
+// key/value projection): value tiles in the load slots of their last K stage,
+// key tiles once the first half of their gate sums has freed that buffer.
 
 #ifdef ENGRAM_GEMM_TRACE
 // Measurement build only: shader-clock stamps of workgroups 0..31 (wave 0),
-// per tile: start, K loop done, epilogue done; per stage of their second tile.
-constexpr int kTrWG = 32, kTrTiles = 48, kTrStages = 96;
-__device__ uint64_t g_gemm_trace[kTrWG * kTrTiles * 3 + kTrWG * kTrStages + 2];
+// per tile: start, K loop done, epilogue done, first stage landed, epilogue
+// midpoint, epilogue stores issued, set-up done, first-stage wait done, key
+// tiles' first h part landed; per stage of their second tile.
+constexpr int kTrWG = 32, kTrTiles = 48, kTrStages = 96, kTrPer = 9;
+__device__ uint64_t g_gemm_trace[kTrWG * kTrTiles * kTrPer + kTrWG * kTrStages + 2];
 #define ENGRAM_TRACE_TILE(which)                                                          \
   do {                                                                                    \
     if (threadIdx.x == 0 && blockIdx.x < kTrWG && it_ < kTrTiles)                         \
-      g_gemm_trace[(blockIdx.x * kTrTiles + it_) * 3 + (which)] = __builtin_readcyclecounter(); \
+      g_gemm_trace[(blockIdx.x * kTrTiles + it_) * kTrPer + (which)] =                    \
+          __builtin_readcyclecounter();                                                   \
   } while (0)
 #define ENGRAM_TRACE_STAGE(k)                                                             \
   do {                                                                                    \
     if (threadIdx.x == 0 && blockIdx.x < kTrWG && it_ == 1 && (k) < kTrStages)           \
-      g_gemm_trace[kTrWG * kTrTiles * 3 + blockIdx.x * kTrStages + (k)] =                \
+      g_gemm_trace[kTrWG * kTrTiles * kTrPer + blockIdx.x * kTrStages + (k)] =           \
           __builtin_readcyclecounter();                                                   \
   } while (0)
 // per wave (lane 0), workgroups 0..7, second tile: stamp w of stage k
@@ -155,6 +170,9 @@ __device__ uint64_t g_gemm_trace2[kTr2WG * kTr2Stages * 4 * 3];
 #endif
 // what the load slots of a K stage carry
 constexpr int kSlotNext = 0, kSlotNone = 1, kSlotH = 2;  // kSlotH + X: part X of h
+// the last two K stages with the next-tile prefetch: h part 0 (key tiles),
+// the next tile's stage 0 (value tiles), chosen per tile without branches
+constexpr int kSlotTail = -1;
 template <int X>
 using SlotHPart = std::integral_constant<int, kSlotH + X>;
 
@@ -193,22 +211,44 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const int64_t tiles_m = (g.M + kBT - 1) / kBT;
   const int tx = xcd < tiles_m ? (int)((tiles_m - 1 - xcd) / 8 + 1) : 0;  // token tiles of list x
   const int nslots = tx * tiles_f;
+  auto tile_of = [&](int sl, int64_t& tm_o, int& f0_o) __attribute__((always_inline)) {
+    const int gm = g.group_m;
+    const int per_group = gm * tiles_f;
+    const int grp = sl / per_group;
+    const int in_g = sl - grp * per_group;
+    const int full = tx / gm;                          // groups of group_m token tiles
+    const int gsz = grp < full ? gm : tx - full * gm;  // token tiles in this group
+    const int tf = in_g / gsz;
+    const int tm_local = in_g - tf * gsz;
+    const int64_t tm_fwd = (int64_t)(grp * gm + tm_local) * 8 + xcd;  // < tiles_m
+    // token tiles walked last to first when asked (the newest rows of B first)
+    tm_o = g.reverse_m ? tiles_m - 1 - tm_fwd : tm_fwd;
+    f0_o = tf * kBF;
+  };
+  constexpr bool kPrefetchTile = ENGRAM_GEMM_PREFETCH_TILE && ENGRAM_GEMM_EARLY_BARRIER &&
+                                 S::kStages == 2 && GT == GEMM_BF16 && EPI == EPI_KV && !GATHER;
+  // how this tile's stage 0 was loaded: 0 by its own prologue; else by the
+  // previous tile, followed there by 1: exactly 32 row stores per wave (a
+  // whole value tile), 2: an unknown number of stores
+  int pf_kind = 0;
+  // this tile's coordinates, found by the previous iteration (the mapping
+  // costs three integer divisions)
+  int64_t tm_c = 0;
+  int f0_c = 0;
+  if ((int)(blockIdx.x >> 3) < nslots) tile_of(blockIdx.x >> 3, tm_c, f0_c);
   for (int slot = blockIdx.x >> 3; slot < nslots; slot += slot_step) {
   [[maybe_unused]] const int it_ = (slot - (int)(blockIdx.x >> 3)) / slot_step;
   ENGRAM_TRACE_TILE(0);
-  const int gm = g.group_m;
-  const int per_group = gm * tiles_f;
-  const int grp = slot / per_group;
-  const int in_g = slot - grp * per_group;
-  const int full = tx / gm;                          // groups of group_m token tiles
-  const int gsz = grp < full ? gm : tx - full * gm;  // token tiles in this group
-  const int tf = in_g / gsz;
-  const int tm_local = in_g - tf * gsz;
-  const int64_t tm_fwd = (int64_t)(grp * gm + tm_local) * 8 + xcd;  // < tiles_m
-  // token tiles walked last to first when asked (the newest rows of B first)
-  const int64_t tm = g.reverse_m ? tiles_m - 1 - tm_fwd : tm_fwd;
-  const int f0 = tf * kBF;
+  const int64_t tm = tm_c;
+  const int f0 = f0_c;
   const int64_t m0 = tm * kBT;
+  // the next tile of this workgroup; with kPrefetchTile its stage 0 is loaded
+  // early when it is a whole token tile (its B rows need no clamping)
+  int64_t tmn = 0;
+  int f0n = 0;
+  const bool has_next = slot + slot_step < nslots;
+  if (has_next) tile_of(slot + slot_step, tmn, f0n);
+  const bool pf_next = kPrefetchTile && has_next && (tmn + 1) * kBT <= g.M;
   // EPI_KV output features: the keys of `branches` branches (d each), then v.
   // A feature tile lies inside one branch key or inside v (d % 256 == 0);
   // fk is its first feature there.  h, gamma, k and the partial sums of a
@@ -257,15 +297,17 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // byte offsets of piece i inside the tile's rows (A: rows f0.., B: rows m0..)
   uint32_t voffA[NL], voffB[NL];
   int gj[NL], gw[NL], grow[NL];  // GATHER: table, element offset and local row of the piece at stage 0
+  // B rows past the last token repeat it (32-bit offsets: a tile's rows span
+  // less than 2^31 bytes, gemm_supported)
+  const int last_row = (int)std::min<int64_t>(g.M - 1 - m0, kBT - 1);
+  const int rb32 = (int)row_bytes;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int ch = wave + 4 * i;
     const int row = ch * S::kRowsPerLoad + lane / S::kPieces;
     const int c = (lane % S::kPieces) ^ S::swz(row);
-    voffA[i] = (uint32_t)(row * row_bytes + c * 16);
-    int64_t m = m0 + row;
-    m = m < g.M ? m : g.M - 1;
-    voffB[i] = (uint32_t)((m - m0) * row_bytes + c * 16);
+    voffA[i] = (uint32_t)(row * rb32 + c * 16);
+    voffB[i] = (uint32_t)(std::min(row, last_row) * rb32 + c * 16);
     if constexpr (GATHER) {
       const int e0 = c * 16 / ES;
       gj[i] = e0 / g.D;
@@ -277,6 +319,8 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   }
   const uint8_t* const tileA = g.A + (int64_t)f0 * row_bytes;
   const uint8_t* const tileB = GATHER ? nullptr : g.B + m0 * row_bytes;
+  const uint8_t* const nextA = kPrefetchTile ? g.A + (int64_t)f0n * row_bytes : nullptr;
+  const uint8_t* const nextB = kPrefetchTile ? g.B + tmn * kBT * row_bytes : nullptr;
   constexpr int kStageElems = SB / ES;
   const int64_t dbytes = (int64_t)g.D * ES;
 
@@ -355,6 +399,28 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     } else {
       load_lds16_s(voffB[i], bB, m0v);
     }
+  };
+  // Load slot j of the next tile's stage 0 into buffer 0.  That tile is
+  // whole, so its B rows are unclamped and take A's offsets.
+  auto issue_tile0 = [&](const void* bA, const void* bB, int j) __attribute__((always_inline)) {
+    const int i = j >> 1, op = j & 1;
+    const uint32_t m0v = lds_addr(st0) + (uint32_t)((wave + 4 * i) * 1024) + (op ? kTS : 0);
+    load_lds16_s(voffA[i], op ? bB : bA, m0v);
+  };
+  // Load slot j of the tail: the next tile's stage 0 (value tiles with a
+  // whole next tile) or else h row pair (2*NL)*wave + j of part 0 (key
+  // tiles), a repeated read of h's first 16 bytes into the same rows (other
+  // value tiles); all of them land in buffer 0.  Selected per tile, no branch.
+  const bool tail_tile0 = kPrefetchTile && !hov && pf_next;
+  auto issue_tail = [&](int j) __attribute__((always_inline)) {
+    const int i = j >> 1, op = j & 1;
+    const int p = 2 * NL * wave + j;
+    const uint32_t hv = hov ? h_voff(0, p) : 0u;
+    const uint32_t voff = tail_tile0 ? voffA[i] : hv;
+    const void* base = tail_tile0 ? (op ? nextB : nextA) : hbase;
+    const uint32_t m0v = tail_tile0 ? lds_addr(st0) + (uint32_t)((wave + 4 * i) * 1024) + (op ? kTS : 0)
+                                    : lds_addr(trow(h_t0(0, p)));
+    load_lds16_s(voff, base, m0v);
   };
   // h row pair (2*NL)*wave + j of part X (load slot j); value tiles (hov
   // false) read the first 16 bytes of the h tile in every lane instead
@@ -501,6 +567,8 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     constexpr int SL = decltype(kSlots)::value;
     if constexpr (SL == kSlotNext)
       issue_one(bA, bB, la, j);
+    else if constexpr (SL == kSlotTail)
+      issue_tail(j);
     else if constexpr (SL >= kSlotH)
       issue_h(SL - kSlotH, j);
   };
@@ -510,8 +578,9 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // two ahead (lkl at lla) after the barrier.
   auto compute2 = [&](const uint8_t* sa, const uint8_t* sb, const uint8_t* na, const uint8_t* nb,
                       auto kEarlyS, int ekl, uint32_t ela, auto kLateS, int lkl, uint32_t lla,
-                      auto kNext, auto kLateAll, [[maybe_unused]] int kid)
+                      auto kNext, auto kLateAll, [[maybe_unused]] int kid, auto kZero)
                       __attribute__((always_inline)) {
+    constexpr bool ZERO = decltype(kZero)::value;  // stage 0: step 0 starts the accumulators
     constexpr int ESL = decltype(kEarlyS)::value;
     constexpr int LSL = decltype(kLateS)::value;
     constexpr bool NEXT = decltype(kNext)::value;
@@ -533,7 +602,16 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       for (int a = 0; a < FB; ++a) {
         const int gi = ss * FB + a;
 #pragma unroll
-        for (int b = 0; b < TB; ++b) Mma<GT>::run(af2[cur][a], bf2[cur][b], acc[a][b]);
+        for (int b = 0; b < TB; ++b) {
+          if constexpr (ZERO) {
+            if (ss == 0)
+              Mma<GT>::run0(af2[cur][a], bf2[cur][b], acc[a][b]);
+            else
+              Mma<GT>::run(af2[cur][a], bf2[cur][b], acc[a][b]);
+          } else {
+            Mma<GT>::run(af2[cur][a], bf2[cur][b], acc[a][b]);
+          }
+        }
         if (ss + 1 < KS) {
           frag_one(sa, sb, ss + 1, a, af2[nx][a], bf2[nx][a]);
 #pragma unroll
@@ -604,22 +682,34 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   if constexpr (kEarlyBarrier) {
     using True_ = std::true_type;
     using False_ = std::false_type;
-    issue(0, l0);
+    ENGRAM_TRACE_TILE(6);
+    if (pf_kind == 0) issue(0, l0);
     {
       const void* bA = stage_base(tileA, 1);
       const void* bB = stage_base(tileB, 1);
 #pragma unroll
       for (int j = 0; j < kLate; ++j) issue_one(bA, bB, l1, j);
     }
-    ENGRAM_WAIT_VM(kLate);  // this wave's stage-0 loads landed
+    // this wave's stage-0 loads landed (counted from the newest operation:
+    // the previous tile's 32 row stores, when known, may still be in flight)
+    if (pf_kind == 1)
+      ENGRAM_WAIT_VM(kLate + 32);
+    else
+      ENGRAM_WAIT_VM(kLate);
+    ENGRAM_TRACE_TILE(7);
     ENGRAM_BARRIER();
+    ENGRAM_TRACE_TILE(3);
     frag(sA0, sB0, 0, af2[0], bf2[0]);
-    int kt = 0;
+    // stages 0 and 1 peeled (nk >= 4 here): stage 0's first step writes the
+    // accumulators instead of adding to zeroed ones
+    compute2(sA0, sB0, sA1, sB1, SlotNext{}, 1, l1, SlotNext{}, 2, l0, True_{}, False_{}, 0, True_{});
+    compute2(sA1, sB1, sA0, sB0, SlotNext{}, 2, l0, SlotNext{}, 3, l1, True_{}, False_{}, 1, False_{});
+    int kt = 2;
     for (; kt + 2 < nk; kt += 2) {
       compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, SlotNext{}, kt + 2, l0, True_{}, False_{},
-               kt);
+               kt, False_{});
       compute2(sA1, sB1, sA0, sB0, SlotNext{}, kt + 2, l0, SlotNext{}, kt + 3, l1, True_{}, False_{},
-               kt + 1);
+               kt + 1, False_{});
     }
     // part 0 of the h tile (placeholder reads in value tiles) as stage nk;
     // part 1 goes out after the loop, where a burst of loads holds up no MFMA
@@ -629,8 +719,16 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
 #else
     using H1 = SlotNone;
 #endif
-    compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, H0{}, 0, 0u, True_{}, False_{}, kt);
-    compute2(sA1, sB1, sA1, sB1, H0{}, 0, 0u, H1{}, 0, 0u, False_{}, True_{}, kt + 1);
+    if constexpr (kPrefetchTile) {
+      // key tiles load part 0 of h into buffer 0, value tiles the next
+      // tile's stage 0 (one code path: a branch here made the compiler spill)
+      using TL = std::integral_constant<int, kSlotTail>;
+      compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, TL{}, 0, 0u, True_{}, False_{}, kt, False_{});
+      compute2(sA1, sB1, sA1, sB1, TL{}, 0, 0u, H1{}, 0, 0u, False_{}, True_{}, kt + 1, False_{});
+    } else {
+      compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, H0{}, 0, 0u, True_{}, False_{}, kt, False_{});
+      compute2(sA1, sB1, sA1, sB1, H0{}, 0, 0u, H1{}, 0, 0u, False_{}, True_{}, kt + 1, False_{});
+    }
   } else if constexpr (NS == 4) {
     uint8_t* const sA2 = st2;
     uint8_t* const sB2 = st2 + kTS;
@@ -692,7 +790,13 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   }
   ENGRAM_TRACE_TILE(1);
   // stage buffers are free from here on (the st0 half of h may be in flight)
-  if (hov) {
+  if (kPrefetchTile || hov) {
+    // with the next tile's stage 0 (value tiles) or h part 0 (key tiles) in
+    // flight into buffer 0: every wave has read the last stage in buffer 1.
+    // Value tiles without a next tile to load read h placeholders into
+    // buffer 0 instead; those land before the tile ends.
+    if (kPrefetchTile && !hov && !pf_next) ENGRAM_WAIT_VM(0);
+    ENGRAM_WAIT_VM_LDS(63);
     ENGRAM_BARRIER();
   } else {
     // A value tile's last stages issued placeholder h loads into the rows its
@@ -746,6 +850,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         ENGRAM_WAIT_VM_LDS(0);
       }
       ENGRAM_BARRIER();
+      ENGRAM_TRACE_TILE(8);
       // Per token (lane column), over this wave's 128 features: sum k^2,
       // sum g h k (g = gamma_q gamma_k), sum h^2.  Variants without gamma and
       // without the k store keep those branches out of the unrolled body.
@@ -834,13 +939,31 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       static_assert(TB == 4, "two token blocks per h half");
       if (hov) {
         sums(I0{}, I2{});       // blocks 0, 1: h rows in st0
-        ENGRAM_WAIT_VM(0);      // own st1-half loads landed
+        ENGRAM_TRACE_TILE(4);
+        ENGRAM_WAIT_VM_LDS(0);  // own st1-half loads landed, own reads of st0 done
         ENGRAM_BARRIER();
+        if constexpr (kPrefetchTile) {
+          // buffer 0 is free: the next tile's stage 0 lands while blocks 2, 3
+          // are summed
+          if (pf_next) {
+            const void* bA = uniform_ptr(nextA);
+            const void* bB = uniform_ptr(nextB);
+#pragma unroll
+            for (int j = 0; j < 2 * NL; ++j) issue_tile0(bA, bB, j);
+          }
+        }
         sums(I2{}, I4{});       // blocks 2, 3: h rows in st1
+        ENGRAM_TRACE_TILE(5);
       } else {
         sums(I0{}, I4{});
       }
-      __syncthreads();
+      if constexpr (kPrefetchTile) {
+        // a fence-free barrier: __syncthreads() would wait for those loads
+        ENGRAM_WAIT_VM_LDS(63);
+        ENGRAM_BARRIER();
+      } else {
+        __syncthreads();
+      }
       {  // 2 wt x TB x 32 = 256 tokens, one per thread; add the two feature halves
         const int wt2 = tid >> 7, b = (tid >> 5) & 3, l = tid & 31;
         const int64_t m = m0 + (wt2 * TB + b) * 32 + l;
@@ -853,6 +976,60 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
           out[2] = p0[2] + p1[2];
         }
       }
+    } else if constexpr (kPrefetchTile) {
+      // value tile, with buffer 0 taken by the next tile's stage 0: the
+      // accumulators go to bf16 rows in buffer 1 in two rounds of 128 tokens
+      // (token blocks 2R, 2R+1 of every wave), each stored as whole rows.
+      // Token t = 128w + 64R + r sits at row 64w + r.
+      auto value_round = [&](auto kR) __attribute__((always_inline)) {
+        constexpr int R = decltype(kR)::value;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int b = 2 * R + bb;
+          const int t = (wt * TB + b) * 32 + l32;
+          uint8_t* row = st1 + ((t >> 7) * 64 + (t & 63)) * 512;
+#pragma unroll
+          for (int a = 0; a < FB; ++a) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c16 = (wf * FB + a) * 4 + q;
+              float x[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) x[r] = acc_read(acc[a][b][q * 4 + r]);
+              u32x2 u;
+              u[0] = pack_bf16x2(x[0], x[1]);
+              u[1] = pack_bf16x2(x[2], x[3]);
+              *reinterpret_cast<u32x2*>(row + ((c16 ^ (t & 31)) << 4) + lhalf * 8) = u;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        ENGRAM_WAIT_VM_LDS(63);
+        ENGRAM_BARRIER();
+        if constexpr (R == 0) ENGRAM_TRACE_TILE(4);
+        // 128 rows x 32 pieces of 16 bytes; a wave writes two rows per instruction
+#pragma unroll kVStoreUnroll
+        for (int i = 0; i < 16; ++i) {
+          const int lr = (wave * 16 + i) * 2 + (lane >> 5);
+          const int t = (lr >> 6) * 128 + 64 * R + (lr & 63);
+          const int c16 = lane & 31;
+          const int64_t m = m0 + t;
+          if (m < g.M) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(st1 + lr * 512 + ((c16 ^ (t & 31)) << 4));
+            u32x4* vp = reinterpret_cast<u32x4*>(g.v_out + (m * d + fk + c16 * 8) * 2);
+            if constexpr (ENGRAM_GEMM_V_NT != 0)
+              __builtin_nontemporal_store(x, vp);
+            else
+              *vp = x;
+          }
+        }
+      };
+      value_round(std::integral_constant<int, 0>{});
+      // round 1 rewrites the rows every wave has just read
+      ENGRAM_WAIT_VM_LDS(63);
+      ENGRAM_BARRIER();
+      value_round(std::integral_constant<int, 1>{});
+      ENGRAM_TRACE_TILE(5);
     } else {
       // value tile: accumulators -> bf16 rows in LDS -> whole rows to v
       // (8-byte stores straight from the accumulators measured 3 % slower)
@@ -891,6 +1068,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         }
       }
       __syncthreads();
+      ENGRAM_TRACE_TILE(4);
       // 256 rows x 32 pieces of 16 bytes; a wave writes two rows per instruction
 #pragma unroll 4
       for (int i = 0; i < 32; ++i) {
@@ -906,6 +1084,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
             *vp = x;
         }
       }
+      ENGRAM_TRACE_TILE(5);
     }
   } else if constexpr (EPI == EPI_KV) {
     // fp32 (small shapes): straight from the accumulators
@@ -1045,6 +1224,13 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   ENGRAM_WAIT_VM_LDS(63);
   ENGRAM_BARRIER();
   ENGRAM_TRACE_TILE(2);
+  if constexpr (kPrefetchTile) {
+    // a whole value tile issued exactly 32 row stores per wave after the
+    // next tile's stage 0; a key or ragged tile an unknown number
+    pf_kind = !pf_next ? 0 : ((!key_tile && (tm + 1) * kBT <= g.M) ? 1 : 2);
+  }
+  tm_c = tmn;
+  f0_c = f0n;
   }  // slot loop
 }
 
@@ -1065,6 +1251,11 @@ static hipError_t launch_one(const GemmArgs& g0, hipStream_t s) {
     per_xcd = std::min<int64_t>(slots, std::max(1, cus / 8));
   }
   const int64_t blocks = 8 * per_xcd;
+  // the two-buffer schedule of bf16/fp16 operands peels its first two
+  // stages before its last two: a K of two stages takes the 64-byte ring
+  if (g.stage_bytes == 128 && (GT == GEMM_BF16 || GT == GEMM_F16) && !GATHER &&
+      (int64_t)g.K * 2 <= 2 * 128)
+    g.stage_bytes = 64;
   if (g.stage_bytes == 128)
     hipLaunchKernelGGL((gemm_kernel<GT, EPI, GATHER, 128>), dim3((unsigned)blocks), dim3(kNT), 0, s, g);
   else

@@ -9,11 +9,17 @@ namespace engram {
 template <int GT>
 struct Mma;
 
+// run0: c = a b with a zero accumulator (an inline-constant C operand, so a
+// tile's accumulators need no zeroing writes)
 template <>
 struct Mma<GEMM_BF16> {
   __device__ static inline void run(const u32x4& a, const u32x4& b, floatx16& c) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline void run0(const u32x4& a, const u32x4& b, floatx16& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), floatx16{}, 0, 0, 0);
   }
 };
 
@@ -22,6 +28,10 @@ struct Mma<GEMM_F16> {
   __device__ static inline void run(const u32x4& a, const u32x4& b, floatx16& c) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
                                                __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+  }
+  __device__ static inline void run0(const u32x4& a, const u32x4& b, floatx16& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                               __builtin_bit_cast(halfx8, b), floatx16{}, 0, 0, 0);
   }
 };
 
@@ -34,6 +44,11 @@ struct Mma<GEMM_FP8> {
                                                          __builtin_bit_cast(i32x8, b), c, 0, 0, 0, 0,
                                                          0, 0);
   }
+  __device__ static inline void run0(const u32x8& a, const u32x8& b, floatx16& c) {
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
+                                                         __builtin_bit_cast(i32x8, b), floatx16{}, 0,
+                                                         0, 0, 0, 0, 0);
+  }
 };
 
 // fp32: lanes 0-31 hold k = 0..3 of the 32-byte K slice, lanes 32-63 hold
@@ -42,6 +57,12 @@ template <>
 struct Mma<GEMM_F32> {
   __device__ static inline void run(const u32x4& a, const u32x4& b, floatx16& c) {
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  }
+  __device__ static inline void run0(const u32x4& a, const u32x4& b, floatx16& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), floatx16{}, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);

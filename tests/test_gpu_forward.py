@@ -148,6 +148,27 @@ def test_tiny_bf16_ragged(torch, oracle_lib, B, T):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("heads,dim", [(4, 32), (6, 64)])
+def test_bf16_short_memory(torch, oracle_lib, heads, dim):
+    """bf16 projections over a memory vector of 4 and 12 K stages of 64
+    values (e_t of 256 values: 8 tables of 32; 768 values: 12 tables of 64):
+    the projection peels its first two stages (whose first step starts the
+    accumulators) and runs its last two with no, or with four, passes of the
+    stage loop between them."""
+    wl = dataclasses.replace(synth.get_workload("tiny"), name=f"tiny_bf16_h{heads}", dtype="bf16",
+                             heads=heads, dim=dim, rows=(10007,) * (2 * heads)).with_shape(2, 300)
+    assert wl.d_mem == 2 * heads * dim
+    inp, dp, bufs, y = _run_full(torch, wl)
+    p = H.oracle_problem(inp)
+    assert np.array_equal(bufs["idx"].cpu().numpy(), p.hash())
+    ref = p.forward(want=("y", "alpha", "e"))
+    assert np.array_equal(H.to_host_f64(bufs["e"]), ref["e"])
+    err = H.rel_max_err(H.to_host_f64(y).reshape(-1, wl.hidden), ref["y"])
+    a_err = float(np.abs(bufs["stats"][:, 0].cpu().numpy() - ref["alpha"]).max())
+    print(f"  d_mem = {wl.d_mem}: max-abs-err/max|ref| = {err:.3e}, alpha err {a_err:.2e}", flush=True)
+    assert err <= TOL["bf16"] and a_err <= 1e-2, (err, a_err)
+
+
 @pytest.mark.parametrize("B,T", [(8, 4096)])
 def test_small_bf16(torch, oracle_lib, B, T):
     wl = synth.get_workload("small").with_shape(B, T)
