@@ -27,7 +27,10 @@
 // fragment.  The grid is persistent (one workgroup per CU).  Workgroup ids
 // reach the 8 XCDs round-robin; the id -> tile map keeps the f-tiles of a
 // small group of token tiles on one XCD so they share rows and weight slabs
-// in its L2.
+// in its L2.  In the bf16 projection a workgroup loads the first K stage of
+// its next tile while it finishes the current one, and every tile's first K
+// step writes its accumulators (zero C operand), so tiles follow each other
+// without a load wait or zeroing writes.
 #include <algorithm>
 #include <type_traits>
 
@@ -124,6 +127,11 @@ constexpr int kLoadGroups = ENGRAM_GEMM_LOAD_GROUPS;
 constexpr int kVStoreUnroll = ENGRAM_GEMM_VSTORE_UNROLL;
 #ifndef ENGRAM_GEMM_PREFETCH_TILE
 #define ENGRAM_GEMM_PREFETCH_TILE 1
+#endif
+// key tiles: 0 = no early stage-0 load, 1 = before token blocks 2 and 3 are
+// summed, 2 = between blocks 2 and 3
+#ifndef ENGRAM_GEMM_PREFETCH_KEY
+#define ENGRAM_GEMM_PREFETCH_KEY 1
 #endif
 // Load stage 0 of a workgroup's next tile while this one finishes (bf16
 // key/value projection): value tiles in the load slots of their last K stage,
@@ -942,17 +950,25 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         ENGRAM_TRACE_TILE(4);
         ENGRAM_WAIT_VM_LDS(0);  // own st1-half loads landed, own reads of st0 done
         ENGRAM_BARRIER();
-        if constexpr (kPrefetchTile) {
-          // buffer 0 is free: the next tile's stage 0 lands while blocks 2, 3
-          // are summed
+        auto key_prefetch = [&]() __attribute__((always_inline)) {
           if (pf_next) {
             const void* bA = uniform_ptr(nextA);
             const void* bB = uniform_ptr(nextB);
 #pragma unroll
             for (int j = 0; j < 2 * NL; ++j) issue_tile0(bA, bB, j);
           }
+        };
+        // buffer 0 is free: the next tile's stage 0 lands while blocks 2, 3
+        // are summed
+        if constexpr (kPrefetchTile && ENGRAM_GEMM_PREFETCH_KEY == 1) key_prefetch();
+        if constexpr (kPrefetchTile && ENGRAM_GEMM_PREFETCH_KEY == 2) {
+          using I3 = std::integral_constant<int, 3>;
+          sums(I2{}, I3{});
+          key_prefetch();
+          sums(I3{}, I4{});
+        } else {
+          sums(I2{}, I4{});     // blocks 2, 3: h rows in st1
         }
-        sums(I2{}, I4{});       // blocks 2, 3: h rows in st1
         ENGRAM_TRACE_TILE(5);
       } else {
         sums(I0{}, I4{});
@@ -1227,7 +1243,9 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   if constexpr (kPrefetchTile) {
     // a whole value tile issued exactly 32 row stores per wave after the
     // next tile's stage 0; a key or ragged tile an unknown number
-    pf_kind = !pf_next ? 0 : ((!key_tile && (tm + 1) * kBT <= g.M) ? 1 : 2);
+    pf_kind = !pf_next || (key_tile && ENGRAM_GEMM_PREFETCH_KEY == 0)
+                  ? 0
+                  : ((!key_tile && (tm + 1) * kBT <= g.M) ? 1 : 2);
   }
   tm_c = tmn;
   f0_c = f0n;
