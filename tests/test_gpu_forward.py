@@ -169,6 +169,25 @@ def test_bf16_short_memory(torch, oracle_lib, heads, dim):
     assert err <= TOL["bf16"] and a_err <= 1e-2, (err, a_err)
 
 
+@pytest.mark.parametrize("B,T", [(1, 4196), (2, 2048), (2, 2085)])
+def test_bf16_tiles_per_workgroup(torch, oracle_lib, B, T):
+    """bf16 forward where the persistent projection gives workgroups several
+    tiles each (d = 2560: 20 feature tiles; 16 or 17 token tiles), so every
+    tile but a workgroup's last loads the next one's first K stage early;
+    with a ragged last token tile (4196 and 4170 tokens) that tile is loaded
+    by its own prologue.  Every position against the oracle."""
+    wl = dataclasses.replace(synth.get_workload("tiny"), name="tiny_bf16_tiles", dtype="bf16",
+                             hidden=2560).with_shape(B, T)
+    print(f"[bf16 tiles per workgroup] B={B} T={T}", flush=True)
+    inp, dp, bufs, y = _run_full(torch, wl, saved=("idx", "stats"))
+    p = H.oracle_problem(inp)
+    ref = p.forward(want=("y", "alpha"))
+    err = H.rel_max_err(H.to_host_f64(y).reshape(-1, wl.hidden), ref["y"])
+    a_err = float(np.abs(bufs["stats"][:, 0].cpu().numpy() - ref["alpha"]).max())
+    print(f"  max-abs-err/max|ref| = {err:.3e}, alpha err {a_err:.2e}", flush=True)
+    assert err <= TOL["bf16"] and a_err <= 1e-2, (err, a_err)
+
+
 @pytest.mark.parametrize("B,T", [(8, 4096)])
 def test_small_bf16(torch, oracle_lib, B, T):
     wl = synth.get_workload("small").with_shape(B, T)
