@@ -130,6 +130,13 @@ constexpr int kVStoreUnroll = ENGRAM_GEMM_VSTORE_UNROLL;
 #endif
 // key tiles: 0 = no early stage-0 load, 1 = before token blocks 2 and 3 are
 // summed, 2 = between blocks 2 and 3
+// Each K stage of the bf16 projection also fetches the workgroup's eighth of
+// its B tile's rows three stages ahead into L2 (into LDS scratch that nothing
+// reads), so the tiles that meet a token tile first do not wait for HBM at
+// every stage.
+#ifndef ENGRAM_GEMM_PREFETCH_E
+#define ENGRAM_GEMM_PREFETCH_E 1
+#endif
 #ifndef ENGRAM_GEMM_PREFETCH_KEY
 #define ENGRAM_GEMM_PREFETCH_KEY 1
 #endif
@@ -329,6 +336,16 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const uint8_t* const tileB = GATHER ? nullptr : g.B + m0 * row_bytes;
   const uint8_t* const nextA = kPrefetchTile ? g.A + (int64_t)f0n * row_bytes : nullptr;
   const uint8_t* const nextB = kPrefetchTile ? g.B + tmn * kBT * row_bytes : nullptr;
+  // B rows fetched ahead: the eighth q = (f-tile mod 8) of the tile's rows,
+  // 8 per wave (the 8 f-tiles that share a token tile in one pass of the XCD
+  // have distinct q); 16-byte piece lane % 8 of a 128-byte stage
+  constexpr bool kPfE = kPrefetchTile && ENGRAM_GEMM_PREFETCH_E && SB == 128;
+  uint32_t pfe_voff = 0;
+  if constexpr (kPfE) {
+    const int q = (f0 / kBF) & 7;
+    const int row = std::min(q * 32 + wave * 8 + (lane >> 3), last_row);
+    pfe_voff = (uint32_t)(row * rb32 + (lane & 7) * 16);
+  }
   constexpr int kStageElems = SB / ES;
   const int64_t dbytes = (int64_t)g.D * ES;
 
@@ -586,9 +603,13 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   // two ahead (lkl at lla) after the barrier.
   auto compute2 = [&](const uint8_t* sa, const uint8_t* sb, const uint8_t* na, const uint8_t* nb,
                       auto kEarlyS, int ekl, uint32_t ela, auto kLateS, int lkl, uint32_t lla,
-                      auto kNext, auto kLateAll, [[maybe_unused]] int kid, auto kZero)
+                      auto kNext, auto kLateAll, [[maybe_unused]] int kid, auto kZero, auto kPfES)
                       __attribute__((always_inline)) {
     constexpr bool ZERO = decltype(kZero)::value;  // stage 0: step 0 starts the accumulators
+    // one B fetch-ahead load after group kPfEGroup: the stage's own loads
+    // have all gone out by then, so its barrier leaves just that one in flight
+    constexpr bool PFE = decltype(kPfES)::value;
+    constexpr int kPfEGroup = 8;
     constexpr int ESL = decltype(kEarlyS)::value;
     constexpr int LSL = decltype(kLateS)::value;
     constexpr bool NEXT = decltype(kNext)::value;
@@ -661,11 +682,22 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PFE) {
+          static_assert(kLate + ENGRAM_GEMM_EARLY_PER * kPfEGroup >= NI && kPfEGroup < kBarGroup,
+                        "the fetch-ahead load follows every early slot");
+          if (gi == kPfEGroup) {
+            const int ks = kid + 3 < nk ? kid + 3 : nk - 1;
+            load_lds16_s(pfe_voff, stage_base(tileB, ks), lds_addr(sIdx) + (uint32_t)wave * 1024u);
+          }
+        }
         if (gi == kBarGroup) {
           // this wave's loads of the next stage and its reads of this one are
-          // done; then every wave's are
+          // done (a fetch-ahead load of this stage may still be in flight);
+          // then every wave's are
           ENGRAM_TRACE_W(kid, 0);
-          if constexpr (NEXT)
+          if constexpr (NEXT && PFE)
+            ENGRAM_WAIT_VM_LDS(1);
+          else if constexpr (NEXT)
             ENGRAM_WAIT_VM_LDS(0);
           else
             ENGRAM_WAIT_VM_LDS(63);
@@ -710,14 +742,15 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     frag(sA0, sB0, 0, af2[0], bf2[0]);
     // stages 0 and 1 peeled (nk >= 4 here): stage 0's first step writes the
     // accumulators instead of adding to zeroed ones
-    compute2(sA0, sB0, sA1, sB1, SlotNext{}, 1, l1, SlotNext{}, 2, l0, True_{}, False_{}, 0, True_{});
-    compute2(sA1, sB1, sA0, sB0, SlotNext{}, 2, l0, SlotNext{}, 3, l1, True_{}, False_{}, 1, False_{});
+    using PfE = std::integral_constant<bool, kPfE>;
+    compute2(sA0, sB0, sA1, sB1, SlotNext{}, 1, l1, SlotNext{}, 2, l0, True_{}, False_{}, 0, True_{}, PfE{});
+    compute2(sA1, sB1, sA0, sB0, SlotNext{}, 2, l0, SlotNext{}, 3, l1, True_{}, False_{}, 1, False_{}, PfE{});
     int kt = 2;
     for (; kt + 2 < nk; kt += 2) {
       compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, SlotNext{}, kt + 2, l0, True_{}, False_{},
-               kt, False_{});
+               kt, False_{}, PfE{});
       compute2(sA1, sB1, sA0, sB0, SlotNext{}, kt + 2, l0, SlotNext{}, kt + 3, l1, True_{}, False_{},
-               kt + 1, False_{});
+               kt + 1, False_{}, PfE{});
     }
     // part 0 of the h tile (placeholder reads in value tiles) as stage nk;
     // part 1 goes out after the loop, where a burst of loads holds up no MFMA
@@ -731,11 +764,15 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       // key tiles load part 0 of h into buffer 0, value tiles the next
       // tile's stage 0 (one code path: a branch here made the compiler spill)
       using TL = std::integral_constant<int, kSlotTail>;
-      compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, TL{}, 0, 0u, True_{}, False_{}, kt, False_{});
-      compute2(sA1, sB1, sA1, sB1, TL{}, 0, 0u, H1{}, 0, 0u, False_{}, True_{}, kt + 1, False_{});
+      compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, TL{}, 0, 0u, True_{}, False_{}, kt, False_{},
+               False_{});
+      compute2(sA1, sB1, sA1, sB1, TL{}, 0, 0u, H1{}, 0, 0u, False_{}, True_{}, kt + 1, False_{},
+               False_{});
     } else {
-      compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, H0{}, 0, 0u, True_{}, False_{}, kt, False_{});
-      compute2(sA1, sB1, sA1, sB1, H0{}, 0, 0u, H1{}, 0, 0u, False_{}, True_{}, kt + 1, False_{});
+      compute2(sA0, sB0, sA1, sB1, SlotNext{}, kt + 1, l1, H0{}, 0, 0u, True_{}, False_{}, kt, False_{},
+               False_{});
+      compute2(sA1, sB1, sA1, sB1, H0{}, 0, 0u, H1{}, 0, 0u, False_{}, True_{}, kt + 1, False_{},
+               False_{});
     }
   } else if constexpr (NS == 4) {
     uint8_t* const sA2 = st2;
