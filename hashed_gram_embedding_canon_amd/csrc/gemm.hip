@@ -137,6 +137,18 @@ constexpr int kVStoreUnroll = ENGRAM_GEMM_VSTORE_UNROLL;
 #ifndef ENGRAM_GEMM_PREFETCH_E
 #define ENGRAM_GEMM_PREFETCH_E 1
 #endif
+// The same in the de contraction (five f-tiles share a token tile: two loads
+// per wave and stage, 64 rows per workgroup).
+#ifndef ENGRAM_GEMM_PREFETCH_E_DE
+#define ENGRAM_GEMM_PREFETCH_E_DE 1
+#endif
+// The de contraction can load its next tile's stage 0 early too (in the load
+// slots of its last two stages; its epilogue stores from the accumulators):
+// its prologue drops from 3.3-5K to 1.4K cycles, yet the kernel time stays
+// the same (1.4261 against 1.4271 ms), so it is off.
+#ifndef ENGRAM_GEMM_PREFETCH_TILE_DE
+#define ENGRAM_GEMM_PREFETCH_TILE_DE 0
+#endif
 #ifndef ENGRAM_GEMM_PREFETCH_KEY
 #define ENGRAM_GEMM_PREFETCH_KEY 1
 #endif
@@ -240,11 +252,14 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     tm_o = g.reverse_m ? tiles_m - 1 - tm_fwd : tm_fwd;
     f0_o = tf * kBF;
   };
-  constexpr bool kPrefetchTile = ENGRAM_GEMM_PREFETCH_TILE && ENGRAM_GEMM_EARLY_BARRIER &&
-                                 S::kStages == 2 && GT == GEMM_BF16 && EPI == EPI_KV && !GATHER;
+  constexpr bool kPrefetchTile =
+      ENGRAM_GEMM_PREFETCH_TILE && ENGRAM_GEMM_EARLY_BARRIER && S::kStages == 2 && !GATHER &&
+      ((GT == GEMM_BF16 && EPI == EPI_KV) ||
+       (ENGRAM_GEMM_PREFETCH_TILE_DE && GT == GEMM_F16 && EPI == EPI_STORE_F32));
   // how this tile's stage 0 was loaded: 0 by its own prologue; else by the
   // previous tile, followed there by 1: exactly 32 row stores per wave (a
-  // whole value tile), 2: an unknown number of stores
+  // whole value tile), 2: an unknown number of stores, 3: 64 stores per wave
+  // (a whole tile of the de contraction)
   int pf_kind = 0;
   // this tile's coordinates, found by the previous iteration (the mapping
   // costs three integer divisions)
@@ -336,15 +351,21 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   const uint8_t* const tileB = GATHER ? nullptr : g.B + m0 * row_bytes;
   const uint8_t* const nextA = kPrefetchTile ? g.A + (int64_t)f0n * row_bytes : nullptr;
   const uint8_t* const nextB = kPrefetchTile ? g.B + tmn * kBT * row_bytes : nullptr;
-  // B rows fetched ahead: the eighth q = (f-tile mod 8) of the tile's rows,
-  // 8 per wave (the 8 f-tiles that share a token tile in one pass of the XCD
-  // have distinct q); 16-byte piece lane % 8 of a 128-byte stage
-  constexpr bool kPfE = kPrefetchTile && ENGRAM_GEMM_PREFETCH_E && SB == 128;
-  uint32_t pfe_voff = 0;
-  if constexpr (kPfE) {
-    const int q = (f0 / kBF) & 7;
-    const int row = std::min(q * 32 + wave * 8 + (lane >> 3), last_row);
-    pfe_voff = (uint32_t)(row * rb32 + (lane & 7) * 16);
+  // B rows fetched ahead: share q = (f-tile mod 8 / kPfEL) of the tile's
+  // rows, kPfEL loads of 8 rows per wave (the f-tiles that share a token tile
+  // in one pass of the XCD take distinct shares); 16-byte piece lane % 8 of a
+  // 128-byte stage
+  constexpr bool kPfE =
+      ENGRAM_GEMM_PREFETCH_E && SB == 128 && !GATHER &&
+      (kPrefetchTile || (ENGRAM_GEMM_PREFETCH_E_DE && EPI == EPI_STORE_F32 && GT == GEMM_F16 &&
+                         ENGRAM_GEMM_EARLY_BARRIER && S::kStages == 2));
+  constexpr int kPfEL = EPI == EPI_KV ? 1 : 2;
+  uint32_t pfe_voff[kPfEL];
+#pragma unroll
+  for (int l = 0; l < kPfEL; ++l) {
+    const int q = (f0 / kBF) % (8 / kPfEL);
+    const int row = std::min(q * 32 * kPfEL + l * 32 + wave * 8 + (lane >> 3), last_row);
+    pfe_voff[l] = kPfE ? (uint32_t)(row * rb32 + (lane & 7) * 16) : 0u;
   }
   constexpr int kStageElems = SB / ES;
   const int64_t dbytes = (int64_t)g.D * ES;
@@ -441,11 +462,17 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     const int i = j >> 1, op = j & 1;
     const int p = 2 * NL * wave + j;
     const uint32_t hv = hov ? h_voff(0, p) : 0u;
-    const uint32_t voff = tail_tile0 ? voffA[i] : hv;
-    const void* base = tail_tile0 ? (op ? nextB : nextA) : hbase;
-    const uint32_t m0v = tail_tile0 ? lds_addr(st0) + (uint32_t)((wave + 4 * i) * 1024) + (op ? kTS : 0)
-                                    : lds_addr(trow(h_t0(0, p)));
-    load_lds16_s(voff, base, m0v);
+    const uint32_t m0t = lds_addr(st0) + (uint32_t)((wave + 4 * i) * 1024) + (op ? kTS : 0);
+    if constexpr (kBf16Epi) {
+      const uint32_t voff = tail_tile0 ? voffA[i] : hv;
+      const void* base = tail_tile0 ? (op ? nextB : nextA) : hbase;
+      load_lds16_s(voff, base, tail_tile0 ? m0t : lds_addr(trow(h_t0(0, p))));
+    } else {
+      // no h here: without a next tile, stage 0 of this one again (valid rows)
+      const uint32_t voff = tail_tile0 ? voffA[i] : (op ? voffB[i] : voffA[i]);
+      const void* base = tail_tile0 ? (op ? nextB : nextA) : (op ? tileB : tileA);
+      load_lds16_s(voff, base, m0t);
+    }
   };
   // h row pair (2*NL)*wave + j of part X (load slot j); value tiles (hov
   // false) read the first 16 bytes of the h tile in every lane instead
@@ -606,10 +633,11 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
                       auto kNext, auto kLateAll, [[maybe_unused]] int kid, auto kZero, auto kPfES)
                       __attribute__((always_inline)) {
     constexpr bool ZERO = decltype(kZero)::value;  // stage 0: step 0 starts the accumulators
-    // one B fetch-ahead load after group kPfEGroup: the stage's own loads
-    // have all gone out by then, so its barrier leaves just that one in flight
+    // kPfEL B fetch-ahead loads from group kPfEGroup on: the stage's own
+    // loads have all gone out by then, so its barrier leaves just those in
+    // flight
     constexpr bool PFE = decltype(kPfES)::value;
-    constexpr int kPfEGroup = 8;
+    constexpr int kPfEGroup = 8;  // the kPfEL loads follow groups 8, 9, ...
     constexpr int ESL = decltype(kEarlyS)::value;
     constexpr int LSL = decltype(kLateS)::value;
     constexpr bool NEXT = decltype(kNext)::value;
@@ -683,11 +711,13 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (PFE) {
-          static_assert(kLate + ENGRAM_GEMM_EARLY_PER * kPfEGroup >= NI && kPfEGroup < kBarGroup,
-                        "the fetch-ahead load follows every early slot");
-          if (gi == kPfEGroup) {
+          static_assert(kLate + ENGRAM_GEMM_EARLY_PER * kPfEGroup >= NI &&
+                            kPfEGroup + kPfEL <= kBarGroup,
+                        "the fetch-ahead loads follow every early slot");
+          if (gi >= kPfEGroup && gi < kPfEGroup + kPfEL) {
             const int ks = kid + 3 < nk ? kid + 3 : nk - 1;
-            load_lds16_s(pfe_voff, stage_base(tileB, ks), lds_addr(sIdx) + (uint32_t)wave * 1024u);
+            load_lds16_s(pfe_voff[gi - kPfEGroup], stage_base(tileB, ks),
+                         lds_addr(sIdx) + (uint32_t)wave * 1024u);
           }
         }
         if (gi == kBarGroup) {
@@ -696,7 +726,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
           // then every wave's are
           ENGRAM_TRACE_W(kid, 0);
           if constexpr (NEXT && PFE)
-            ENGRAM_WAIT_VM_LDS(1);
+            ENGRAM_WAIT_VM_LDS(kPfEL);
           else if constexpr (NEXT)
             ENGRAM_WAIT_VM_LDS(0);
           else
@@ -734,6 +764,8 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
     // the previous tile's 32 row stores, when known, may still be in flight)
     if (pf_kind == 1)
       ENGRAM_WAIT_VM(kLate + 32);
+    else if (pf_kind == 3)
+      ENGRAM_WAIT_VM(63);
     else
       ENGRAM_WAIT_VM(kLate);
     ENGRAM_TRACE_TILE(7);
@@ -1280,9 +1312,10 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
   if constexpr (kPrefetchTile) {
     // a whole value tile issued exactly 32 row stores per wave after the
     // next tile's stage 0; a key or ragged tile an unknown number
+    const bool whole = (tm + 1) * kBT <= g.M;
     pf_kind = !pf_next || (key_tile && ENGRAM_GEMM_PREFETCH_KEY == 0)
                   ? 0
-                  : ((!key_tile && (tm + 1) * kBT <= g.M) ? 1 : 2);
+                  : (!whole || key_tile ? 2 : (EPI == EPI_KV ? 1 : 3));
   }
   tm_c = tmn;
   f0_c = f0n;
