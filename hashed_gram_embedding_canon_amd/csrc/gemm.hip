@@ -120,7 +120,7 @@ constexpr int kLoadGroups = ENGRAM_GEMM_LOAD_GROUPS;
 #define ENGRAM_GEMM_V_NT 0
 #endif
 // Row stores of a value tile's epilogue unrolled this far (all 16 LDS reads
-// of a round in flight): 1.485 ms per projection against 1.494 ms with 4.
+// of a pass in flight): 1.485 ms per projection against 1.494 ms with 4.
 #ifndef ENGRAM_GEMM_VSTORE_UNROLL
 #define ENGRAM_GEMM_VSTORE_UNROLL 16
 #endif
@@ -1063,7 +1063,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
       }
     } else if constexpr (kPrefetchTile) {
       // value tile, with buffer 0 taken by the next tile's stage 0: the
-      // accumulators go to bf16 rows in buffer 1 in two rounds of 128 tokens
+      // accumulators go to bf16 rows in buffer 1 in two passes of 128 tokens
       // (token blocks 2R, 2R+1 of every wave), each stored as whole rows.
       // Token t = 128w + 64R + r sits at row 64w + r.
       auto value_round = [&](auto kR) __attribute__((always_inline)) {
@@ -1110,7 +1110,7 @@ __global__ __launch_bounds__(kNT) void gemm_kernel(GemmArgs g) {
         }
       };
       value_round(std::integral_constant<int, 0>{});
-      // round 1 rewrites the rows every wave has just read
+      // the second pass rewrites the rows every wave has just read
       ENGRAM_WAIT_VM_LDS(63);
       ENGRAM_BARRIER();
       value_round(std::integral_constant<int, 1>{});
